@@ -1,0 +1,46 @@
+"""Planted mistakes in a copy of the oracle must be caught by its pins (CPU only).
+
+Each mutation is a plausible slip (a sign, an index, a dropped term, a swapped
+operand). The oracle pin tests are re-run in a subprocess with the mutated
+copy first on sys.path; the run must fail.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    ("forward.py", "a * c - b * s, b * c + a * s", "a * c + b * s, b * c - a * s"),        # RoPE direction
+    ("forward.py", "qg = q[i].reshape(m.Hkv, G, m.dh)",
+     "qg = q[i].reshape(G, m.Hkv, m.dh).transpose(1, 0, 2)"),                                # GQA head map
+    ("forward.py", "[: p + 1]", "[: p]"),                                                       # causal limit
+    ("forward.py", "x = x + o.reshape", "x = o.reshape"),                                       # dropped residual
+    ("forward.py", "/ np.sqrt(m.dh)", "/ m.dh"),                                                # attention scale
+    ("forward.py", "(silu(gate) * up)", "(silu(up) * gate)"),                                   # gate/up swap
+    ("forward.py", "keepdims=True) + eps)", "keepdims=True))"),                                 # RMSNorm eps
+    ("forward.py", "kc[local(slots)] = k", "pass"),                                             # no KV write
+    ("expand.py", "ids[o] = tid[j + 1]", "ids[o] = tid[j]"),                                   # input shift
+    ("expand.py", "pos[o] = p_ntp + mm", "pos[o] = p_ntp + mm - 1"),                           # MASK positions
+    ("expand.py", "slot[o] = -1 if is_rej[o] else _slot(bt[r], int(pos[o]), block_size)",
+     "slot[o] = _slot(bt[r], int(pos[o]), block_size)"),                                       # -1 for rejected
+    ("expand.py", "new_idx[r * K] = out_start + v - 1", "new_idx[r * K] = out_start + v"),     # NTP index
+]
+
+
+@pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[m[2][:24] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, fname, old, new):
+    dst = tmp_path / "oracle"
+    shutil.copytree(os.path.join(ROOT, "oracle"), dst,
+                    ignore=shutil.ignore_patterns("__pycache__", "*.so", "*.o"))
+    src = (dst / fname).read_text()
+    assert src.count(old) == 1, f"mutation anchor not unique in {fname}: {old}"
+    (dst / fname).write_text(src.replace(old, new))
+    env = dict(os.environ, PD_ORACLE_MUTANT_DIR=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_expand.py", "tests/test_oracle_forward.py"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, "the oracle pins did not catch: " + new + "\n" + r.stdout[-2000:]
