@@ -1,0 +1,215 @@
+"""Benchmark of the P-EAGLE parallel drafting step on one MI355X.
+
+One step = pd_expand_batch + pd_draft_forward for the whole batch (every row
+of the hot path), on synthetic inputs already resident in HBM. Default
+workload: the GPT-OSS-20B-scale drafter at C=1, context 4096, K=7.
+
+    python bench.py [--steps K] [--warmup W] [--workload g_c1|g_c4|g_c64|...]
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value      draft steps/s (drafted tokens/s = value * C * K is reported too)
+  roofline   the dominant kernel's achieved bandwidth (algorithmic bytes per
+             launch / average launch time from HIP events on the launch
+             stream during the timed region) against the 8 TB/s HBM peak
+  cpu_baseline  the fp64 oracle (expand + forward) timed on the host cores on
+             a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+DESCR = {
+    "tiny": "tiny drafter prefill (d 256, 4 layers, vocab 4096), 128-token prompt, K=4",
+    "g_c1": "GPT-OSS-20B-scale drafter (d 2880, 64q/8kv x 64, SwiGLU 7680, 4 layers, vocab 201088), C=1, context 4096, K=7",
+    "g_c4": "GPT-OSS-20B-scale drafter, C=4, lognormal contexts (median 3891, P90 10800, 128..20000), K=7",
+    "g_c64": "GPT-OSS-20B-scale drafter, C=64, lognormal contexts, K=7",
+    "g_c64_k3": "GPT-OSS-20B-scale drafter, C=64, lognormal contexts, K=3",
+    "g_c64_k5": "GPT-OSS-20B-scale drafter, C=64, lognormal contexts, K=5",
+    "q_c16": "Qwen3-Coder-30B-scale drafter (d 2048, 32q/4kv x 128, SwiGLU 6144, 4 layers, vocab 151936), C=16, context 20000, K=7",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lm_head_bytes(dm, R: int) -> int:
+    """Algorithmic bytes of one LM-head launch: the bf16 weight matrix, the R
+    normalized bf16 input rows, and the R int32 draft ids."""
+    return dm.V * dm.d * 2 + R * dm.d * 2 + R * 4
+
+
+def step_bytes(dm, b, K: int) -> int:
+    """Algorithmic bytes of one whole step (weights once, visible KV once per
+    layer and kv head, KV writes, hidden rows in and out, ids)."""
+    w = dm.V * dm.d * 2 * 2 + dm.d * dm.hidden3 * 2
+    for l in range(dm.N):
+        w += dm.qkv_out * dm.qkv_in(l) * 2 + dm.d * dm.Hq * dm.dh * 2 + 3 * dm.F * dm.d * 2 + 4 * dm.d * 2
+    C = b["C"]
+    v = b["num_tokens"] - b["num_rejected"]
+    seq = b["context_lens"] + v + K - 1
+    kv_read = int(seq.sum()) * dm.Hkv * dm.dh * 2 * 2 * dm.N
+    T_eff = int((v + K - 1).sum())
+    kv_write = T_eff * dm.Hkv * dm.dh * 2 * 2 * dm.N
+    T_in = b["T_in"]
+    T_out = T_in + C * (K - 1)
+    hid = (T_in + T_out) * dm.hidden3 * 2 + dm.hidden3 * 2
+    emb = T_eff * dm.d * 2
+    return w + kv_read + kv_write + hid + emb + C * K * 4
+
+
+def cpu_baseline(w, model_np, b, pool, budget_s: float = 30.0) -> dict:
+    """Time the oracle (as it stands) on a bounded sample: the first request(s)
+    of the workload, one full expand + forward, in fp64 on the host cores."""
+    import oracle  # CPU baseline leg only
+
+    threads = len(os.sched_getaffinity(0))
+    reqs = [0] if w.C > 1 else None
+    t0 = time.perf_counter()
+    exp = oracle.expand(b["num_tokens"], b["num_rejected"], b["target_ids"], b["target_pos"],
+                        b["target_hidden"], b["next_token_ids"], b["block_table"], model_np["h_shared"],
+                        w.K, b["mask_id"], b["block_size"])
+    oracle.draft_forward(model_np, exp, b["block_table"], pool, w.K, requests=reqs,
+                         block_size=b["block_size"])
+    dt = time.perf_counter() - t0
+    n_req = 1 if reqs else w.C
+    # one sampled request of C: scale to whole steps of the workload
+    steps_per_s = (n_req / w.C) / dt
+    return {"value": steps_per_s, "unit": "draft steps/s", "cores": threads, "kind": "oracle",
+            "sample": (f"{'request 0 of ' + str(w.C) if reqs else 'the whole step'}: fp64 NumPy oracle "
+                       f"expand + forward ({dt:.2f} s), scaled to whole steps"),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="g_c1", choices=sorted(DESCR))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    import drafting_pd_expand_amd as pdx
+    def i32(a, dev):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def bf16(a, dev):
+        a = np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)
+        return torch.from_numpy(a).to(dev).view(torch.bfloat16)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pdx.load()
+    dev = torch.device("cuda:0")
+    w = synth.get_workload(args.workload)
+    dm = w.model
+    log(f"[bench] {args.workload}: generating model + inputs")
+    t0 = time.perf_counter()
+    model_np = synth.make_model(dm, seed=1234)
+    b = synth.make_batch(w)
+    pool = synth.make_kv_pool(dm, b["num_blocks"], w.seed)
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    mdev = pdx.device_model(model_np, dev)
+    dims = pdx.batch_dims(b["C"], w.K, b["T_in"], b["mask_id"], dm.hidden3, b["max_blocks"], b["num_blocks"])
+    inp = {
+        "num_tokens": i32(b["num_tokens"], dev), "num_rejected": i32(b["num_rejected"], dev),
+        "target_ids": i32(b["target_ids"], dev), "target_pos": i32(b["target_pos"], dev),
+        "target_hidden": bf16(b["target_hidden"], dev), "next_token_ids": i32(b["next_token_ids"], dev),
+        "block_table": i32(b["block_table"], dev), "h_shared": mdev["h_shared"],
+    }
+    out = pdx.alloc_batch(dims, dev)
+    cache = pdx.pack_kv_cache(bf16(pool["k"], dev), bf16(pool["v"], dev))
+    R = b["C"] * w.K
+    draft = torch.empty(R, dtype=torch.int32, device=dev)
+    h = pdx.Handle()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pdx.pd_expand_batch(dims, inp, out, stream)
+        pdx.pd_draft_forward(h, mdev, dims, out, inp["block_table"], cache, draft, None, stream)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = h.status() | int(out["status"].item())
+    if st:
+        raise SystemExit(f"device status {st} after warmup")
+    h.profile(1 << pdx.KERNEL_LMHEAD)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1)
+    lm_ms, lm_n = h.profile_read(pdx.KERNEL_LMHEAD)
+    h.profile(0)
+    ms_step = ms / args.steps
+    steps_s = 1000.0 / ms_step
+    lm_avg_s = lm_ms / max(lm_n, 1) / 1000.0
+    lm_b = lm_head_bytes(dm, R)
+    achieved = lm_b / lm_avg_s / 1e9
+    sb = step_bytes(dm, b, w.K)
+    log(f"[bench] {ms_step * 1000:.1f} us/step ({steps_s:.1f} steps/s, wall {wall * 1000 / args.steps:.1f} us/step); "
+        f"LM head {lm_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; whole step {sb / 1e9:.3f} GB algorithmic = "
+        f"{sb / (ms_step / 1000) / 1e9:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, model_np, b, pool)
+        log(f"[bench] oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores")
+        cpu.pop("seconds")
+
+    res = {
+        "metric": "draft steps/s & drafted tok/s (K=7) at C=1/4/64; % HBM / MFMA roofline",
+        "value": steps_s,
+        "unit": "draft steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "C": w.C, "K": w.K,
+                   "T_in": b["T_in"], "T_out": b["T_in"] + w.C * (w.K - 1)},
+        "drafted_tok_per_s": steps_s * R,
+        "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": "gemm_skinny_kernel<ARGMAX> (LM head + fused argmax)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    h.free()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

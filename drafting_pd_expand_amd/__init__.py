@@ -1,0 +1,348 @@
+"""Python binding of libpdexpand.so -- the P-EAGLE parallel-drafting step on MI355X.
+
+Argument marshalling only: every step of the drafting path runs in the HIP
+library (include/pd.h). The binding checks dtypes, devices, contiguity and
+sizes on the host, turns torch tensors into device pointers and calls the
+C ABI with the same names: pd_expand_batch, pd_draft_forward, pd_free.
+There is no CPU fallback: without the built library every call raises.
+
+Also here: helpers that allocate the expanded-batch buffers, move a model's
+bf16 weights to the device, and convert a slot-addressed KV cache to and from
+the library's paged layout (setup plumbing, outside the drafting step).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_void_p
+
+import numpy as np
+import torch
+
+__all__ = [
+    "PD_OK", "PD_EINVAL", "PD_ENOMEM", "PD_EHIP", "PD_PAGE", "PD_MAX_LAYERS",
+    "KERNEL_LMHEAD", "KERNEL_GEMM", "KERNEL_ATTN", "KERNEL_OTHER",
+    "PdError", "library_path", "load", "pd_expand_batch", "pd_draft_forward", "pd_free",
+    "Handle", "batch_dims", "alloc_batch", "device_model", "pack_kv_cache",
+    "unpack_kv_cache", "kv_cache_elems",
+]
+
+PD_OK, PD_EINVAL, PD_ENOMEM, PD_EHIP = 0, -1, -2, -3
+PD_PAGE = 16
+PD_MAX_LAYERS = 16
+KERNEL_LMHEAD, KERNEL_GEMM, KERNEL_ATTN, KERNEL_OTHER = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpdexpand.so")
+
+
+class PdError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {_strerror(code)} ({code})")
+        self.code = code
+
+
+class BatchDims(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in
+                ("C", "K", "T_in", "mask_token_id", "hidden3", "block_size", "max_blocks", "num_blocks")]
+
+
+class ExpandIn(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in
+                ("num_tokens", "num_rejected", "target_ids", "target_pos", "target_hidden",
+                 "next_token_ids", "block_table", "h_shared")]
+
+
+_BATCH_FIELDS = ("input_ids", "positions", "slot_mapping", "is_rejected", "is_masked",
+                 "hidden_state_mapping", "new_token_indices", "cu_out", "seq_lens", "hidden", "status")
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in _BATCH_FIELDS]
+
+
+_L = c_void_p * PD_MAX_LAYERS
+
+
+class Model(ctypes.Structure):
+    _fields_ = [(n, c_int32) for n in ("d", "Hq", "Hkv", "dh", "F", "N", "V", "hidden3")] + [
+        ("rms_eps", c_float), ("rope_theta", c_float),
+        ("embed", c_void_p), ("fc", c_void_p), ("norm_emb", c_void_p), ("norm_hid", c_void_p),
+        ("norm_in", _L), ("w_qkv", _L), ("w_o", _L), ("norm_post", _L),
+        ("w_gate", _L), ("w_up", _L), ("w_down", _L),
+        ("norm_final", c_void_p), ("lm_head", c_void_p),
+    ]
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run `python -m drafting_pd_expand_amd.build`)")
+    lib = ctypes.CDLL(path)
+    lib.pd_expand_batch.argtypes = [POINTER(BatchDims), POINTER(ExpandIn), POINTER(Batch), c_void_p]
+    lib.pd_expand_batch.restype = c_int
+    lib.pd_draft_forward.argtypes = [POINTER(c_void_p), POINTER(Model), POINTER(BatchDims),
+                                     POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+    lib.pd_draft_forward.restype = c_int
+    lib.pd_free.argtypes = [c_void_p]
+    lib.pd_free.restype = None
+    lib.pd_strerror.argtypes = [c_int]
+    lib.pd_strerror.restype = ctypes.c_char_p
+    lib.pd_status.argtypes = [c_void_p, POINTER(c_int32), c_void_p]
+    lib.pd_status.restype = c_int
+    lib.pd_set_debug_resid.argtypes = [c_void_p, c_void_p]
+    lib.pd_set_debug_resid.restype = c_int
+    lib.pd_profile.argtypes = [c_void_p, c_int]
+    lib.pd_profile.restype = c_int
+    lib.pd_profile_read.argtypes = [c_void_p, c_int, POINTER(c_double), POINTER(c_int64)]
+    lib.pd_profile_read.restype = c_int
+    _LIB = lib
+    return lib
+
+
+def _strerror(code: int) -> str:
+    try:
+        return load().pd_strerror(code).decode()
+    except Exception:  # pragma: no cover
+        return "error"
+
+
+def _check(code: int, what: str):
+    if code != PD_OK:
+        raise PdError(code, what)
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _dev(t, name, dtypes, numel=None, device=None, align=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device (cuda) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: has {t.numel()} elements, needs {numel}")
+    if align is None:
+        align = 16 if t.dtype in _BF16 or t.dtype == torch.float32 else 4
+    if t.data_ptr() % align:
+        raise ValueError(f"{name}: must be {align}-byte aligned")
+    return t.data_ptr()
+
+
+def batch_dims(C, K, T_in, mask_token_id, hidden3, max_blocks, num_blocks, block_size=PD_PAGE) -> dict:
+    return dict(C=int(C), K=int(K), T_in=int(T_in), mask_token_id=int(mask_token_id),
+                hidden3=int(hidden3), block_size=int(block_size), max_blocks=int(max_blocks),
+                num_blocks=int(num_blocks))
+
+
+def _dims_struct(d: dict) -> BatchDims:
+    return BatchDims(*[int(d[n]) for n, _ in BatchDims._fields_])
+
+
+def alloc_batch(dims: dict, device) -> dict:
+    """Allocate the expanded-batch buffers for `dims` (contents undefined)."""
+    C, K, T_in = dims["C"], dims["K"], dims["T_in"]
+    T_out = T_in + C * (K - 1)
+    i32 = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=device)
+    u8 = lambda n: torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return {
+        "input_ids": i32(T_out), "positions": i32(T_out), "slot_mapping": i32(T_out),
+        "is_rejected": u8(T_out), "is_masked": u8(T_out), "hidden_state_mapping": i32(T_in),
+        "new_token_indices": i32(C * K), "cu_out": i32(C + 1), "seq_lens": i32(C),
+        "hidden": torch.empty((max(T_out, 1), dims["hidden3"]), dtype=torch.bfloat16, device=device),
+        "status": torch.zeros(1, dtype=torch.int32, device=device),
+    }
+
+
+def _batch_struct(b: dict, dims: dict, device=None) -> Batch:
+    C, K, T_in = dims["C"], dims["K"], dims["T_in"]
+    T_out = T_in + C * (K - 1)
+    sizes = {"input_ids": T_out, "positions": T_out, "slot_mapping": T_out, "is_rejected": T_out,
+             "is_masked": T_out, "hidden_state_mapping": T_in, "new_token_indices": C * K,
+             "cu_out": C + 1, "seq_lens": C, "hidden": T_out * dims["hidden3"], "status": 1}
+    types = {"is_rejected": (torch.uint8,), "is_masked": (torch.uint8,), "hidden": _BF16}
+    aligns = {"is_rejected": 1, "is_masked": 1}
+    vals = []
+    for n in _BATCH_FIELDS:
+        if n == "status" and b.get("status") is None:
+            vals.append(None)
+            continue
+        vals.append(_dev(b[n], n, types.get(n, (torch.int32,)), sizes[n], device, aligns.get(n)))
+    return Batch(*vals)
+
+
+def pd_expand_batch(dims: dict, inp: dict, out: dict, stream=None) -> None:
+    """Enqueue the batch expansion (include/pd.h: pd_expand_batch)."""
+    lib = load()
+    C, T_in = dims["C"], dims["T_in"]
+    dev = inp["num_tokens"].device if C else None
+    ein = ExpandIn(
+        _dev(inp["num_tokens"], "num_tokens", (torch.int32,), C, dev),
+        _dev(inp["num_rejected"], "num_rejected", (torch.int32,), C, dev),
+        _dev(inp["target_ids"], "target_ids", (torch.int32,), T_in, dev),
+        _dev(inp["target_pos"], "target_pos", (torch.int32,), T_in, dev),
+        _dev(inp["target_hidden"], "target_hidden", _BF16, T_in * dims["hidden3"], dev),
+        _dev(inp["next_token_ids"], "next_token_ids", (torch.int32,), C, dev),
+        _dev(inp["block_table"], "block_table", (torch.int32,), C * dims["max_blocks"], dev),
+        _dev(inp["h_shared"], "h_shared", _BF16, dims["hidden3"], dev),
+    ) if C else ExpandIn()
+    bs = _batch_struct(out, dims, dev) if C else Batch()
+    d = _dims_struct(dims)
+    _check(lib.pd_expand_batch(ctypes.byref(d), ctypes.byref(ein), ctypes.byref(bs),
+                               c_void_p(_stream_ptr(stream))), "pd_expand_batch")
+
+
+class Handle:
+    """Owner of a pd_handle (library scratch for pd_draft_forward)."""
+
+    def __init__(self):
+        self.ptr = c_void_p(None)
+
+    def free(self):
+        if self.ptr.value:
+            load().pd_free(self.ptr)
+            self.ptr = c_void_p(None)
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.free()
+        except Exception:
+            pass
+
+    def status(self, stream=None) -> int:
+        if not self.ptr.value:
+            return 0
+        out = c_int32(0)
+        _check(load().pd_status(self.ptr, ctypes.byref(out), c_void_p(_stream_ptr(stream))), "pd_status")
+        return int(out.value)
+
+    def set_debug_resid(self, t):
+        _check(load().pd_set_debug_resid(self.ptr, c_void_p(t.data_ptr() if t is not None else None)),
+               "pd_set_debug_resid")
+
+    def profile(self, class_mask: int):
+        """Record events around launches of the kernel classes in class_mask
+        (bit 1 << KERNEL_*); 0 stops. Drops earlier records."""
+        _check(load().pd_profile(self.ptr, int(class_mask)), "pd_profile")
+
+    def profile_read(self, kernel_class: int):
+        ms, n = c_double(0), c_int64(0)
+        _check(load().pd_profile_read(self.ptr, int(kernel_class), ctypes.byref(ms), ctypes.byref(n)),
+               "pd_profile_read")
+        return float(ms.value), int(n.value)
+
+
+def _model_struct(m: dict) -> Model:
+    dm = m["dims"]
+    st = Model()
+    for n in ("d", "Hq", "Hkv", "dh", "F", "N", "V"):
+        setattr(st, n, int(getattr(dm, n)))
+    st.hidden3 = int(dm.hidden3)
+    st.rms_eps = float(dm.rms_eps)
+    st.rope_theta = float(dm.rope_theta)
+    P = lambda t, n: _dev(t, n, _BF16)
+    st.embed = P(m["embed"], "embed")
+    st.fc = P(m["fc"], "fc")
+    st.norm_emb = P(m["norm_emb"], "norm_emb")
+    st.norm_hid = P(m["norm_hid"], "norm_hid")
+    st.norm_final = P(m["norm_final"], "norm_final")
+    st.lm_head = P(m["lm_head"], "lm_head")
+    for l, L in enumerate(m["layers"]):
+        st.norm_in[l] = P(L["norm_in"], "norm_in")
+        st.w_qkv[l] = P(L["w_qkv"], "w_qkv")
+        st.w_o[l] = P(L["w_o"], "w_o")
+        st.norm_post[l] = P(L["norm_post"], "norm_post")
+        st.w_gate[l] = P(L["w_gate"], "w_gate")
+        st.w_up[l] = P(L["w_up"], "w_up")
+        st.w_down[l] = P(L["w_down"], "w_down")
+    return st
+
+
+def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block_table, kv_cache,
+                     draft_ids, logits=None, stream=None) -> None:
+    """Enqueue the drafter pass (include/pd.h: pd_draft_forward). `model` is a
+    dict made by device_model(); `batch` holds the expanded-batch tensors."""
+    lib = load()
+    dm = model["dims"]
+    C, K = dims["C"], dims["K"]
+    if C == 0:
+        return
+    dev = batch["input_ids"].device
+    ms = model.get("_struct")
+    if ms is None:
+        ms = model["_struct"] = _model_struct(model)
+    bs = _batch_struct(batch, dims, dev)
+    d = _dims_struct(dims)
+    bt = _dev(block_table, "block_table", (torch.int32,), C * dims["max_blocks"], dev)
+    kv = _dev(kv_cache, "kv_cache", _BF16, kv_cache_elems(dm, dims["num_blocks"]), dev)
+    di = _dev(draft_ids, "draft_ids", (torch.int32,), C * K, dev)
+    lg = _dev(logits, "logits", (torch.float32,), C * K * dm.V, dev) if logits is not None else None
+    _check(lib.pd_draft_forward(ctypes.byref(handle.ptr), ctypes.byref(ms), ctypes.byref(d),
+                                ctypes.byref(bs), c_void_p(bt), c_void_p(kv), c_void_p(di),
+                                c_void_p(lg), c_void_p(_stream_ptr(stream))), "pd_draft_forward")
+
+
+def pd_free(handle: Handle) -> None:
+    handle.free()
+
+
+# ----------------------------------------------------------------------------- setup plumbing
+
+def _to_dev_bf16(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(device).view(
+        torch.bfloat16)
+
+
+def device_model(model_np: dict, device) -> dict:
+    """Upload bf16-bit numpy weights (synth.make_model layout) to the device."""
+    up = lambda a: _to_dev_bf16(a, device)
+    out = {"dims": model_np["dims"], "layers": []}
+    for k in ("embed", "fc", "norm_emb", "norm_hid", "norm_final", "lm_head", "h_shared"):
+        out[k] = up(model_np[k])
+    for L in model_np["layers"]:
+        out["layers"].append({k: up(v) for k, v in L.items()})
+    return out
+
+
+def kv_cache_elems(dm, num_blocks: int) -> int:
+    return dm.N * 2 * num_blocks * dm.Hkv * PD_PAGE * dm.dh
+
+
+def pack_kv_cache(k_slots: torch.Tensor, v_slots: torch.Tensor) -> torch.Tensor:
+    """Slot-addressed K/V [N][num_blocks*16][Hkv][dh] -> the library's paged
+    cache [N][2][num_blocks][Hkv][16*dh] (K pages token-major, V pages
+    dim-major)."""
+    N, S, Hkv, dh = k_slots.shape
+    nb = S // PD_PAGE
+    kp = k_slots.reshape(N, nb, PD_PAGE, Hkv, dh).permute(0, 1, 3, 2, 4).reshape(N, nb, Hkv, PD_PAGE * dh)
+    vp = v_slots.reshape(N, nb, PD_PAGE, Hkv, dh).permute(0, 1, 3, 4, 2).reshape(N, nb, Hkv, PD_PAGE * dh)
+    return torch.stack([kp, vp], dim=1).contiguous()
+
+
+def unpack_kv_cache(cache: torch.Tensor, Hkv: int, dh: int):
+    """Inverse of pack_kv_cache: returns (k_slots, v_slots)."""
+    N, _, nb = cache.shape[:3]
+    kp = cache[:, 0].reshape(N, nb, Hkv, PD_PAGE, dh).permute(0, 1, 3, 2, 4).reshape(N, nb * PD_PAGE, Hkv, dh)
+    vp = cache[:, 1].reshape(N, nb, Hkv, dh, PD_PAGE).permute(0, 1, 4, 2, 3).reshape(N, nb * PD_PAGE, Hkv, dh)
+    return kp, vp

@@ -1,0 +1,404 @@
+// C ABI of the parallel-drafting step: argument checks, the handle's scratch,
+// the launch sequence of one drafter pass, status word and event timing.
+//
+// [Blog] = "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding
+// in vLLM" (summary page); [Paper] = "P-EAGLE: Parallel-Drafting EAGLE with
+// Scalable Training" (summary page); [arXiv] = its ScienceStack page.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "kernels.hpp"
+#include "pd.h"
+
+using namespace pd;
+
+struct pd_handle {
+    int device = -1;
+    char* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    int* counters = nullptr;
+    int counters_n = 0;
+    int32_t* status = nullptr;
+    float* dbg = nullptr;
+    int prof = 0;  // bit mask of recorded kernel classes
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[PD_KERNEL_CLASSES];
+    std::vector<hipEvent_t> spare;
+};
+
+namespace {
+
+constexpr int kMaxTin = 1 << 20;
+constexpr int kCounters = 1 << 14;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool dims_ok(const pd_batch_dims* d) {
+    if (!d) return false;
+    if (d->C < 0 || d->C > PD_MAX_C) return false;
+    if (d->K < 1 || d->K > PD_MAX_K) return false;
+    if (d->T_in < d->C || d->T_in > kMaxTin) return false;
+    if (d->hidden3 <= 0 || d->hidden3 % 8 != 0) return false;
+    if (d->block_size < 1 || d->max_blocks < 1 || d->num_blocks < 1) return false;
+    if ((long long)d->num_blocks * d->block_size > (1LL << 31) - 1) return false;
+    if ((long long)d->max_blocks * d->block_size > (1LL << 30)) return false;
+    return true;
+}
+
+hipEvent_t take_event(pd_handle* h) {
+    if (!h->spare.empty()) {
+        hipEvent_t e = h->spare.back();
+        h->spare.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Event pair around one launch when profiling is on.
+struct Timed {
+    pd_handle* h;
+    int cls;
+    hipStream_t s;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    Timed(pd_handle* h_, int cls_, hipStream_t s_) : h(h_), cls(cls_), s(s_) {
+        if (h->prof & (1 << cls)) {
+            e0 = take_event(h);
+            e1 = take_event(h);
+            if (e0 && e1) (void)hipEventRecord(e0, s);
+        }
+    }
+    ~Timed() {
+        if (e0 && e1) {
+            (void)hipEventRecord(e1, s);
+            h->ev[cls].emplace_back(e0, e1);
+        }
+    }
+};
+
+struct Layout {
+    size_t x, u, qkv, q, ao, act, z, ws, po, pml, amv, ami, total;
+    int T, R, nsmax, min_split, ntilesV;
+};
+
+Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
+    Layout L;
+    const int T = d->T_in + d->C * (d->K - 1);
+    const int R = d->C * d->K;
+    L.T = T;
+    L.R = R;
+    const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
+    const int hd = m->Hq * m->dh;
+    // split-KV: aim for ~2048 workgroups, at least 256 keys per split
+    L.min_split = 256;
+    L.nsmax = std::max(1, std::min(128, (2048 + d->C * m->Hkv - 1) / (d->C * m->Hkv)));
+    size_t ws = 0;
+    auto need = [&](int M, int N, int K, int epi) {
+        GemmPlan p = plan_gemm(M, N, K, epi);
+        ws = std::max(ws, gemm_ws_floats(p, M, N, epi));
+    };
+    need(T, m->d, m->hidden3, EPI_STORE_F32);
+    need(T, qkvw, 2 * m->d, EPI_STORE_BF16);
+    need(T, qkvw, m->d, EPI_STORE_BF16);
+    need(T, m->d, hd, EPI_RESID_F32);
+    need(T, m->F, m->d, EPI_SWIGLU);
+    need(T, m->d, m->F, EPI_RESID_F32);
+    L.ntilesV = plan_gemm(R, m->V, m->d, EPI_ARGMAX).ntiles;
+    size_t off = 0;
+    auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    L.x = carve((size_t)T * m->d * 4);
+    L.u = carve((size_t)T * 2 * m->d * 2);
+    L.qkv = carve((size_t)T * qkvw * 2);
+    L.q = carve((size_t)T * hd * 2);
+    L.ao = carve((size_t)T * hd * 2);
+    L.act = carve((size_t)T * m->F * 2);
+    L.z = carve((size_t)R * m->d * 2);
+    L.ws = carve(ws * 4);
+    L.po = carve((size_t)L.nsmax * T * hd * 4);
+    L.pml = carve((size_t)L.nsmax * T * m->Hq * 2 * 4);
+    L.amv = carve((size_t)R * L.ntilesV * 4);
+    L.ami = carve((size_t)R * L.ntilesV * 4);
+    L.total = off;
+    return L;
+}
+
+int ensure_scratch(pd_handle* h, size_t bytes, hipStream_t s) {
+    if (h->scratch_bytes >= bytes) return PD_OK;
+    if (h->scratch) {
+        (void)hipStreamSynchronize(s);
+        (void)hipFree(h->scratch);
+        h->scratch = nullptr;
+        h->scratch_bytes = 0;
+    }
+    const size_t want = bytes + bytes / 4;
+    if (hipMalloc(&h->scratch, want) != hipSuccess) {
+        h->scratch = nullptr;
+        return PD_ENOMEM;
+    }
+    h->scratch_bytes = want;
+    return PD_OK;
+}
+
+int create_handle(pd_handle** out) {
+    pd_handle* h = new (std::nothrow) pd_handle();
+    if (!h) return PD_ENOMEM;
+    (void)hipGetDevice(&h->device);
+    if (hipMalloc(&h->counters, kCounters * sizeof(int)) != hipSuccess ||
+        hipMalloc(&h->status, sizeof(int32_t)) != hipSuccess) {
+        pd_free(h);
+        return PD_ENOMEM;
+    }
+    h->counters_n = kCounters;
+    if (hipMemset(h->counters, 0, kCounters * sizeof(int)) != hipSuccess ||
+        hipMemset(h->status, 0, sizeof(int32_t)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        pd_free(h);
+        return PD_EHIP;
+    }
+    *out = h;
+    return PD_OK;
+}
+
+bool model_ok(const pd_model* m) {
+    if (!m) return false;
+    if (m->d <= 0 || m->d % 16 || m->F <= 0 || m->F % 16 || m->V <= 0 || m->V % 16) return false;
+    if (m->hidden3 != 3 * m->d) return false;
+    if (m->Hq <= 0 || m->Hkv <= 0 || m->Hq % m->Hkv) return false;
+    if (m->dh != 64 && m->dh != 128) return false;
+    if (m->N < 1 || m->N > PD_MAX_LAYERS) return false;
+    if (!(m->rms_eps > 0.f) || !(m->rope_theta > 0.f)) return false;
+    if (!m->embed || !m->fc || !m->norm_emb || !m->norm_hid || !m->norm_final || !m->lm_head)
+        return false;
+    for (int l = 0; l < m->N; ++l) {
+        if (!m->w_qkv[l] || !m->w_o[l] || !m->norm_post[l] || !m->w_gate[l] || !m->w_up[l] ||
+            !m->w_down[l])
+            return false;
+        if (l > 0 && !m->norm_in[l]) return false;
+    }
+    return true;
+}
+
+bool batch_ok(const pd_batch* b) {
+    return b && b->input_ids && b->positions && b->slot_mapping && b->is_rejected &&
+           b->is_masked && b->hidden_state_mapping && b->new_token_indices && b->cu_out &&
+           b->seq_lens && b->hidden;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pd_strerror(int code) {
+    switch (code) {
+        case PD_OK: return "ok";
+        case PD_EINVAL: return "invalid argument";
+        case PD_ENOMEM: return "device allocation failed";
+        case PD_EHIP: return "HIP launch error";
+        default: return "unknown error";
+    }
+}
+
+int pd_expand_batch(const pd_batch_dims* dims, const pd_expand_in* in, const pd_batch* out,
+                    void* stream) {
+    if (!dims_ok(dims) || !in || !out) return PD_EINVAL;
+    if (dims->C == 0) return PD_OK;
+    if (!in->num_tokens || !in->num_rejected || !in->target_ids || !in->target_pos ||
+        !in->target_hidden || !in->next_token_ids || !in->block_table || !in->h_shared)
+        return PD_EINVAL;
+    if (!batch_ok(out)) return PD_EINVAL;
+    if (((uintptr_t)in->target_hidden | (uintptr_t)in->h_shared | (uintptr_t)out->hidden) & 15)
+        return PD_EINVAL;
+    return launch_expand(*dims, *in, *out, (hipStream_t)stream);
+}
+
+int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
+                     const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
+                     int32_t* draft_ids, float* logits, void* stream) {
+    if (!hp || !model_ok(m) || !dims_ok(dims) || !batch_ok(b)) return PD_EINVAL;
+    if (dims->C == 0) return PD_OK;
+    if (dims->block_size != PD_PAGE || dims->hidden3 != m->hidden3) return PD_EINVAL;
+    if (!block_table || !kv_cache || !draft_ids) return PD_EINVAL;
+    if ((long long)dims->num_blocks * m->Hkv * PD_PAGE * m->dh * 2 * m->N > (1LL << 40))
+        return PD_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    int rc;
+    if (!*hp) {
+        if ((rc = create_handle(hp)) != PD_OK) return rc;
+    }
+    pd_handle* h = *hp;
+    const Layout L = plan_layout(m, dims);
+    if ((rc = ensure_scratch(h, L.total, s)) != PD_OK) return rc;
+    char* S = h->scratch;
+    float* x = (float*)(S + L.x);
+    uint16_t* u = (uint16_t*)(S + L.u);
+    uint16_t* qkv = (uint16_t*)(S + L.qkv);
+    uint16_t* q = (uint16_t*)(S + L.q);
+    uint16_t* ao = (uint16_t*)(S + L.ao);
+    uint16_t* act = (uint16_t*)(S + L.act);
+    uint16_t* z = (uint16_t*)(S + L.z);
+    float* ws = (float*)(S + L.ws);
+    const int T = L.T, R = L.R, d = m->d;
+    const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
+    const int hd = m->Hq * m->dh;
+    const size_t plane = (size_t)dims->num_blocks * m->Hkv * PD_PAGE * m->dh;
+    int32_t* st = h->status;
+
+    auto gemm = [&](int cls, int epi, const uint16_t* X, int ldx, const int32_t* xrows,
+                    int xlimit, const uint16_t* W, const uint16_t* W2, int M, int N, int K,
+                    float* yf, int ldyf, uint16_t* yb, int ldyb) -> int {
+        GemmPlan p = plan_gemm(M, N, K, epi);
+        if (p.splits > 1 && p.ntiles * p.mblocks > h->counters_n) return PD_EINVAL;
+        GemmArgs a;
+        std::memset(&a, 0, sizeof(a));
+        a.X = X; a.ldx = ldx; a.xrows = xrows; a.xrows_limit = xlimit;
+        a.W = W; a.W2 = W2; a.M = M; a.N = N; a.K = K;
+        a.ws = ws; a.counters = h->counters;
+        a.yf = yf; a.ldyf = ldyf; a.yb = yb; a.ldyb = ldyb;
+        a.logits = logits; a.ldlog = m->V;
+        a.amax_v = (float*)(S + L.amv); a.amax_i = (int*)(S + L.ami);
+        a.status = st;
+        Timed t(h, cls, s);
+        return launch_gemm(epi, p, a, s);
+    };
+    auto dbg = [&](int slot) -> int {
+        if (!h->dbg) return PD_OK;
+        return hipMemcpyAsync(h->dbg + (size_t)slot * T * d, x, (size_t)T * d * 4,
+                              hipMemcpyDeviceToDevice, s) == hipSuccess ? PD_OK : PD_EHIP;
+    };
+#define PD_TRY(expr) do { if ((rc = (expr)) != PD_OK) return rc; } while (0)
+
+    // fc projection 3d -> d: starts the residual stream
+    PD_TRY(gemm(PD_KERNEL_GEMM, EPI_STORE_F32, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr,
+                T, d, m->hidden3, x, d, nullptr, 0));
+    PD_TRY(dbg(0));
+    {
+        Timed t(h, PD_KERNEL_OTHER, s);
+        PD_TRY(launch_layer0_input(b->input_ids, m->embed, m->V, x, m->norm_emb, m->norm_hid, u, T,
+                                   d, m->rms_eps, st, s));
+    }
+    for (int l = 0; l < m->N; ++l) {
+        const int in_l = (l == 0) ? 2 * d : d;
+        if (l > 0) {
+            Timed t(h, PD_KERNEL_OTHER, s);
+            PD_TRY(launch_rmsnorm(x, d, nullptr, 0, T, m->norm_in[l], u, d, d, m->rms_eps, st, s));
+        }
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_STORE_BF16, u, in_l, nullptr, 0, m->w_qkv[l], nullptr, T,
+                    qkvw, in_l, nullptr, 0, qkv, qkvw));
+        uint16_t* kpl = kv_cache + (size_t)(2 * l) * plane;
+        uint16_t* vpl = kv_cache + (size_t)(2 * l + 1) * plane;
+        {
+            Timed t(h, PD_KERNEL_OTHER, s);
+            PD_TRY(launch_rope_cache(qkv, b->positions, b->slot_mapping, T, m->Hq, m->Hkv, m->dh,
+                                     m->rope_theta, q, kpl, vpl, dims->num_blocks, st, s));
+        }
+        AttnArgs aa;
+        aa.q = q; aa.kplane = kpl; aa.vplane = vpl;
+        aa.positions = b->positions; aa.is_rejected = b->is_rejected;
+        aa.cu_out = b->cu_out; aa.seq_lens = b->seq_lens; aa.block_table = block_table;
+        aa.C = dims->C; aa.T = T; aa.Hq = m->Hq; aa.Hkv = m->Hkv;
+        aa.max_blocks = dims->max_blocks; aa.num_blocks = dims->num_blocks;
+        aa.nsmax = L.nsmax; aa.min_split = L.min_split;
+        aa.scale_log2 = 1.4426950408889634f / sqrtf((float)m->dh);
+        aa.part_o = (float*)(S + L.po); aa.part_ml = (float*)(S + L.pml);
+        aa.out = ao; aa.status = st;
+        {
+            hipEvent_t e0 = nullptr, e1 = nullptr;
+            if (h->prof & (1 << PD_KERNEL_ATTN)) { e0 = take_event(h); e1 = take_event(h); }
+            rc = launch_attention(m->dh, aa, s, e0, e1);
+            if (e0 && e1) h->ev[PD_KERNEL_ATTN].emplace_back(e0, e1);
+            if (rc != PD_OK) return rc;
+        }
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_RESID_F32, ao, hd, nullptr, 0, m->w_o[l], nullptr, T, d, hd,
+                    x, d, nullptr, 0));
+        {
+            Timed t(h, PD_KERNEL_OTHER, s);
+            PD_TRY(launch_rmsnorm(x, d, nullptr, 0, T, m->norm_post[l], u, d, d, m->rms_eps, st, s));
+        }
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_SWIGLU, u, d, nullptr, 0, m->w_gate[l], m->w_up[l], T, m->F,
+                    d, nullptr, 0, act, m->F));
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_RESID_F32, act, m->F, nullptr, 0, m->w_down[l], nullptr, T,
+                    d, m->F, x, d, nullptr, 0));
+        PD_TRY(dbg(l + 1));
+    }
+    // final norm on the K sampled rows of every request, LM head, greedy argmax
+    {
+        Timed t(h, PD_KERNEL_OTHER, s);
+        PD_TRY(launch_rmsnorm(x, d, b->new_token_indices, T, R, m->norm_final, z, d, d, m->rms_eps,
+                              st, s));
+    }
+    PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, z, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
+                nullptr, 0, nullptr, 0));
+    {
+        Timed t(h, PD_KERNEL_OTHER, s);
+        PD_TRY(launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV,
+                                    draft_ids, st, s));
+    }
+#undef PD_TRY
+    return PD_OK;
+}
+
+void pd_free(pd_handle* h) {
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    for (auto& v : h->ev)
+        for (auto& p : v) {
+            (void)hipEventDestroy(p.first);
+            (void)hipEventDestroy(p.second);
+        }
+    for (auto e : h->spare) (void)hipEventDestroy(e);
+    if (h->scratch) (void)hipFree(h->scratch);
+    if (h->counters) (void)hipFree(h->counters);
+    if (h->status) (void)hipFree(h->status);
+    delete h;
+}
+
+int pd_status(pd_handle* h, int32_t* out, void* stream) {
+    if (!h || !out) return PD_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipStreamSynchronize(s) != hipSuccess) return PD_EHIP;
+    if (hipMemcpy(out, h->status, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+        return PD_EHIP;
+    if (hipMemset(h->status, 0, sizeof(int32_t)) != hipSuccess) return PD_EHIP;
+    return hipDeviceSynchronize() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+int pd_set_debug_resid(pd_handle* h, float* dst) {
+    if (!h) return PD_EINVAL;
+    h->dbg = dst;
+    return PD_OK;
+}
+
+int pd_profile(pd_handle* h, int class_mask) {
+    if (!h) return PD_EINVAL;
+    (void)hipDeviceSynchronize();
+    for (auto& v : h->ev) {
+        for (auto& p : v) {
+            h->spare.push_back(p.first);
+            h->spare.push_back(p.second);
+        }
+        v.clear();
+    }
+    h->prof = class_mask & ((1 << PD_KERNEL_CLASSES) - 1);
+    return PD_OK;
+}
+
+int pd_profile_read(pd_handle* h, int cls, double* total_ms, int64_t* launches) {
+    if (!h || cls < 0 || cls >= PD_KERNEL_CLASSES || !total_ms || !launches) return PD_EINVAL;
+    double tot = 0.0;
+    for (auto& p : h->ev[cls]) {
+        if (hipEventSynchronize(p.second) != hipSuccess) return PD_EHIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) return PD_EHIP;
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = (int64_t)h->ev[cls].size();
+    return PD_OK;
+}
+
+}  // extern "C"

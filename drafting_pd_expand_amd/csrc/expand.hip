@@ -1,0 +1,183 @@
+// Batch expansion for parallel drafting, one fused launch.
+//
+// [Blog] = "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding
+// in vLLM" (summary page), section "vLLM engineering details": the draft batch
+// no longer matches the verify batch because each request gains K-1 MASK
+// slots; ids, positions and hidden rows are expanded, positions grow, the
+// slot mapping and per-request starts are rebuilt, and the metadata (rejected
+// mask, MASK-slot mask, new-token indices, hidden-state map) is produced in a
+// single kernel; the hidden rows are scattered through the map and MASK rows
+// take the learned shared hidden state; rejected tokens get slot -1.
+// Section "P-EAGLE core method": slot i pairs the token of position i+1 with
+// the hidden state of position i; the NTP slot takes the sampled token.
+//
+// Design for gfx950: every workgroup recomputes the per-request start
+// indices with a block-wide prefix sum over <= 1024 counts (4 KB, L2
+// resident), so no second launch or global scratch is needed; it then owns a
+// few output rows, writes their metadata and copies each 3d-wide bf16 row with
+// 16-byte vector loads/stores (a full row is contiguous, so every wave issues
+// fully coalesced 1 KB transactions).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pd {
+
+namespace {
+
+constexpr int kRowsPerBlock = 2;
+
+struct ExpandArgs {
+    pd_batch_dims d;
+    pd_expand_in in;
+    pd_batch out;
+    int T_out;
+};
+
+__device__ __forceinline__ int slot_of(const int32_t* bt_row, int pos, int bs, int max_blocks,
+                                       int num_blocks, int32_t* status) {
+    if (pos < 0) { flag(status, PD_STATUS_BAD_POSITION); return -1; }
+    const int b = pos / bs;
+    if (b >= max_blocks) { flag(status, PD_STATUS_BAD_POSITION); return -1; }
+    const int page = bt_row[b];
+    if (page < 0 || page >= num_blocks) { flag(status, PD_STATUS_BAD_PAGE); return -1; }
+    return page * bs + pos % bs;
+}
+
+__global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
+    __shared__ int s_in[PD_MAX_C + 1];  // first input row of each request
+    __shared__ int s_n[PD_MAX_C];
+    __shared__ int s_v[PD_MAX_C];
+    __shared__ int s_scan[256];
+    __shared__ int s_bad;
+
+    const int C = a.d.C, K = a.d.K, tid = threadIdx.x;
+    const int T_in = a.d.T_in;
+    int32_t* status = a.out.status;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+
+    // counts: thread t owns requests 4t .. 4t+3
+    int cnt[4];
+    int sum = 0, bad = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = tid * 4 + i;
+        int n = 0;
+        if (r < C) {
+            n = a.in.num_tokens[r];
+            const int rho = a.in.num_rejected[r];
+            if (n < 1 || n > T_in || rho < 0 || rho >= n) {
+                bad = 1;
+                n = 1;
+            }
+            s_n[r] = n;
+            s_v[r] = n - ((rho >= 0 && rho < n) ? rho : 0);
+        }
+        cnt[i] = n;
+        sum += n;
+    }
+    if (bad) atomicOr(&s_bad, 1);
+    // inclusive scan of the per-thread sums (Hillis-Steele over 256 entries)
+    s_scan[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int t = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += t;
+        __syncthreads();
+    }
+    int run = s_scan[tid] - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = tid * 4 + i;
+        if (r < C) s_in[r] = run;
+        run += cnt[i];
+    }
+    if (tid == 0) s_in[C] = s_scan[255];
+    __syncthreads();
+    if (s_in[C] != T_in) s_bad = 1;  // benign race: every writer stores 1
+    __syncthreads();
+    if (s_bad) {
+        if (blockIdx.x == 0 && tid == 0) flag(status, PD_STATUS_BAD_COUNTS);
+        return;
+    }
+
+    const int H3 = a.d.hidden3;
+    const int bs = a.d.block_size, maxb = a.d.max_blocks, nb = a.d.num_blocks;
+
+    // per-request outputs: block 0 writes them
+    if (blockIdx.x == 0) {
+        for (int r = tid; r < C; r += 256) {
+            const int in0 = s_in[r];
+            const int p_ntp = a.in.target_pos[in0 + s_v[r] - 1];
+            a.out.cu_out[r] = in0 + r * (K - 1);
+            a.out.seq_lens[r] = p_ntp + K;
+        }
+        if (tid == 0) a.out.cu_out[C] = a.T_out;
+    }
+
+    for (int rr = 0; rr < kRowsPerBlock; ++rr) {
+        const int o = blockIdx.x * kRowsPerBlock + rr;
+        if (o >= a.T_out) break;
+        // request of row o: the last r whose first output row is <= o
+        int lo = 0, hi = C - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_in[mid] + mid * (K - 1) <= o) lo = mid; else hi = mid - 1;
+        }
+        const int r = lo;
+        const int in0 = s_in[r];
+        const int i = o - (in0 + r * (K - 1));
+        const int n = s_n[r], v = s_v[r];
+        const int32_t* bt_row = a.in.block_table + (size_t)r * maxb;
+        const uint16_t* src;
+        if (i < n) {
+            const int j = in0 + i;
+            src = a.in.target_hidden + (size_t)j * H3;
+            if (tid == 0) {
+                const int next = a.in.next_token_ids[r];
+                const int id = (i == v - 1 || i + 1 >= n) ? next : a.in.target_ids[j + 1];
+                const int pos = a.in.target_pos[j];
+                const bool rej = i >= v;
+                a.out.input_ids[o] = id;
+                a.out.positions[o] = pos;
+                a.out.is_rejected[o] = rej ? 1 : 0;
+                a.out.is_masked[o] = 0;
+                a.out.slot_mapping[o] = rej ? -1 : slot_of(bt_row, pos, bs, maxb, nb, status);
+                a.out.hidden_state_mapping[j] = o;
+                if (i == v - 1) a.out.new_token_indices[r * K] = o;
+            }
+        } else {
+            const int m = i - n + 1;  // 1 .. K-1
+            src = a.in.h_shared;
+            if (tid == 0) {
+                const int pos = a.in.target_pos[in0 + v - 1] + m;
+                a.out.input_ids[o] = a.d.mask_token_id;
+                a.out.positions[o] = pos;
+                a.out.is_rejected[o] = 0;
+                a.out.is_masked[o] = 1;
+                a.out.slot_mapping[o] = slot_of(bt_row, pos, bs, maxb, nb, status);
+                a.out.new_token_indices[r * K + m] = o;
+            }
+        }
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+        uint4* d4 = reinterpret_cast<uint4*>(a.out.hidden + (size_t)o * H3);
+        for (int c = tid; c < H3 / 8; c += 256) d4[c] = s4[c];
+    }
+}
+
+}  // namespace
+
+int launch_expand(const pd_batch_dims& d, const pd_expand_in& in, const pd_batch& out,
+                  hipStream_t s) {
+    ExpandArgs a;
+    a.d = d;
+    a.in = in;
+    a.out = out;
+    a.T_out = d.T_in + d.C * (d.K - 1);
+    const int grid = (a.T_out + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(expand_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+}  // namespace pd

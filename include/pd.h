@@ -1,0 +1,234 @@
+/*
+ * pd.h -- C ABI of the P-EAGLE parallel-drafting step on AMD MI355X (gfx950).
+ *
+ * Pages cited (titles; sections are those printed on the pages):
+ *   [Blog]  "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding
+ *           in vLLM" (summary page of the vLLM blog post)
+ *   [Paper] "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training"
+ *           (summary page)
+ *   [arXiv] ScienceStack page for arXiv 2602.01469 (the same paper)
+ *
+ * One draft step = pd_expand_batch + pd_draft_forward on one stream.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [dev] are device pointers (hipMalloc / torch CUDA
+ *     tensors on the current device); pointers to the structs themselves are
+ *     host pointers. bf16 values travel as uint16_t bit patterns.
+ *   - The caller owns every buffer it passes; the library never frees or
+ *     keeps caller memory beyond the call. Work is enqueued asynchronously on
+ *     `stream` (a hipStream_t; NULL = the null stream) and nothing waits for
+ *     it, except where a call says it may synchronize.
+ *   - Return codes: PD_OK, or PD_EINVAL for bad host arguments (nothing is
+ *     enqueued), PD_ENOMEM when a library scratch allocation fails, PD_EHIP
+ *     when a launch reports a HIP error.
+ *   - Device data is never trusted for addressing: an index that would fall
+ *     outside a buffer is skipped and a bit is set in a device status word
+ *     (PD_STATUS_*), which the caller reads after the stream is done.
+ */
+#ifndef PD_H
+#define PD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PD_OK      0
+#define PD_EINVAL (-1)
+#define PD_ENOMEM (-2)
+#define PD_EHIP   (-3)
+
+#define PD_MAX_C      1024  /* requests per step (the blog's serving runs allow 1024 sequences) */
+#define PD_MAX_K      16    /* draft depth; the blog's drafter predicts up to 10 tokens */
+#define PD_MAX_LAYERS 16
+#define PD_PAGE       16    /* KV page size (tokens) the forward's cache layout uses */
+
+/* Device status bits (ORed into a caller- or handle-owned int32). */
+#define PD_STATUS_BAD_COUNTS   1  /* n_r < 1, rho_r outside [0, n_r), or sum(n_r) != T_in   */
+#define PD_STATUS_BAD_POSITION 2  /* a position < 0 or past the block table's reach         */
+#define PD_STATUS_BAD_PAGE     4  /* a block-table entry outside [0, num_blocks)            */
+#define PD_STATUS_BAD_TOKEN    8  /* a token id outside [0, V)                              */
+#define PD_STATUS_BAD_ROW     16  /* row bookkeeping (cu_out / new-token index) inconsistent */
+
+/* Sizes of one draft step. [host]
+ *   C             requests, 0..PD_MAX_C (0 = nothing to do)
+ *   K             draft depth, 1..PD_MAX_K (K = 1 is autoregressive EAGLE's single pass)
+ *   T_in          rows of the verify batch = sum of num_tokens
+ *   mask_token_id the MASK placeholder's token id ([Blog] fused-kernel paragraph)
+ *   hidden3       width of a target hidden row (3d; [arXiv] Figure 2), multiple of 8
+ *   block_size    KV page size in tokens (pd_draft_forward needs PD_PAGE)
+ *   max_blocks    columns of the block table
+ *   num_blocks    pages in the KV pool; valid block-table entries are < num_blocks
+ * The expanded batch has T_out = T_in + C*(K-1) rows. */
+typedef struct {
+    int32_t C, K, T_in, mask_token_id, hidden3, block_size, max_blocks, num_blocks;
+} pd_batch_dims;
+
+/* The verify batch the expansion reads. All [dev]. */
+typedef struct {
+    const int32_t*  num_tokens;     /* [C]  n_r >= 1 verify tokens of request r                 */
+    const int32_t*  num_rejected;   /* [C]  rho_r in [0, n_r): the last rho_r were rejected      */
+    const int32_t*  target_ids;     /* [T_in] token ids, request-major                          */
+    const int32_t*  target_pos;     /* [T_in] positions (consecutive within a request)           */
+    const uint16_t* target_hidden;  /* [T_in][hidden3] bf16 target hidden rows                   */
+    const int32_t*  next_token_ids; /* [C]  the token the target sampled for request r          */
+    const int32_t*  block_table;    /* [C][max_blocks] page numbers                              */
+    const uint16_t* h_shared;       /* [hidden3] bf16 learned shared hidden state                */
+} pd_expand_in;
+
+/* The expanded (draft) batch: written by pd_expand_batch, read by
+ * pd_draft_forward. All [dev], sized by the caller. */
+typedef struct {
+    int32_t*  input_ids;            /* [T_out] */
+    int32_t*  positions;            /* [T_out] */
+    int32_t*  slot_mapping;         /* [T_out] page*block_size + offset; -1 = rejected, no KV write */
+    uint8_t*  is_rejected;          /* [T_out] 1 for a rejected verify token                    */
+    uint8_t*  is_masked;            /* [T_out] 1 for a MASK (parallel-drafting) slot             */
+    int32_t*  hidden_state_mapping; /* [T_in]  target row j -> expanded row                     */
+    int32_t*  new_token_indices;    /* [C*K]   request-major: the NTP row, then the K-1 MASK rows */
+    int32_t*  cu_out;               /* [C+1]   first expanded row of each request; cu_out[C] = T_out */
+    int32_t*  seq_lens;             /* [C]     keys visible to the request's last row (p_ntp + K) */
+    uint16_t* hidden;               /* [T_out][hidden3] bf16 expanded hidden rows                */
+    int32_t*  status;               /* [1] or NULL: PD_STATUS_* bits ORed in on bad device data  */
+} pd_batch;
+
+/*
+ * pd_expand_batch -- build the draft batch from the verify batch.
+ *
+ * Follows [Blog] "vLLM engineering details": the draft batch appends MASK
+ * slots after each request's tokens, so ids, hidden rows and positions are
+ * expanded, positions grow, and the slot mapping and per-request starts are
+ * rebuilt; one fused launch copies ids/positions into their new slots,
+ * inserts the sampled token, fills the MASK ids and emits the rejected-token
+ * mask, the MASK-slot mask, the new-token indices and the hidden-state map;
+ * target hidden rows are scattered through that map and MASK rows take
+ * h_shared; rejected tokens get slot -1 so no KV entry is written for them.
+ * The pairing is the one-position shift of [Blog] "P-EAGLE core method"
+ * (slot i: token i+1 with hidden i; the last accepted slot: the sampled token).
+ *
+ * For request r with n_r tokens, rho_r rejected, v_r = n_r - rho_r, starting
+ * at input row a_r and output row b_r = a_r + r*(K-1):
+ *   row b_r+i (i < n_r): id = next_r if i == v_r-1 or i == n_r-1, else
+ *     target_ids[a_r+i+1]; position = target_pos[a_r+i]; rejected iff
+ *     i >= v_r; hidden = target_hidden[a_r+i].
+ *   row b_r+n_r+m-1 (m = 1..K-1): id = mask_token_id, position = p_ntp + m
+ *     with p_ntp = target_pos[a_r+v_r-1]; hidden = h_shared.
+ *   seq_lens[r] = p_ntp + K.
+ * The hidden rows are copied bit-for-bit.
+ *
+ * Errors: PD_EINVAL if dims/in/out or a required pointer is NULL, C outside
+ * [0, PD_MAX_C], K outside [1, PD_MAX_K], T_in < C, hidden3 <= 0 or not a
+ * multiple of 8, block_size < 1, max_blocks < 1 or num_blocks < 1. C = 0 is a
+ * no-op. Bad device data sets out->status bits (if given) and never makes the
+ * kernel read or write outside the buffers sized above.
+ */
+int pd_expand_batch(const pd_batch_dims* dims, const pd_expand_in* in,
+                    const pd_batch* out, void* stream);
+
+/* Drafter weights. [host] struct of [dev] bf16 pointers, row-major [out][in].
+ * Layer 0 takes [RMSNorm(emb; norm_emb) || RMSNorm(fc(h); norm_hid)] (2d wide)
+ * into its QKV projection and starts the residual stream at fc(h); layers
+ * 1..N-1 are pre-norm LLaMA layers ([Paper] sec. 2 architecture and experiment
+ * setup; [Blog] Input_i equation; [arXiv] Figure 2). */
+typedef struct {
+    int32_t d, Hq, Hkv, dh, F, N, V, hidden3;
+    float   rms_eps, rope_theta;
+    const uint16_t* embed;                    /* [V][d]                                    */
+    const uint16_t* fc;                       /* [d][hidden3]                              */
+    const uint16_t* norm_emb;                 /* [d]                                       */
+    const uint16_t* norm_hid;                 /* [d]                                       */
+    const uint16_t* norm_in[PD_MAX_LAYERS];   /* [d] (layers >= 1)                         */
+    const uint16_t* w_qkv[PD_MAX_LAYERS];     /* [(Hq+2*Hkv)*dh][2d at layer 0, else d]; q, k, v row blocks */
+    const uint16_t* w_o[PD_MAX_LAYERS];       /* [d][Hq*dh]                                */
+    const uint16_t* norm_post[PD_MAX_LAYERS]; /* [d]                                       */
+    const uint16_t* w_gate[PD_MAX_LAYERS];    /* [F][d]                                    */
+    const uint16_t* w_up[PD_MAX_LAYERS];      /* [F][d]                                    */
+    const uint16_t* w_down[PD_MAX_LAYERS];    /* [d][F]                                    */
+    const uint16_t* norm_final;               /* [d]                                       */
+    const uint16_t* lm_head;                  /* [V][d]                                    */
+} pd_model;
+
+typedef struct pd_handle pd_handle;
+
+/*
+ * pd_draft_forward -- the one drafter pass that yields all K draft tokens of
+ * every request ([Blog] "P-EAGLE core method": all positions go through the
+ * N layers and the LM head together).
+ *
+ * Computes, for every non-rejected row of the expanded batch: fc projection
+ * (hidden3 -> d), the layer-0 input above, N layers of [RMSNorm] -> QKV ->
+ * rotate-half RoPE at the row's position (base rope_theta) -> K/V written to
+ * the cache at slot_mapping (rows with slot -1 write nothing; [Blog] KV-cache
+ * paragraph) -> causal GQA attention over positions 0..p of the row's own
+ * request, read through block_table -> O projection + residual -> RMSNorm ->
+ * SwiGLU MLP + residual; then the final RMSNorm and LM head on the K rows
+ * named by new_token_indices, and the greedy argmax (lowest index on ties).
+ * Within a layer every K/V write lands before any row attends. Rejected
+ * rows are computed as don't-care values and influence nothing.
+ *
+ * Arguments:
+ *   h          [host] handle slot: *h == NULL creates the handle (scratch is
+ *              allocated then, and again, after a stream synchronize, when a
+ *              later call needs more). One handle serves one stream at a time.
+ *   m          [host] model; requires d, F, V multiples of 16, hidden3 = 3d,
+ *              Hq % Hkv == 0, dh in {64, 128}, 1 <= N <= PD_MAX_LAYERS,
+ *              every weight pointer non-NULL.
+ *   dims       [host] the same sizes given to pd_expand_batch; block_size must
+ *              be PD_PAGE.
+ *   batch      [host] struct of [dev] pointers written by pd_expand_batch
+ *              (status may be NULL).
+ *   block_table[dev] [C][max_blocks].
+ *   kv_cache   [dev] bf16, N layers x {K plane, V plane}; each plane is
+ *              [num_blocks][Hkv][PD_PAGE*dh]: a K page is token-major
+ *              [16][dh], a V page is dim-major [dh][16]. Element (layer l,
+ *              plane t, page b, head g, token s, dim c) sits at
+ *              ((l*2+t)*num_blocks + b)*Hkv*16*dh + g*16*dh + (t ? c*16+s : s*dh+c).
+ *   draft_ids  [dev] int32 [C*K] out, request-major like new_token_indices.
+ *   logits     [dev] float [C*K][V] out, or NULL.
+ * Errors: PD_EINVAL on bad host arguments (nothing enqueued), PD_ENOMEM,
+ * PD_EHIP. Bad device data sets bits in the handle's status word
+ * (pd_status) and never leads to an out-of-bounds access.
+ */
+int pd_draft_forward(pd_handle** h, const pd_model* m, const pd_batch_dims* dims,
+                     const pd_batch* batch, const int32_t* block_table,
+                     uint16_t* kv_cache, int32_t* draft_ids, float* logits, void* stream);
+
+/* Free a handle and its scratch (NULL-safe; waits for the handle's device
+ * work to finish). Never frees caller memory. */
+void pd_free(pd_handle* h);
+
+/* ---- extras ---------------------------------------------------------------- */
+
+/* Text for a PD_* return code. */
+const char* pd_strerror(int code);
+
+/* Synchronize `stream`, copy the handle's PD_STATUS_* word to *out [host] and
+ * clear it. PD_EINVAL if h or out is NULL. */
+int pd_status(pd_handle* h, int32_t* out, void* stream);
+
+/* Optional copy of the residual stream: when dst [dev] is non-NULL, later
+ * pd_draft_forward calls write float [N+1][T_out][d] (after fc, then after
+ * each layer). Pass NULL to stop. */
+int pd_set_debug_resid(pd_handle* h, float* dst);
+
+/* Per-kernel timing with HIP events on the launch stream. Kernel classes: */
+#define PD_KERNEL_LMHEAD  0   /* LM-head GEMM with the fused argmax partials     */
+#define PD_KERNEL_GEMM    1   /* every other GEMM (fc, QKV, O, gate/up, down)    */
+#define PD_KERNEL_ATTN    2   /* split-KV paged attention (not the merge)         */
+#define PD_KERNEL_OTHER   3   /* norms, RoPE+cache, merge, argmax reduce          */
+#define PD_KERNEL_CLASSES 4
+/* class_mask != 0 starts recording an event pair around every launch of the
+ * kernel classes whose bit (1 << PD_KERNEL_*) is set, for later
+ * pd_draft_forward calls with this handle; 0 stops. Either way the records
+ * collected so far are dropped (after a device synchronize). */
+int pd_profile(pd_handle* h, int class_mask);
+/* Wait for the recorded events and return the summed duration (ms) and the
+ * launch count of one kernel class since profiling was enabled. */
+int pd_profile_read(pd_handle* h, int kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PD_H */

@@ -1,0 +1,153 @@
+"""GPU parity of the whole drafting step (pd_expand_batch + pd_draft_forward,
+through the C ABI) against the oracle.
+
+Small models cover every row (and the residual stream layer by layer); the
+full-size workloads are checked on every request when the oracle is quick
+(C <= 4) and on sampled requests otherwise (requests are independent, so a
+request's outputs can be computed alone). Also: K = 1, dh = 128, GQA groups
+of 1, 4 and 8, causality and determinism (bit-identical), page relabelling
+(bit-identical), request independence, and the status word on bad data.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from harness import Case, check_case, check_logits, gpu_expand
+
+pytestmark = pytest.mark.gpu
+
+GQA64 = synth.ModelDims("gqa64", d=256, Hq=8, Hkv=2, dh=64, F=512, N=2, V=2048)
+GQA128 = synth.ModelDims("gqa128", d=512, Hq=4, Hkv=1, dh=128, F=1024, N=2, V=1024)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_tiny_prefill_all_rows_and_layers():
+    w = synth.get_workload("tiny")
+    _say(f"[forward] tiny C={w.C} K={w.K}")
+    c = Case(w, debug_resid=True).run()
+    assert c.status() == 0
+    res = check_case(c, check_layers=True)
+    _say(f"  worst logit err/RMS {res['worst_logit_ratio']:.4g}")
+    c.close()
+
+
+@pytest.mark.parametrize("dims,C,K,ctx,L", [
+    (GQA64, 5, 5, "lognormal", 0),
+    (GQA64, 4, 1, "fixed", 777),
+    (GQA64, 3, 16, "fixed", 40),
+    (GQA128, 3, 7, "fixed", 1000),
+    (GQA128, 2, 3, "lognormal", 0),
+], ids=["gqa64-c5k5", "gqa64-k1", "gqa64-k16", "gqa128-c3k7", "gqa128-c2k3"])
+def test_small_models_all_rows(dims, C, K, ctx, L):
+    w = synth.Workload(f"{dims.name}-c{C}k{K}", dims, C=C, K=K, context=ctx, L=L, seed=17 + C + K)
+    _say(f"[forward] {w.name}")
+    c = Case(w, debug_resid=True).run()
+    assert c.status() == 0
+    res = check_case(c, check_layers=True)
+    _say(f"  worst logit err/RMS {res['worst_logit_ratio']:.4g}")
+    c.close()
+
+
+def _sample(b, K, k=3):
+    """Requests to check at large C: the longest context, the most rejections, the first."""
+    L = b["context_lens"]
+    picks = [int(np.argmax(L)), int(np.argmax(b["num_rejected"])), 0]
+    out = []
+    for p in picks:
+        if p not in out:
+            out.append(p)
+    return out[:k]
+
+
+@pytest.mark.parametrize("name", ["g_c1", "g_c4", "g_c64", "g_c64_k3", "g_c64_k5", "q_c16"])
+def test_full_size_workloads(name):
+    w = synth.get_workload(name)
+    _say(f"[forward] {name} C={w.C} K={w.K}")
+    c = Case(w).run()
+    assert c.status() == 0
+    reqs = None if w.C <= 4 else _sample(c.b, w.K, 3 if w.C >= 64 else 2)
+    res = check_case(c, requests=reqs)
+    _say(f"  requests {reqs or 'all'}: worst logit err/RMS {res['worst_logit_ratio']:.4g}, "
+         f"argmax checked {res['argmax_checked']}/{res['rows']}")
+    c.close()
+
+
+def test_causality_and_determinism_bit_identical():
+    """(c) perturbing the last MASK row of every request changes nothing before
+    it; a repeated step is bit-identical."""
+    w = synth.Workload("gqa64-causal", GQA64, C=4, K=6, context="lognormal", seed=23)
+    c = Case(w).run()
+    base = c.logits.clone()
+    base_ids = c.draft.clone()
+    c.run()
+    assert torch.equal(c.logits, base) and torch.equal(c.draft, base_ids)
+    nti = c.out["new_token_indices"].cpu().numpy().reshape(w.C, w.K)
+    last = torch.from_numpy(nti[:, -1].astype(np.int64)).to(c.dev)
+    g = torch.Generator(device="cpu").manual_seed(3)
+    noise = torch.randn((w.C, w.model.hidden3), generator=g).to(torch.bfloat16).to(c.dev)
+    c.out["hidden"][last] = noise
+    c.out["input_ids"][last] = 7
+    c.run()
+    keep = np.array([r * w.K + m for r in range(w.C) for m in range(w.K - 1)])
+    keep_t = torch.from_numpy(keep).to(c.dev)
+    assert torch.equal(c.logits[keep_t], base[keep_t])
+    lastrows = torch.arange(w.K - 1, w.C * w.K, w.K, device=c.dev)
+    assert not torch.equal(c.logits[lastrows], base[lastrows])
+    c.close()
+
+
+def test_page_relabelling_is_bit_identical():
+    w = synth.Workload("gqa64-pages", GQA64, C=3, K=5, context="lognormal", seed=29)
+    c1 = Case(w).run()
+    b = dict(c1.b)
+    nb = b["num_blocks"]
+    perm = np.random.default_rng(1).permutation(nb)          # old page -> new page
+    bt = b["block_table"]
+    b["block_table"] = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1).astype(np.int32)
+    c2 = Case(w, batch=b)
+    src = np.argsort(perm)
+    sl = (src[:, None] * 16 + np.arange(16)).reshape(-1)
+    import drafting_pd_expand_amd as pdx
+    from harness import bf16
+    k = bf16(c1.pool["k"][:, sl], c2.dev)
+    v = bf16(c1.pool["v"][:, sl], c2.dev)
+    c2.cache = pdx.pack_kv_cache(k, v)
+    c2.run()
+    assert torch.equal(c1.logits, c2.logits)
+    assert torch.equal(c1.draft, c2.draft)
+    c1.close(); c2.close()
+
+
+def test_request_alone_matches_batch():
+    w = synth.Workload("gqa64-indep", GQA64, C=4, K=5, context="lognormal", seed=31)
+    c = Case(w).run()
+    r = 2
+    b = c.b
+    lo = int(b["num_tokens"][:r].sum())
+    hi = lo + int(b["num_tokens"][r])
+    one = dict(b)
+    one.update(C=1, T_in=hi - lo, num_tokens=b["num_tokens"][r:r + 1], num_rejected=b["num_rejected"][r:r + 1],
+               target_ids=b["target_ids"][lo:hi], target_pos=b["target_pos"][lo:hi],
+               target_hidden=b["target_hidden"][lo:hi], next_token_ids=b["next_token_ids"][r:r + 1],
+               block_table=b["block_table"][r:r + 1], context_lens=b["context_lens"][r:r + 1])
+    c1 = Case(w, batch=one).run()
+    got = c1.logits.cpu().numpy()
+    want = c.logits[r * w.K:(r + 1) * w.K].cpu().numpy().astype(np.float64)
+    check_logits(got, want, tol=0.01)
+    c.close(); c1.close()
+
+
+def test_bad_token_and_page_flagged_in_forward():
+    """Bad ids / slots reaching the forward are flagged and skipped (no fault)."""
+    w = synth.Workload("gqa64-bad", GQA64, C=2, K=3, context="fixed", L=50, seed=37)
+    c = Case(w)
+    c.out["input_ids"][0] = GQA64.V + 5
+    c.out["slot_mapping"][1] = 10 ** 8
+    c.run()
+    st = c.handle.status()
+    assert st & 8 and st & 4
+    c.close()
