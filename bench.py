@@ -54,7 +54,7 @@ def lm_head_bytes(dm, R: int) -> int:
 def step_bytes(dm, b, K: int) -> int:
     """Algorithmic bytes of one whole step (weights once, visible KV once per
     layer and kv head, KV writes, hidden rows in and out, ids)."""
-    w = dm.V * dm.d * 2 * 2 + dm.d * dm.hidden3 * 2
+    w = dm.V * dm.d * 2 + dm.d * dm.hidden3 * 2          # LM head + fc (embedding rows: gathered, below)
     for l in range(dm.N):
         w += dm.qkv_out * dm.qkv_in(l) * 2 + dm.d * dm.Hq * dm.dh * 2 + 3 * dm.F * dm.d * 2 + 4 * dm.d * 2
     C = b["C"]

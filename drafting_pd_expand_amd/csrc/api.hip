@@ -21,8 +21,6 @@ struct pd_handle {
     int device = -1;
     char* scratch = nullptr;
     size_t scratch_bytes = 0;
-    int* counters = nullptr;
-    int counters_n = 0;
     int32_t* status = nullptr;
     float* dbg = nullptr;
     int prof = 0;  // bit mask of recorded kernel classes
@@ -33,7 +31,6 @@ struct pd_handle {
 namespace {
 
 constexpr int kMaxTin = 1 << 20;
-constexpr int kCounters = 1 << 14;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -82,7 +79,7 @@ struct Timed {
 };
 
 struct Layout {
-    size_t x, u, qkv, q, ao, act, z, ws, po, pml, amv, ami, total;
+    size_t x, u, q, ao, act, ws, po, pml, amv, ami, total;
     int T, R, nsmax, min_split, ntilesV;
 };
 
@@ -94,30 +91,27 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
     L.R = R;
     const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
     const int hd = m->Hq * m->dh;
-    // split-KV: aim for ~2048 workgroups, at least 256 keys per split
-    L.min_split = 256;
+    // split-KV: aim for ~2048 workgroups, at least min_split keys per split
+    L.min_split = 128;
     L.nsmax = std::max(1, std::min(128, (2048 + d->C * m->Hkv - 1) / (d->C * m->Hkv)));
     size_t ws = 0;
-    auto need = [&](int M, int N, int K, int epi) {
-        GemmPlan p = plan_gemm(M, N, K, epi);
-        ws = std::max(ws, gemm_ws_floats(p, M, N, epi));
+    auto need = [&](int M, int N, int K) {
+        GemmPlan p = plan_gemm(M, N, K, EPI_PARTIAL);
+        ws = std::max(ws, gemm_ws_floats(p, M, N, EPI_PARTIAL));
     };
-    need(T, m->d, m->hidden3, EPI_STORE_F32);
-    need(T, qkvw, 2 * m->d, EPI_STORE_BF16);
-    need(T, qkvw, m->d, EPI_STORE_BF16);
-    need(T, m->d, hd, EPI_RESID_F32);
-    need(T, m->F, m->d, EPI_SWIGLU);
-    need(T, m->d, m->F, EPI_RESID_F32);
+    need(T, m->d, m->hidden3);
+    need(T, qkvw, 2 * m->d);
+    need(T, qkvw, m->d);
+    need(T, m->d, hd);
+    need(T, m->d, m->F);
     L.ntilesV = plan_gemm(R, m->V, m->d, EPI_ARGMAX).ntiles;
     size_t off = 0;
     auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     L.x = carve((size_t)T * m->d * 4);
     L.u = carve((size_t)T * 2 * m->d * 2);
-    L.qkv = carve((size_t)T * qkvw * 2);
     L.q = carve((size_t)T * hd * 2);
     L.ao = carve((size_t)T * hd * 2);
     L.act = carve((size_t)T * m->F * 2);
-    L.z = carve((size_t)R * m->d * 2);
     L.ws = carve(ws * 4);
     L.po = carve((size_t)L.nsmax * T * hd * 4);
     L.pml = carve((size_t)L.nsmax * T * m->Hq * 2 * 4);
@@ -148,14 +142,11 @@ int create_handle(pd_handle** out) {
     pd_handle* h = new (std::nothrow) pd_handle();
     if (!h) return PD_ENOMEM;
     (void)hipGetDevice(&h->device);
-    if (hipMalloc(&h->counters, kCounters * sizeof(int)) != hipSuccess ||
-        hipMalloc(&h->status, sizeof(int32_t)) != hipSuccess) {
+    if (hipMalloc(&h->status, sizeof(int32_t)) != hipSuccess) {
         pd_free(h);
         return PD_ENOMEM;
     }
-    h->counters_n = kCounters;
-    if (hipMemset(h->counters, 0, kCounters * sizeof(int)) != hipSuccess ||
-        hipMemset(h->status, 0, sizeof(int32_t)) != hipSuccess ||
+    if (hipMemset(h->status, 0, sizeof(int32_t)) != hipSuccess ||
         hipDeviceSynchronize() != hipSuccess) {
         pd_free(h);
         return PD_EHIP;
@@ -166,7 +157,8 @@ int create_handle(pd_handle** out) {
 
 bool model_ok(const pd_model* m) {
     if (!m) return false;
-    if (m->d <= 0 || m->d % 16 || m->F <= 0 || m->F % 16 || m->V <= 0 || m->V % 16) return false;
+    if (m->d <= 0 || m->d % 16 || m->d > 4096 || m->F <= 0 || m->F % 16 || m->V <= 0 || m->V % 16)
+        return false;
     if (m->hidden3 != 3 * m->d) return false;
     if (m->Hq <= 0 || m->Hkv <= 0 || m->Hq % m->Hkv) return false;
     if (m->dh != 64 && m->dh != 128) return false;
@@ -236,11 +228,9 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     char* S = h->scratch;
     float* x = (float*)(S + L.x);
     uint16_t* u = (uint16_t*)(S + L.u);
-    uint16_t* qkv = (uint16_t*)(S + L.qkv);
     uint16_t* q = (uint16_t*)(S + L.q);
     uint16_t* ao = (uint16_t*)(S + L.ao);
     uint16_t* act = (uint16_t*)(S + L.act);
-    uint16_t* z = (uint16_t*)(S + L.z);
     float* ws = (float*)(S + L.ws);
     const int T = L.T, R = L.R, d = m->d;
     const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
@@ -248,17 +238,17 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     const size_t plane = (size_t)dims->num_blocks * m->Hkv * PD_PAGE * m->dh;
     int32_t* st = h->status;
 
+    // one projection; returns its split count through *splits (EPI_PARTIAL)
     auto gemm = [&](int cls, int epi, const uint16_t* X, int ldx, const int32_t* xrows,
                     int xlimit, const uint16_t* W, const uint16_t* W2, int M, int N, int K,
-                    float* yf, int ldyf, uint16_t* yb, int ldyb) -> int {
+                    uint16_t* yb, int ldyb, int* splits) -> int {
         GemmPlan p = plan_gemm(M, N, K, epi);
-        if (p.splits > 1 && p.ntiles * p.mblocks > h->counters_n) return PD_EINVAL;
+        if (splits) *splits = p.splits;
         GemmArgs a;
         std::memset(&a, 0, sizeof(a));
         a.X = X; a.ldx = ldx; a.xrows = xrows; a.xrows_limit = xlimit;
         a.W = W; a.W2 = W2; a.M = M; a.N = N; a.K = K;
-        a.ws = ws; a.counters = h->counters;
-        a.yf = yf; a.ldyf = ldyf; a.yb = yb; a.ldyb = ldyb;
+        a.ws = ws; a.yb = yb; a.ldyb = ldyb;
         a.logits = logits; a.ldlog = m->V;
         a.amax_v = (float*)(S + L.amv); a.amax_i = (int*)(S + L.ami);
         a.status = st;
@@ -271,29 +261,26 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
                               hipMemcpyDeviceToDevice, s) == hipSuccess ? PD_OK : PD_EHIP;
     };
 #define PD_TRY(expr) do { if ((rc = (expr)) != PD_OK) return rc; } while (0)
+    int sp = 1;
 
-    // fc projection 3d -> d: starts the residual stream
-    PD_TRY(gemm(PD_KERNEL_GEMM, EPI_STORE_F32, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr,
-                T, d, m->hidden3, x, d, nullptr, 0));
-    PD_TRY(dbg(0));
+    // fc projection 3d -> d (starts the residual stream), then the layer-0 input
+    PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr, T, d,
+                m->hidden3, nullptr, 0, &sp));
     {
         Timed t(h, PD_KERNEL_OTHER, s);
-        PD_TRY(launch_layer0_input(b->input_ids, m->embed, m->V, x, m->norm_emb, m->norm_hid, u, T,
-                                   d, m->rms_eps, st, s));
+        PD_TRY(launch_layer0_input(ws, sp, b->input_ids, m->embed, m->V, x, m->norm_emb, m->norm_hid,
+                                   u, T, d, m->rms_eps, st, s));
     }
+    PD_TRY(dbg(0));
     for (int l = 0; l < m->N; ++l) {
         const int in_l = (l == 0) ? 2 * d : d;
-        if (l > 0) {
-            Timed t(h, PD_KERNEL_OTHER, s);
-            PD_TRY(launch_rmsnorm(x, d, nullptr, 0, T, m->norm_in[l], u, d, d, m->rms_eps, st, s));
-        }
-        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_STORE_BF16, u, in_l, nullptr, 0, m->w_qkv[l], nullptr, T,
-                    qkvw, in_l, nullptr, 0, qkv, qkvw));
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, u, in_l, nullptr, 0, m->w_qkv[l], nullptr, T, qkvw,
+                    in_l, nullptr, 0, &sp));
         uint16_t* kpl = kv_cache + (size_t)(2 * l) * plane;
         uint16_t* vpl = kv_cache + (size_t)(2 * l + 1) * plane;
         {
             Timed t(h, PD_KERNEL_OTHER, s);
-            PD_TRY(launch_rope_cache(qkv, b->positions, b->slot_mapping, T, m->Hq, m->Hkv, m->dh,
+            PD_TRY(launch_rope_cache(ws, sp, b->positions, b->slot_mapping, T, m->Hq, m->Hkv, m->dh,
                                      m->rope_theta, q, kpl, vpl, dims->num_blocks, st, s));
         }
         AttnArgs aa;
@@ -313,26 +300,27 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
             if (e0 && e1) h->ev[PD_KERNEL_ATTN].emplace_back(e0, e1);
             if (rc != PD_OK) return rc;
         }
-        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_RESID_F32, ao, hd, nullptr, 0, m->w_o[l], nullptr, T, d, hd,
-                    x, d, nullptr, 0));
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, ao, hd, nullptr, 0, m->w_o[l], nullptr, T, d, hd,
+                    nullptr, 0, &sp));
         {
             Timed t(h, PD_KERNEL_OTHER, s);
-            PD_TRY(launch_rmsnorm(x, d, nullptr, 0, T, m->norm_post[l], u, d, d, m->rms_eps, st, s));
+            PD_TRY(launch_resid_norm(ws, sp, x, m->norm_post[l], u, T, d, m->rms_eps, s));
         }
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_SWIGLU, u, d, nullptr, 0, m->w_gate[l], m->w_up[l], T, m->F,
-                    d, nullptr, 0, act, m->F));
-        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_RESID_F32, act, m->F, nullptr, 0, m->w_down[l], nullptr, T,
-                    d, m->F, x, d, nullptr, 0));
+                    d, act, m->F, nullptr));
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, act, m->F, nullptr, 0, m->w_down[l], nullptr, T, d,
+                    m->F, nullptr, 0, &sp));
+        {
+            // next layer's input norm, or the final norm after the last layer
+            const uint16_t* gamma = (l + 1 < m->N) ? m->norm_in[l + 1] : m->norm_final;
+            Timed t(h, PD_KERNEL_OTHER, s);
+            PD_TRY(launch_resid_norm(ws, sp, x, gamma, u, T, d, m->rms_eps, s));
+        }
         PD_TRY(dbg(l + 1));
     }
-    // final norm on the K sampled rows of every request, LM head, greedy argmax
-    {
-        Timed t(h, PD_KERNEL_OTHER, s);
-        PD_TRY(launch_rmsnorm(x, d, b->new_token_indices, T, R, m->norm_final, z, d, d, m->rms_eps,
-                              st, s));
-    }
-    PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, z, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
-                nullptr, 0, nullptr, 0));
+    // LM head on the K sampled rows of every request (gathered), greedy argmax
+    PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, u, d, b->new_token_indices, T, m->lm_head, nullptr, R,
+                m->V, d, nullptr, 0, nullptr));
     {
         Timed t(h, PD_KERNEL_OTHER, s);
         PD_TRY(launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV,
@@ -352,7 +340,6 @@ void pd_free(pd_handle* h) {
         }
     for (auto e : h->spare) (void)hipEventDestroy(e);
     if (h->scratch) (void)hipFree(h->scratch);
-    if (h->counters) (void)hipFree(h->counters);
     if (h->status) (void)hipFree(h->status);
     delete h;
 }

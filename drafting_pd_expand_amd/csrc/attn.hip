@@ -12,20 +12,28 @@
 //
 // Work unit = (request, kv head, KV split). All query vectors of the request
 // that share the kv head (GQA group x rows, e.g. 8 x 13 = 104) are packed
-// into 16-wide MFMA tiles; each wave carries two such tiles. Per 16-token
-// page:
+// into 16-wide MFMA tiles (two per wave at dh 64, one at dh 128). For each
+// pair of 16-token pages:
 //   S^T(16 keys x 16 queries) = K_page (16 x dh) * Q^T  -- 16x16x32 MFMA,
 //       the K page is token-major so a lane's 16-byte load is one key's
 //       8 consecutive dims;
 //   online softmax per query column (fp32, exp2 domain; the four lane groups
 //       of a column are combined with two xor shuffles);
-//   O^T(dh x 16 queries) += V^T_page (dh x 16 keys) * P^T -- 16x16x16 MFMA,
-//       the S^T accumulator layout is exactly the B-operand layout of this
-//       MFMA, and the V page is dim-major so a lane's 8-byte load is one
-//       dim's 4 consecutive keys.
-// Nothing is transposed through LDS. Each split writes an unnormalized
-// partial (O, running max, running sum) per query; a merge kernel combines
-// the splits in order (deterministic) and writes bf16 output.
+//   O^T(dh x 16 queries) += V^T (dh x 32 keys) * P^T -- one 16x16x32 MFMA
+//       per pair of pages: a lane's S^T accumulators (keys 4*g4..+3 of each
+//       page) are its B operand once the MFMA's k slots are mapped to
+//       (page A keys 4*g4..+3, page B keys 4*g4..+3); the V page is
+//       dim-major so the matching A operand is two 8-byte reads;
+//   softmax bookkeeping per 32 keys: one max and one sum exchange, scores
+//       scaled inside a single FMA, masking and accumulator rescaling only
+//       when a wave vote says some lane needs them.
+// The workgroup stages each chunk of pages into LDS once (all waves share it;
+// the next chunk's global loads are in flight while the current one is
+// used). Nothing is transposed: the LDS layout is the page layout, with K rows
+// padded by 16 bytes and V^T rows to 48 bytes so the fragment reads hit
+// distinct banks. Each split writes an
+// unnormalized partial (O, running max, running sum) per query; a merge
+// kernel combines the splits in order (deterministic) and writes bf16 output.
 #include <math.h>
 
 #include "common.hpp"
@@ -35,8 +43,17 @@ namespace pd {
 
 namespace {
 
-constexpr int kTilesPerWave = 2;
+// Query tiles per wave and waves per workgroup: 2 x 4 for dh 64, 1 x 8 for
+// dh 128 (register budget); either way one workgroup holds 128 queries.
+// KV is staged through LDS in chunks of chunk_pages() pages, double buffered.
 constexpr float kNegInf = -INFINITY;
+template <int DH> constexpr int tiles_per_wave() { return DH == 64 ? 2 : 1; }
+template <int DH> constexpr int waves_per_wg() { return DH == 64 ? 4 : 8; }
+template <int DH> constexpr int chunk_pages() { return DH == 64 ? 4 : 2; }
+// Running maxima are raised only when a new score exceeds them by more than
+// this (log2 units); exp2 arguments then stay <= kRescale, the final O / l is
+// unchanged, and the 4*dh/16 accumulator rescales are skipped on most pages.
+constexpr float kRescale = 8.0f;
 
 __device__ __forceinline__ int num_splits(int seq, int nsmax, int min_split) {
     const int ns = (seq + min_split - 1) / min_split;
@@ -49,17 +66,31 @@ __device__ __forceinline__ int split_len(int seq, int ns) {
 }
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * waves_per_wg<DH>()) void attn_split_kernel(AttnArgs a) {
     constexpr int KB = DH / 32;  // 16x16x32 steps over dh for the scores
     constexpr int OT = DH / 16;  // 16-dim output tiles
+    constexpr int TPW = tiles_per_wave<DH>();
+    constexpr int NW = waves_per_wg<DH>();
+    constexpr int NT = 64 * NW;
+    constexpr int CH = chunk_pages<DH>();
+    constexpr int KROW = DH + 8;            // padded K row in LDS (elements): spreads banks
+    constexpr int VROW = PD_PAGE + 8;       // padded V^T row in LDS (elements): 48 B stride
+    constexpr int UPP = 4 * DH;             // 16-byte units per page (K then V)
+    constexpr int UPT = CH * UPP / NT;      // units each thread stages per chunk
+    static_assert(CH * UPP % NT == 0, "staging split");
+    __shared__ __align__(16) uint16_t ks[2][CH * 16 * KROW];
+    __shared__ __align__(16) uint16_t vs[2][CH * DH * VROW];
+    __shared__ int pvalid[2][CH];
+
     const int r = blockIdx.z, g = blockIdx.y, s = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g4 = lane >> 4;
 
     const int row0 = a.cu_out[r], row1 = a.cu_out[r + 1];
     const int seq = a.seq_lens[r];
     if (row0 < 0 || row1 > a.T || row1 < row0 || seq < 1 || seq > a.max_blocks * PD_PAGE) {
-        if (s == 0 && g == 0 && threadIdx.x == 0) flag(a.status, PD_STATUS_BAD_ROW);
+        if (s == 0 && g == 0 && tid == 0) flag(a.status, PD_STATUS_BAD_ROW);
         return;
     }
     const int ns = num_splits(seq, a.nsmax, a.min_split);
@@ -67,20 +98,68 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     const int sl = split_len(seq, ns);
     const int kb = s * sl;
     const int ke = min(seq, kb + sl);
+    const int npages = ke > kb ? (ke - kb + PD_PAGE - 1) / PD_PAGE : 0;
+    const int nchunks = (npages + CH - 1) / CH;
     const int G = a.Hq / a.Hkv;
     const int nq = (row1 - row0) * G;
-    const int32_t* bt = a.block_table + (size_t)r * a.max_blocks;
+    const int32_t* bt = a.block_table + (size_t)r * a.max_blocks + kb / PD_PAGE;
 
-    for (int qbase = 0; qbase < nq; qbase += 4 * kTilesPerWave * 16) {
-        if (qbase + wave * 16 >= nq) continue;  // this wave has no query here (wave-uniform)
-        bf16x8 qv[kTilesPerWave][KB];
-        int qpos[kTilesPerWave], qrow[kTilesPerWave], qh[kTilesPerWave];
-        bool qok[kTilesPerWave];
-        f32x4 o[kTilesPerWave][OT];
-        float mrun[kTilesPerWave], lrun[kTilesPerWave];
+    uint4 stg[UPT];
+    // global -> registers for chunk c (pages past the split read nothing)
+    auto stage = [&](int c) {
 #pragma unroll
-        for (int tt = 0; tt < kTilesPerWave; ++tt) {
-            const int qi = qbase + (wave + 4 * tt) * 16 + r16;
+        for (int j = 0; j < UPT; ++j) {
+            const int u = tid + j * NT;
+            const int pi = u / UPP, w = u % UPP;
+            const int pg = c * CH + pi;
+            stg[j] = make_uint4(0, 0, 0, 0);
+            if (pg < npages) {
+                const int blk = bt[pg];
+                if (blk >= 0 && blk < a.num_blocks) {
+                    const size_t base = ((size_t)blk * a.Hkv + g) * PD_PAGE * DH;
+                    const uint16_t* src = (w < 2 * DH) ? a.kplane + base + w * 8
+                                                       : a.vplane + base + (w - 2 * DH) * 8;
+                    stg[j] = *reinterpret_cast<const uint4*>(src);
+                }
+            }
+        }
+    };
+    // registers -> LDS buffer b; page validity flags alongside
+    auto commit = [&](int c, int b) {
+#pragma unroll
+        for (int j = 0; j < UPT; ++j) {
+            const int u = tid + j * NT;
+            const int pi = u / UPP, w = u % UPP;
+            if (w < 2 * DH) {
+                const int key = w / (DH / 8), c8 = w % (DH / 8);
+                *reinterpret_cast<uint4*>(&ks[b][(pi * 16 + key) * KROW + c8 * 8]) = stg[j];
+            } else {
+                const int vu = w - 2 * DH;  // V^T row vu / 2, keys 8 * (vu % 2) ..
+                *reinterpret_cast<uint4*>(&vs[b][(pi * DH + vu / 2) * VROW + 8 * (vu % 2)]) = stg[j];
+            }
+        }
+        if (tid < CH) {
+            const int pg = c * CH + tid;
+            int ok = 0;
+            if (pg < npages) {
+                const int blk = bt[pg];
+                ok = blk >= 0 && blk < a.num_blocks;
+                if (!ok) flag(a.status, PD_STATUS_BAD_PAGE);
+            }
+            pvalid[b][tid] = ok;
+        }
+    };
+
+    for (int qbase = 0; qbase < nq; qbase += NW * TPW * 16) {
+        const bool wave_has = qbase + wave * 16 < nq;   // wave-uniform
+        bf16x8 qv[TPW][KB];
+        int qpos[TPW], qrow[TPW], qh[TPW];
+        bool qok[TPW];
+        f32x4 o[TPW][OT];
+        float mrun[TPW], lrun[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int qi = qbase + (wave + NW * tt) * 16 + r16;
             qok[tt] = qi < nq;
             qrow[tt] = row0 + (qok[tt] ? qi / G : 0);
             qh[tt] = g * G + (qok[tt] ? qi % G : 0);
@@ -95,64 +174,96 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
             lrun[tt] = 0.f;
         }
 
-        for (int p0 = kb; p0 < ke; p0 += PD_PAGE) {
-            const int blk = bt[p0 / PD_PAGE];
-            if (blk < 0 || blk >= a.num_blocks) {  // uniform across the workgroup
-                if (threadIdx.x == 0) flag(a.status, PD_STATUS_BAD_PAGE);
-                continue;
+        if (nchunks > 0) {
+            stage(0);
+            commit(0, 0);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            const int b = c & 1;
+            if (c + 1 < nchunks) stage(c + 1);   // next chunk's loads in flight
+            if (wave_has) {
+                // pages in pairs: 32 keys per softmax step and per PV MFMA
+                for (int pi = 0; pi < CH; pi += 2) {
+                    const int p0 = kb + (c * CH + pi) * PD_PAGE;
+                    if (p0 >= ke) break;
+                    const bool okA = pvalid[b][pi] != 0;
+                    const bool okB = p0 + PD_PAGE < ke && pvalid[b][pi + 1] != 0;
+                    bf16x8 kA[KB], kB[KB], vab[OT];
+#pragma unroll
+                    for (int kk = 0; kk < KB; ++kk) {
+                        kA[kk] = *reinterpret_cast<const bf16x8*>(&ks[b][(pi * 16 + r16) * KROW + 32 * kk + 8 * g4]);
+                        kB[kk] = *reinterpret_cast<const bf16x8*>(&ks[b][((pi + 1) * 16 + r16) * KROW + 32 * kk + 8 * g4]);
+                    }
+                    // V^T fragments of both pages: k slots 0-3 = page A keys 4*g4.., 4-7 = page B keys 4*g4..
+#pragma unroll
+                    for (int j = 0; j < OT; ++j) {
+                        uint2 va = *reinterpret_cast<const uint2*>(&vs[b][(pi * DH + 16 * j + r16) * VROW + 4 * g4]);
+                        uint2 vb = *reinterpret_cast<const uint2*>(&vs[b][((pi + 1) * DH + 16 * j + r16) * VROW + 4 * g4]);
+                        if (!okA) va = make_uint2(0, 0);
+                        if (!okB) vb = make_uint2(0, 0);
+                        const uint4 v4 = make_uint4(va.x, va.y, vb.x, vb.y);
+                        vab[j] = __builtin_bit_cast(bf16x8, v4);
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        f32x4 sA = f32x4{0.f, 0.f, 0.f, 0.f}, sB = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kk = 0; kk < KB; ++kk) {
+                            sA = mfma_16x16x32(kA[kk], qv[tt][kk], sA);
+                            sB = mfma_16x16x32(kB[kk], qv[tt][kk], sB);
+                        }
+                        // raw scores of keys p0+4*g4+i (page A) and p0+16+4*g4+i (page B)
+                        float sc[8] = {sA[0], sA[1], sA[2], sA[3], sB[0], sB[1], sB[2], sB[3]};
+                        // keys this query may see: t <= lim (invalid queries: no limit, don't care)
+                        const int lim = qok[tt] && qpos[tt] >= 0 ? min(ke - 1, qpos[tt]) : 0x7fffffff;
+                        if (__any(p0 + 2 * PD_PAGE - 1 > lim || !okA || !okB)) {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                const int t = p0 + (i >> 2) * PD_PAGE + 4 * g4 + (i & 3);
+                                const bool ok = (i < 4 ? okA : okB) && t <= lim;
+                                sc[i] = ok ? sc[i] : kNegInf;
+                            }
+                        }
+                        float mx = sc[0];
+#pragma unroll
+                        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+                        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                        const float mnew = mx * a.scale_log2;   // -inf stays -inf
+                        const bool raise = mnew > mrun[tt] + kRescale;
+                        if (__any(raise)) {
+                            const float alpha = raise ? __builtin_amdgcn_exp2f(mrun[tt] - mnew) : 1.0f;
+                            if (raise) mrun[tt] = mnew;
+                            lrun[tt] *= alpha;
+#pragma unroll
+                            for (int j = 0; j < OT; ++j) o[tt][j] = o[tt][j] * alpha;
+                        }
+                        const float muse = (mrun[tt] == kNegInf) ? 0.f : mrun[tt];
+                        float p[8], ls = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            // raw v_exp_f32: weights below 2^-126 flush to zero
+                            p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -muse));
+                            ls += p[i];
+                        }
+                        ls += __shfl_xor(ls, 16, kWave);
+                        ls += __shfl_xor(ls, 32, kWave);
+                        lrun[tt] += ls;
+                        bf16x8 pb;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
+#pragma unroll
+                        for (int j = 0; j < OT; ++j) o[tt][j] = mfma_16x16x32(vab[j], pb, o[tt][j]);
+                    }
+                }
             }
-            const uint16_t* kp = a.kplane + ((size_t)blk * a.Hkv + g) * PD_PAGE * DH;
-            const uint16_t* vp = a.vplane + ((size_t)blk * a.Hkv + g) * PD_PAGE * DH;
-            bf16x8 kf[KB];
-#pragma unroll
-            for (int kk = 0; kk < KB; ++kk) kf[kk] = ld_bf16x8(kp + r16 * DH + 32 * kk + 8 * g4);
-            s16x4 vf[OT];
-#pragma unroll
-            for (int j = 0; j < OT; ++j)
-                vf[j] = *reinterpret_cast<const s16x4*>(vp + (16 * j + r16) * PD_PAGE + 4 * g4);
-
-#pragma unroll
-            for (int tt = 0; tt < kTilesPerWave; ++tt) {
-                f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KB; ++kk) sc = mfma_16x16x32(kf[kk], qv[tt][kk], sc);
-                // lane holds scores of keys p0+4*g4+i for query column r16
-                float sv[4];
-                float mx = kNegInf;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = p0 + 4 * g4 + i;
-                    sv[i] = (t < ke && t <= qpos[tt]) ? sc[i] * a.scale_log2 : kNegInf;
-                    mx = fmaxf(mx, sv[i]);
-                }
-                mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-                const float mnew = fmaxf(mrun[tt], mx);
-                const float muse = (mnew == kNegInf) ? 0.f : mnew;
-                const float alpha = exp2f(mrun[tt] - muse);
-                float p[4], ls = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = exp2f(sv[i] - muse);
-                    ls += p[i];
-                }
-                ls += __shfl_xor(ls, 16, kWave);
-                ls += __shfl_xor(ls, 32, kWave);
-                lrun[tt] = lrun[tt] * alpha + ls;
-                mrun[tt] = mnew;
-                s16x4 pb;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pb[i] = (short)f2bf(p[i]);
-#pragma unroll
-                for (int j = 0; j < OT; ++j) {
-                    o[tt][j] = o[tt][j] * alpha;
-                    o[tt][j] = mfma_16x16x16(vf[j], pb, o[tt][j]);
-                }
-            }
+            if (c + 1 < nchunks) commit(c + 1, b ^ 1);
+            __syncthreads();
         }
 
 #pragma unroll
-        for (int tt = 0; tt < kTilesPerWave; ++tt) {
+        for (int tt = 0; tt < TPW; ++tt) {
             if (!qok[tt]) continue;
             const size_t base = ((size_t)s * a.T + qrow[tt]) * a.Hq + qh[tt];
 #pragma unroll
@@ -166,12 +277,15 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     }
 }
 
-// out[row][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order.
+// out[row][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in
+// order. One wave per (row, q head): the split weights are formed across
+// lanes, then each lane accumulates its dims over the splits.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-    const int row = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // request of this row
+    const int pair = blockIdx.x * 4 + wave;
+    if (pair >= a.T * a.Hq) return;
+    const int row = pair / a.Hq, h = pair % a.Hq;
     int lo = 0, hi = a.C - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -181,38 +295,53 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int seq = a.seq_lens[r];
     const bool ok = !a.is_rejected[row] && seq >= 1 && seq <= a.max_blocks * PD_PAGE &&
                     a.cu_out[r] <= row && row < a.cu_out[r + 1];
-    const int ns = ok ? num_splits(seq, a.nsmax, a.min_split) : 0;
+    const int ns = ok ? num_splits(seq, a.nsmax, a.min_split) : 0;  // <= 128
     constexpr int PER = DH / 64;
-    for (int h = wave; h < a.Hq; h += 4) {
-        float M = kNegInf;
-        for (int sp = 0; sp < ns; ++sp)
-            M = fmaxf(M, a.part_ml[(((size_t)sp * a.T + row) * a.Hq + h) * 2]);
-        float L = 0.f, acc[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-        if (M != kNegInf) {
-            for (int sp = 0; sp < ns; ++sp) {
-                const size_t base = ((size_t)sp * a.T + row) * a.Hq + h;
-                const float w = exp2f(a.part_ml[base * 2] - M);
-                L += w * a.part_ml[base * 2 + 1];
-#pragma unroll
-                for (int i = 0; i < PER; ++i) acc[i] += w * a.part_o[base * DH + lane + 64 * i];
-            }
+    const size_t stride = (size_t)a.T * a.Hq;   // between splits, in (row, head) units
+    const size_t base = (size_t)row * a.Hq + h;
+    float m0 = kNegInf, m1 = kNegInf;
+    if (lane < ns) m0 = a.part_ml[(lane * stride + base) * 2];
+    if (lane + 64 < ns) m1 = a.part_ml[((lane + 64) * stride + base) * 2];
+    const float M = wave_max(fmaxf(m0, m1));
+    float w0 = 0.f, w1 = 0.f, L = 0.f;
+    if (M != kNegInf) {
+        if (lane < ns) {
+            w0 = exp2f(m0 - M);
+            L += w0 * a.part_ml[(lane * stride + base) * 2 + 1];
         }
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        uint16_t* op = a.out + ((size_t)row * a.Hq + h) * DH;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) op[lane + 64 * i] = f2bf(acc[i] * inv);
+        if (lane + 64 < ns) {
+            w1 = exp2f(m1 - M);
+            L += w1 * a.part_ml[((lane + 64) * stride + base) * 2 + 1];
+        }
     }
+    L = wave_sum(L);
+    float acc[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+#pragma unroll 16
+    for (int sp = 0; sp < ns; ++sp) {
+        const float w = __shfl(sp < 64 ? w0 : w1, sp & 63, kWave);
+        const float* po = a.part_o + (sp * stride + base) * DH;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += w * po[lane + 64 * i];
+    }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    uint16_t* op = a.out + base * DH;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) op[lane + 64 * i] = f2bf(acc[i] * inv);
 }
 
 template <int DH>
 int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (e0) (void)hipEventRecord(e0, s);
-    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3(a.nsmax, a.Hkv, a.C), dim3(256), 0, s, a);
+    // splits a request can have: bounded by nsmax and by the block table's reach
+    const int reach = (a.max_blocks * PD_PAGE + a.min_split - 1) / a.min_split;
+    const int gx = reach < a.nsmax ? reach : a.nsmax;
+    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3(gx, a.Hkv, a.C), dim3(64 * waves_per_wg<DH>()), 0, s,
+                       a);
     if (e1) (void)hipEventRecord(e1, s);
     if (hipGetLastError() != hipSuccess) return PD_EHIP;
-    hipLaunchKernelGGL(attn_merge_kernel<DH>, dim3(a.T), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_merge_kernel<DH>, dim3((a.T * a.Hq + 3) / 4), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 

@@ -160,9 +160,23 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
                 a.out.new_token_indices[r * K + m] = o;
             }
         }
+        // the row copy: every thread's 16-byte loads are issued before its stores
         const uint4* s4 = reinterpret_cast<const uint4*>(src);
         uint4* d4 = reinterpret_cast<uint4*>(a.out.hidden + (size_t)o * H3);
-        for (int c = tid; c < H3 / 8; c += 256) d4[c] = s4[c];
+        const int n16 = H3 / 8;
+        for (int c0 = 0; c0 < n16; c0 += 256 * 8) {
+            uint4 buf[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = c0 + j * 256 + tid;
+                if (c < n16) buf[j] = s4[c];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = c0 + j * 256 + tid;
+                if (c < n16) d4[c] = buf[j];
+            }
+        }
     }
 }
 

@@ -1,28 +1,32 @@
 // bf16 GEMMs of the drafter, Y = X W^T with fp32 accumulation on CDNA4 MFMA.
 //
 // The drafter's projections (fc 3d->d, QKV, O, gate/up, down, LM head;
-// [Paper] sec. 2 architecture, [arXiv] Figure 2) run with few rows per step:
-// the expanded batch has only v_r + K - 1 computed rows per request and the
-// LM head sees C*K rows. At low concurrency every projection is a stream of
-// its weight matrix, so this kernel is built around streaming W from HBM:
+// [Paper] = "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training" summary
+// page, sec. 2 architecture; [arXiv] = its ScienceStack page, Figure 2) see
+// few rows per step: the draft batch has v_r + K - 1 computed rows per
+// request and the LM head C*K rows. At low concurrency every projection is a
+// stream of its weight matrix, so this kernel is built to stream W at HBM
+// speed:
 //
-//  * a workgroup is 4 waves; each wave owns 16 rows of W (16 output columns)
-//    and multiplies them with up to 64 rows of X using
-//    v_mfma_f32_16x16x32_bf16 (W is the A operand, X the B operand, so each
-//    lane ends up with 4 consecutive output columns of one row: vector
-//    epilogue stores);
-//  * the reduction index is permuted per lane: in one 256-wide K step, lane
-//    group g (lanes 16g..16g+15) owns k in [64g, 64g+64) and feeds it to the
-//    8 MFMAs in 8-element pieces. Both operands use the same permutation, so
-//    the sum is unchanged while each lane reads 128 contiguous bytes of its W
-//    row -- whole cache lines, 8 x 16-byte loads in flight per lane;
-//  * small-N projections split K across workgroups to put >= ~1000
-//    workgroups on 256 CUs; partial tiles go to a workspace and the last
-//    workgroup to arrive (per-tile counter, agent-scope fences) sums them in
-//    split order -- deterministic, and no extra launch;
-//  * epilogues: fp32 store, fp32 residual add, bf16 store, SwiGLU on a pair
-//    of matrices (gate and up rows read side by side), and LM-head max/argmax
-//    per 64-column tile (lowest index on ties) with optional fp32 logits.
+//  * a wave owns RG groups of 16 W rows (the A operand of
+//    v_mfma_f32_16x16x32_bf16) and up to 64 X rows (the B operand), so each
+//    lane ends with 4 consecutive output columns of one row;
+//  * in every 128-wide K step, lane group g (lanes 16g..16g+15) takes
+//    k = 32j + 8g .. +7 for j = 0..3: each load instruction reads 64
+//    contiguous bytes of each of the 16 rows, and 4 such loads per row group
+//    are in flight; the next step's W loads are issued before the current
+//    step's MFMAs (register double buffering);
+//  * a workgroup has WK waves that split its K range; their partial tiles are
+//    summed through LDS inside the workgroup;
+//  * projections with few output columns are further split over S
+//    workgroups along K. Those splits never meet inside this kernel: each
+//    writes an fp32 partial plane, and the row kernel that consumes the
+//    projection (layer-0 input, RoPE + KV write, residual + RMSNorm) sums the
+//    planes in split order. No workgroup ever waits on another, so no
+//    device-wide fence is needed, and the result is deterministic.
+//  * epilogues: fp32 partial plane, SwiGLU on a pair of matrices (gate and up
+//    rows streamed side by side, one bf16 rounding), and LM-head max/argmax per
+//    column tile (lowest index on ties) with optional fp32 logits.
 #include <float.h>
 #include <limits.h>
 
@@ -33,53 +37,50 @@ namespace pd {
 
 namespace {
 
-constexpr int kU = 8;                 // 16-byte loads per lane per operand per K step
-constexpr int kKStep = 32 * kU;       // 256 reduction elements per K step
-constexpr int kTileN = 64;            // output columns per workgroup (4 waves x 16)
+constexpr int kU = 4;             // 16-byte loads per lane per row group per K step
+constexpr int kKStep = 32 * kU;   // 128 reduction elements per K step
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
-
-template <int EPI>
-__device__ __forceinline__ void epi_apply(const GemmArgs& a, int m, int n, f32x4 v, f32x4 v2) {
-    if constexpr (EPI == EPI_STORE_F32) {
-        *reinterpret_cast<f32x4*>(a.yf + (size_t)m * a.ldyf + n) = v;
-    } else if constexpr (EPI == EPI_RESID_F32) {
-        f32x4* p = reinterpret_cast<f32x4*>(a.yf + (size_t)m * a.ldyf + n);
-        *p = *p + v;
-    } else if constexpr (EPI == EPI_STORE_BF16 || EPI == EPI_SWIGLU) {
-        float r[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = (EPI == EPI_SWIGLU) ? silu(v[i]) * v2[i] : v[i];
-        uint2 pk;
-        pk.x = uint32_t(f2bf(r[0])) | (uint32_t(f2bf(r[1])) << 16);
-        pk.y = uint32_t(f2bf(r[2])) | (uint32_t(f2bf(r[3])) << 16);
-        *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
-    }
-}
 
 __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
     if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
 }
 
-template <int MT, int EPI>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a) {
+template <int MT, int RG, int WK, int EPI>
+__global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmArgs a) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NM = DUAL ? 2 : 1;  // matrices streamed side by side
+    const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
     const int r16 = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * kTileN + wave * 16;
-    const int m0 = blockIdx.z * (16 * MT);
-    const int kbeg = blockIdx.y * a.kper;
-    const int kend = min(a.K, kbeg + a.kper);
-    const bool wact = n0 < a.N;
+    const int n0 = blockIdx.x * 16 * RG;
+    const int m0 = blockIdx.z * 16 * MT;
 
-    f32x4 acc[MT], acc2[MT];
+    // K range of this wave: part (split * WK + wave) of S*WK equal parts, in K steps
+    const int ksteps = (a.K + kKStep - 1) / kKStep;
+    const int parts = a.splits * WK;
+    const int per = (ksteps + parts - 1) / parts;
+    const int part = blockIdx.y * WK + wk;
+    const int kb = min(a.K, part * per * kKStep);
+    const int ke = min(a.K, (part + 1) * per * kKStep);
+
+    f32x4 acc[NM][MT][RG];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int q = 0; q < NM; ++q)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < RG; ++r) acc[q][t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // X rows of this lane (B operand column = r16 of each 16-row tile)
+    // operand rows of this lane
+    const uint16_t* wp[NM][RG];
+    bool rok[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        rok[r] = n0 + 16 * r < a.N;
+        const size_t row = (size_t)(rok[r] ? n0 + 16 * r + r16 : 0) * a.K;
+        wp[0][r] = a.W + row;
+        if constexpr (DUAL) wp[NM - 1][r] = a.W2 + row;
+    }
     const uint16_t* xp[MT];
     bool xok[MT];
 #pragma unroll
@@ -97,49 +98,94 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a) {
         xp[t] = a.X + (size_t)(xok[t] ? row : 0) * a.ldx;
     }
 
-    if (wact) {
-        const uint16_t* wp = a.W + (size_t)(n0 + r16) * a.K;
-        const uint16_t* wp2 = DUAL ? a.W2 + (size_t)(n0 + r16) * a.K : nullptr;
-        for (int kk = kbeg; kk < kend; kk += kKStep) {
-            const int k0 = kk + g * (8 * kU);
-            bf16x8 w[kU], w2[DUAL ? kU : 1];
+    if (kb < ke) {
+        bf16x8 w[NM][RG][kU];
 #pragma unroll
-            for (int j = 0; j < kU; ++j) {
-                const int k = k0 + 8 * j;
-                w[j] = k < kend ? ld_bf16x8(wp + k) : zero_bf16x8();
-                if constexpr (DUAL) w2[j] = k < kend ? ld_bf16x8(wp2 + k) : zero_bf16x8();
+        for (int q = 0; q < NM; ++q)
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int j = 0; j < kU; ++j) {
+                    const int k = kb + 32 * j + 8 * g;
+                    w[q][r][j] = (rok[r] && k < ke) ? ld_bf16x8(wp[q][r] + k) : zero_bf16x8();
+                }
+        for (int kk = kb; kk < ke; kk += kKStep) {
+            const bool more = kk + kKStep < ke;
+            bf16x8 nx[NM][RG][kU];
+            if (more) {
+#pragma unroll
+                for (int q = 0; q < NM; ++q)
+#pragma unroll
+                    for (int r = 0; r < RG; ++r)
+#pragma unroll
+                        for (int j = 0; j < kU; ++j) {
+                            const int k = kk + kKStep + 32 * j + 8 * g;
+                            nx[q][r][j] = (rok[r] && k < ke) ? ld_bf16x8(wp[q][r] + k) : zero_bf16x8();
+                        }
             }
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 bf16x8 x[kU];
 #pragma unroll
                 for (int j = 0; j < kU; ++j) {
-                    const int k = k0 + 8 * j;
-                    x[j] = (xok[t] && k < kend) ? ld_bf16x8(xp[t] + k) : zero_bf16x8();
+                    const int k = kk + 32 * j + 8 * g;
+                    x[j] = (xok[t] && k < ke) ? ld_bf16x8(xp[t] + k) : zero_bf16x8();
                 }
 #pragma unroll
-                for (int j = 0; j < kU; ++j) {
-                    acc[t] = mfma_16x16x32(w[j], x[j], acc[t]);
-                    if constexpr (DUAL) acc2[t] = mfma_16x16x32(w2[j], x[j], acc2[t]);
-                }
+                for (int q = 0; q < NM; ++q)
+#pragma unroll
+                    for (int r = 0; r < RG; ++r)
+#pragma unroll
+                        for (int j = 0; j < kU; ++j) acc[q][t][r] = mfma_16x16x32(w[q][r][j], x[j], acc[q][t][r]);
+            }
+            if (more) {
+#pragma unroll
+                for (int q = 0; q < NM; ++q)
+#pragma unroll
+                    for (int r = 0; r < RG; ++r)
+#pragma unroll
+                        for (int j = 0; j < kU; ++j) w[q][r][j] = nx[q][r][j];
             }
         }
     }
 
+    // sum the WK waves' partial tiles through LDS (wave 0 keeps the result)
+    if constexpr (WK > 1) {
+        __shared__ f32x4 red[WK - 1][NM * MT * RG][64];
+        if (wk > 0) {
+#pragma unroll
+            for (int q = 0; q < NM; ++q)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int r = 0; r < RG; ++r) red[wk - 1][(q * MT + t) * RG + r][lane] = acc[q][t][r];
+        }
+        __syncthreads();
+        if (wk > 0) return;
+        for (int w = 0; w < WK - 1; ++w)
+#pragma unroll
+            for (int q = 0; q < NM; ++q)
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int r = 0; r < RG; ++r) acc[q][t][r] = acc[q][t][r] + red[w][(q * MT + t) * RG + r][lane];
+    }
+
+    // wave 0: lane holds rows m0+16t+r16, columns n0+16r+4g .. +3
     if constexpr (EPI == EPI_ARGMAX) {
-        // one K split only: lane holds logits of row m0+16t+r16, columns n0+4g .. +3
-        __shared__ float s_v[4][16 * MT];
-        __shared__ int s_i[4][16 * MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             const int m = m0 + 16 * t + r16;
             float bv = -FLT_MAX;
             int bi = INT_MAX;
-            if (wact) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) better(bv, bi, acc[t][i], n0 + 4 * g + i);
+            for (int r = 0; r < RG; ++r) {
+                if (!rok[r]) continue;
+                const int n = n0 + 16 * r + 4 * g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) better(bv, bi, acc[0][t][r][i], n + i);
                 if (a.logits && m < a.M)
-                    *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n0 + 4 * g) = acc[t];
+                    *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[0][t][r];
             }
 #pragma unroll
             for (int off = 16; off <= 32; off <<= 1) {
@@ -147,87 +193,65 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a) {
                 const int oi = __shfl_xor(bi, off, kWave);
                 better(bv, bi, ov, oi);
             }
-            if (g == 0) {
-                s_v[wave][16 * t + r16] = bv;
-                s_i[wave][16 * t + r16] = bi;
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x < 16 * MT) {
-            const int m = m0 + threadIdx.x;
-            float bv = s_v[0][threadIdx.x];
-            int bi = s_i[0][threadIdx.x];
-#pragma unroll
-            for (int w = 1; w < 4; ++w) better(bv, bi, s_v[w][threadIdx.x], s_i[w][threadIdx.x]);
-            if (m < a.M) {
+            if (g == 0 && m < a.M) {
                 a.amax_v[(size_t)m * a.ntiles + blockIdx.x] = bv;
                 a.amax_i[(size_t)m * a.ntiles + blockIdx.x] = bi;
             }
         }
-        return;
     } else {
-        if (a.splits == 1) {
-            if (wact) {
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const int m = m0 + 16 * t + r16;
-                    if (m < a.M) epi_apply<EPI>(a, m, n0 + 4 * g, acc[t], acc2[t]);
-                }
-            }
-            return;
-        }
-        // split-K: publish this split's partial tile
-        const size_t plane = (size_t)a.splits * a.M * a.N;
-        if (wact) {
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int m = m0 + 16 * t + r16;
-                if (m < a.M) {
-                    const size_t off = ((size_t)blockIdx.y * a.M + m) * a.N + n0 + 4 * g;
-                    *reinterpret_cast<f32x4*>(a.ws + off) = acc[t];
-                    if constexpr (DUAL) *reinterpret_cast<f32x4*>(a.ws + plane + off) = acc2[t];
-                }
-            }
-        }
-        __shared__ int s_last;
-        __threadfence();
-        __syncthreads();
-        const int tile = blockIdx.z * gridDim.x + blockIdx.x;
-        if (threadIdx.x == 0) {
-            const int prev = atomicAdd(&a.counters[tile], 1);
-            s_last = (prev == a.splits - 1);
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        // last arrival: sum the splits in order, then the epilogue
-        const int n = blockIdx.x * kTileN + 4 * (threadIdx.x & 15);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-            const int m = m0 + 16 * t + (threadIdx.x >> 4);
-            if (m < a.M && n < a.N) {
-                f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, s2 = f32x4{0.f, 0.f, 0.f, 0.f};
-                for (int sp = 0; sp < a.splits; ++sp) {
-                    const size_t off = ((size_t)sp * a.M + m) * a.N + n;
-                    s = s + *reinterpret_cast<const f32x4*>(a.ws + off);
-                    if constexpr (DUAL) s2 = s2 + *reinterpret_cast<const f32x4*>(a.ws + plane + off);
+            const int m = m0 + 16 * t + r16;
+            if (m >= a.M) continue;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                if (!rok[r]) continue;
+                const int n = n0 + 16 * r + 4 * g;
+                if constexpr (EPI == EPI_PARTIAL) {
+                    *reinterpret_cast<f32x4*>(a.ws + ((size_t)blockIdx.y * a.M + m) * a.N + n) = acc[0][t][r];
+                } else if constexpr (EPI == EPI_SWIGLU) {
+                    float h[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) h[i] = silu(acc[0][t][r][i]) * acc[NM - 1][t][r][i];
+                    uint2 pk;
+                    pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
+                    pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
+                    *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
                 }
-                epi_apply<EPI>(a, m, n, s, s2);
             }
         }
-        if (threadIdx.x == 0) atomicExch(&a.counters[tile], 0);
     }
 }
 
-template <int EPI>
-int launch_mt(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-    dim3 grid(p.ntiles, p.splits, p.mblocks), block(256);
-    switch (p.mt) {
-        case 1: hipLaunchKernelGGL((gemm_skinny_kernel<1, EPI>), grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemm_skinny_kernel<2, EPI>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemm_skinny_kernel<4, EPI>), grid, block, 0, s, a); break;
+// Row groups of W per wave: fewer when more X rows share the registers.
+template <int MT, int EPI>
+constexpr int rows_groups() {
+    return EPI == EPI_ARGMAX ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
+                             : (EPI == EPI_SWIGLU ? (MT == 1 ? 2 : 1) : 1);
+}
+
+template <int MT, int EPI>
+int launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    constexpr int RG = rows_groups<MT, EPI>();
+    dim3 grid(p.ntiles, p.splits, p.mblocks);
+    if (p.rg != RG) return PD_EINVAL;
+    if constexpr (EPI == EPI_PARTIAL) {
+        if (p.wk == 8) {
+            hipLaunchKernelGGL((gemm_stream_kernel<MT, RG, 8, EPI>), grid, dim3(512), 0, s, a);
+            return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+        }
     }
+    hipLaunchKernelGGL((gemm_stream_kernel<MT, RG, 4, EPI>), grid, dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+template <int EPI>
+int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    switch (p.mt) {
+        case 1: return launch_cfg<1, EPI>(p, a, s);
+        case 2: return launch_cfg<2, EPI>(p, a, s);
+        default: return launch_cfg<4, EPI>(p, a, s);
+    }
 }
 
 }  // namespace
@@ -236,35 +260,38 @@ GemmPlan plan_gemm(int M, int N, int K, int epi) {
     GemmPlan p;
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.mblocks = (M + 16 * p.mt - 1) / (16 * p.mt);
-    p.ntiles = (N + kTileN - 1) / kTileN;
-    const int tiles = p.ntiles * p.mblocks;
-    int splits = 1;
-    if (epi != EPI_ARGMAX && tiles < 512) splits = (1024 + tiles - 1) / tiles;
-    int ksteps = (K + kKStep - 1) / kKStep;
-    if (splits > ksteps) splits = ksteps;
-    if (splits < 1) splits = 1;
-    const int steps_per = (ksteps + splits - 1) / splits;
-    p.kper = steps_per * kKStep;
-    p.splits = (K + p.kper - 1) / p.kper;
-    if (p.splits < 1) p.splits = 1;
+    p.rg = p.mt == 1 ? (epi == EPI_ARGMAX ? rows_groups<1, EPI_ARGMAX>() : rows_groups<1, EPI_SWIGLU>())
+         : p.mt == 2 ? (epi == EPI_ARGMAX ? rows_groups<2, EPI_ARGMAX>() : rows_groups<2, EPI_SWIGLU>())
+                     : (epi == EPI_ARGMAX ? rows_groups<4, EPI_ARGMAX>() : rows_groups<4, EPI_SWIGLU>());
+    if (epi == EPI_PARTIAL) p.rg = 1;
+    p.wk = 4;
+    p.ntiles = (N + 16 * p.rg - 1) / (16 * p.rg);
+    p.splits = 1;
+    if (epi == EPI_PARTIAL) {
+        // 8 waves per workgroup along K, and enough K splits across
+        // workgroups for ~6000 waves (short projections are latency-bound)
+        p.wk = 8;
+        const int ksteps = (K + kKStep - 1) / kKStep;
+        const long base = (long)p.ntiles * p.mblocks * p.wk;
+        int s = (int)((6000 + base - 1) / base);
+        if (s > 8) s = 8;
+        while (s > 1 && s * p.wk > ksteps) --s;
+        p.splits = s < 1 ? 1 : s;
+    }
     return p;
 }
 
 size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi) {
-    if (p.splits <= 1) return 0;
-    return (size_t)p.splits * M * N * (epi == EPI_SWIGLU ? 2 : 1);
+    return epi == EPI_PARTIAL ? (size_t)p.splits * M * N : 0;
 }
 
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s) {
     a.splits = p.splits;
-    a.kper = p.kper;
     a.ntiles = p.ntiles;
     switch (epi) {
-        case EPI_STORE_F32: return launch_mt<EPI_STORE_F32>(p, a, s);
-        case EPI_RESID_F32: return launch_mt<EPI_RESID_F32>(p, a, s);
-        case EPI_STORE_BF16: return launch_mt<EPI_STORE_BF16>(p, a, s);
-        case EPI_SWIGLU: return launch_mt<EPI_SWIGLU>(p, a, s);
-        case EPI_ARGMAX: return launch_mt<EPI_ARGMAX>(p, a, s);
+        case EPI_PARTIAL: return launch_epi<EPI_PARTIAL>(p, a, s);
+        case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(p, a, s);
+        case EPI_ARGMAX: return launch_epi<EPI_ARGMAX>(p, a, s);
         default: return PD_EINVAL;
     }
 }

@@ -14,11 +14,9 @@ int launch_expand(const pd_batch_dims& d, const pd_expand_in& in, const pd_batch
 
 // ---------------------------------------------------------------- GEMM
 enum Epi : int {
-    EPI_STORE_F32 = 0,  // y_f32 = acc
-    EPI_RESID_F32 = 1,  // y_f32 += acc (residual stream)
-    EPI_STORE_BF16 = 2, // y_bf16 = acc
-    EPI_SWIGLU = 3,     // y_bf16 = silu(X W^T) * (X W2^T)
-    EPI_ARGMAX = 4,     // per (row, 64-column tile) max / argmax (+ optional fp32 logits)
+    EPI_PARTIAL = 0,  // fp32 partial plane per K split: ws[split][M][N] (the consumer sums)
+    EPI_SWIGLU = 1,   // y_bf16 = silu(X W^T) * (X W2^T)
+    EPI_ARGMAX = 2,   // per (row, column tile) max / argmax (+ optional fp32 logits)
 };
 
 struct GemmArgs {
@@ -29,10 +27,8 @@ struct GemmArgs {
     const uint16_t* W;       // bf16 [N][K]
     const uint16_t* W2;      // second matrix for EPI_SWIGLU
     int M, N, K;
-    int splits, kper;        // split-K: split s covers k in [s*kper, min(K, (s+1)*kper))
-    float* ws;               // split-K partials [splits][M][N] (x2 planes for SWIGLU)
-    int* counters;           // per output tile arrival counters (all zero between launches)
-    float* yf; int ldyf;
+    int splits;              // K splits across workgroups (EPI_PARTIAL only)
+    float* ws;               // partial planes [splits][M][N]
     uint16_t* yb; int ldyb;
     float* logits; int ldlog;
     float* amax_v; int* amax_i; int ntiles;
@@ -40,11 +36,12 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-    int mt;        // 16-row MFMA tiles per workgroup (1, 2 or 4)
+    int mt;        // 16-row MFMA tiles of X per workgroup (1, 2 or 4)
     int mblocks;   // workgroups along M
-    int ntiles;    // 64-column tiles along N
-    int splits;
-    int kper;
+    int rg;        // 16-row groups of W per workgroup
+    int wk;        // waves per workgroup, splitting its K range
+    int ntiles;    // workgroups along N
+    int splits;    // workgroups along K
 };
 
 GemmPlan plan_gemm(int M, int N, int K, int epi);
@@ -52,13 +49,14 @@ size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi);
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 
 // ---------------------------------------------------------------- row kernels
-int launch_rmsnorm(const float* x, int ldx, const int32_t* rows, int rows_limit, int nrows,
-                   const uint16_t* gamma, uint16_t* y, int ldy, int d, float eps,
-                   int32_t* status, hipStream_t s);
-int launch_layer0_input(const int32_t* ids, const uint16_t* embed, int V, const float* x,
-                        const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T, int d,
-                        float eps, int32_t* status, hipStream_t s);
-int launch_rope_cache(const uint16_t* qkv, const int32_t* positions, const int32_t* slots, int T,
+// Every consumer of a projection sums its fp32 partial planes
+// (ws[s][T][width], s < S) in split order.
+int launch_layer0_input(const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
+                        float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
+                        int d, float eps, int32_t* status, hipStream_t s);
+int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
+                      int d, float eps, hipStream_t s);
+int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
                       int Hq, int Hkv, int dh, float theta, uint16_t* q_out, uint16_t* kplane,
                       uint16_t* vplane, int num_blocks, int32_t* status, hipStream_t s);
 int launch_argmax_reduce(const float* amax_v, const int* amax_i, int M, int ntiles, int32_t* out,

@@ -1,5 +1,6 @@
-// Row-wise kernels of the drafter: RMSNorm, the layer-0 input, RoPE with the
-// paged KV write, and the final argmax reduction.
+// Row-wise kernels of the drafter: residual + RMSNorm, the layer-0 input, RoPE
+// with the paged KV write, and the final argmax reduction. Each one also
+// finishes the projection that feeds it by summing its split-K planes.
 //
 // [Blog] = "P-EAGLE: Faster LLM Inference with Parallel Speculative Decoding
 // in vLLM" (summary page); [Paper] = "P-EAGLE: Parallel-Drafting EAGLE with
@@ -19,52 +20,84 @@ namespace pd {
 
 namespace {
 
-// y[i] = bf16(gamma * x / sqrt(mean(x^2) + eps)); x fp32 row `rows[o]` (or o).
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int ldx, const int32_t* rows,
-                                                      int rows_limit, const uint16_t* gamma,
-                                                      uint16_t* y, int ldy, int d, float eps,
-                                                      int32_t* status) {
+constexpr int kMaxSplits = 8;   // split-K planes a projection may leave behind
+
+__device__ __forceinline__ void add4(float4& a, const float4& b) {
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+}
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    uint2 pk;
+    pk.x = uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+    pk.y = uint32_t(f2bf(c)) | (uint32_t(f2bf(d)) << 16);
+    return pk;
+}
+
+// Row chunks of 4 floats per thread: NC = ceil(d / 1024) <= 4 (d <= 4096).
+// All loads of a row (x and every split plane) are issued before any is used.
+template <int NC>
+__device__ __forceinline__ void load_row_sum(float4 (&v)[NC], const float* xr, const float* ws,
+                                             int S, size_t plane, size_t rowoff, int d, bool from_x) {
+    float4 p[kMaxSplits][NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = threadIdx.x * 4 + 1024 * n;
+        v[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < d && from_x) v[n] = *reinterpret_cast<const float4*>(xr + c);
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < S && c < d) p[sp][n] = *reinterpret_cast<const float4*>(ws + sp * plane + rowoff + c);
+    }
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+            if (sp < S) add4(v[n], p[sp][n]);
+}
+
+// Residual stream update and the next RMSNorm, one row per workgroup:
+// x += sum_s ws[s] (the projection's split planes, in order), then
+// y = bf16(gamma * x / sqrt(mean(x^2) + eps)).
+template <int NC>
+__global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int S, float* x,
+                                                         const uint16_t* gamma, uint16_t* y, int T,
+                                                         int d, float eps) {
     __shared__ float red[4];
     const int o = blockIdx.x;
-    int src = o;
-    if (rows) {
-        src = rows[o];
-        if (src < 0 || src >= rows_limit) {
-            if (threadIdx.x == 0) flag(status, PD_STATUS_BAD_ROW);
-            src = -1;
-        }
-    }
-    uint16_t* yr = y + (size_t)o * ldy;
-    if (src < 0) {
-        for (int c = threadIdx.x; c < d; c += 256) yr[c] = 0;
-        return;
-    }
-    const float* xr = x + (size_t)src * ldx;
+    float* xr = x + (size_t)o * d;
+    float4 v[NC];
+    load_row_sum<NC>(v, xr, ws, S, (size_t)T * d, (size_t)o * d, d, true);
+    uint2 gb[NC];
     float ss = 0.f;
-    for (int c = threadIdx.x * 4; c < d; c += 1024) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + c);
-        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = threadIdx.x * 4 + 1024 * n;
+        if (c < d) {
+            gb[n] = *reinterpret_cast<const uint2*>(gamma + c);
+            if (S > 0) *reinterpret_cast<float4*>(xr + c) = v[n];
+            ss += v[n].x * v[n].x + v[n].y * v[n].y + v[n].z * v[n].z + v[n].w * v[n].w;
+        }
     }
     ss = block_sum_256(ss, red);
     const float rs = 1.0f / sqrtf(ss / (float)d + eps);
-    for (int c = threadIdx.x * 4; c < d; c += 1024) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + c);
-        const uint2 gb = *reinterpret_cast<const uint2*>(gamma + c);
-        uint2 pk;
-        pk.x = uint32_t(f2bf(v.x * rs * bf2f(gb.x & 0xffff))) |
-               (uint32_t(f2bf(v.y * rs * bf2f(gb.x >> 16))) << 16);
-        pk.y = uint32_t(f2bf(v.z * rs * bf2f(gb.y & 0xffff))) |
-               (uint32_t(f2bf(v.w * rs * bf2f(gb.y >> 16))) << 16);
-        *reinterpret_cast<uint2*>(yr + c) = pk;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = threadIdx.x * 4 + 1024 * n;
+        if (c < d)
+            *reinterpret_cast<uint2*>(y + (size_t)o * d + c) =
+                pack4(v[n].x * rs * bf2f(gb[n].x & 0xffff), v[n].y * rs * bf2f(gb[n].x >> 16),
+                      v[n].z * rs * bf2f(gb[n].y & 0xffff), v[n].w * rs * bf2f(gb[n].y >> 16));
     }
 }
 
 // Layer-0 input of the drafter ([Blog] Input_i equation, emb (+) hidden):
-// u = [RMSNorm(E[id]; g_emb) || RMSNorm(x; g_hid)] with x = fc(hidden) (fp32).
-__global__ __launch_bounds__(256) void layer0_input_kernel(const int32_t* ids, const uint16_t* embed,
-                                                           int V, const float* x,
+// x = fc(hidden) = sum of the fc projection's split planes (starts the
+// residual stream), u = [RMSNorm(E[id]; g_emb) || RMSNorm(x; g_hid)].
+template <int NC>
+__global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int S, const int32_t* ids,
+                                                           const uint16_t* embed, int V, float* x,
                                                            const uint16_t* g_emb,
-                                                           const uint16_t* g_hid, uint16_t* u,
+                                                           const uint16_t* g_hid, uint16_t* u, int T,
                                                            int d, float eps, int32_t* status) {
     __shared__ float red[4];
     const int o = blockIdx.x;
@@ -74,72 +107,115 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const int32_t* ids, c
         id = 0;
     }
     const uint16_t* er = embed + (size_t)id * d;
-    const float* xr = x + (size_t)o * d;
+    float* xr = x + (size_t)o * d;
+    float4 v[NC];
+    uint2 eb[NC], ge[NC], gh[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = threadIdx.x * 4 + 1024 * n;
+        if (c < d) {
+            eb[n] = *reinterpret_cast<const uint2*>(er + c);
+            ge[n] = *reinterpret_cast<const uint2*>(g_emb + c);
+            gh[n] = *reinterpret_cast<const uint2*>(g_hid + c);
+        }
+    }
+    load_row_sum<NC>(v, xr, ws, S, (size_t)T * d, (size_t)o * d, d, false);
     float se = 0.f, sx = 0.f;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        const float e = bf2f(er[c]);
-        const float h = xr[c];
-        se += e * e;
-        sx += h * h;
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = threadIdx.x * 4 + 1024 * n;
+        if (c < d) {
+            *reinterpret_cast<float4*>(xr + c) = v[n];
+            const float e0 = bf2f(eb[n].x & 0xffff), e1 = bf2f(eb[n].x >> 16);
+            const float e2 = bf2f(eb[n].y & 0xffff), e3 = bf2f(eb[n].y >> 16);
+            se += e0 * e0 + e1 * e1 + e2 * e2 + e3 * e3;
+            sx += v[n].x * v[n].x + v[n].y * v[n].y + v[n].z * v[n].z + v[n].w * v[n].w;
+        }
     }
     se = block_sum_256(se, red);
     sx = block_sum_256(sx, red);
     const float re = 1.0f / sqrtf(se / (float)d + eps);
     const float rx = 1.0f / sqrtf(sx / (float)d + eps);
     uint16_t* ur = u + (size_t)o * 2 * d;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        ur[c] = f2bf(bf2f(er[c]) * re * bf2f(g_emb[c]));
-        ur[d + c] = f2bf(xr[c] * rx * bf2f(g_hid[c]));
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const int c = threadIdx.x * 4 + 1024 * n;
+        if (c < d) {
+            *reinterpret_cast<uint2*>(ur + c) =
+                pack4(bf2f(eb[n].x & 0xffff) * re * bf2f(ge[n].x & 0xffff),
+                      bf2f(eb[n].x >> 16) * re * bf2f(ge[n].x >> 16),
+                      bf2f(eb[n].y & 0xffff) * re * bf2f(ge[n].y & 0xffff),
+                      bf2f(eb[n].y >> 16) * re * bf2f(ge[n].y >> 16));
+            *reinterpret_cast<uint2*>(ur + d + c) =
+                pack4(v[n].x * rx * bf2f(gh[n].x & 0xffff), v[n].y * rx * bf2f(gh[n].x >> 16),
+                      v[n].z * rx * bf2f(gh[n].y & 0xffff), v[n].w * rx * bf2f(gh[n].y >> 16));
+        }
     }
 }
 
 // Rotate-half RoPE of q and k at the row's position, then the paged KV write
 // at slot_mapping ([Blog] KV-cache paragraph: -1 = rejected, nothing
-// written). K pages are token-major [16][dh], V pages dim-major [dh][16].
-// The angle pos * theta^(-2i/dh) is formed and reduced in double precision,
-// so positions up to 20k keep full fp32 accuracy in cos/sin.
-__global__ __launch_bounds__(256) void rope_cache_kernel(const uint16_t* qkv, const int32_t* positions,
-                                                         const int32_t* slots, int Hq, int Hkv, int dh,
-                                                         float theta, uint16_t* q_out, uint16_t* kplane,
-                                                         uint16_t* vplane, int num_blocks,
-                                                         int32_t* status) {
-    const int o = blockIdx.x;
+// written). The QKV projection arrives as fp32 split planes and is rounded to
+// bf16 once, after the rotation. One thread per rotation pair (or V element),
+// so every thread's loads go out together. K pages are token-major [16][dh],
+// V pages dim-major [dh][16]. The angle pos * theta^(-2i/dh) is formed and
+// reduced in double precision, so positions up to 20k keep full fp32
+// accuracy in cos/sin.
+__global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S, const int32_t* positions,
+                                                         const int32_t* slots, int T, int Hq, int Hkv,
+                                                         int dh, float theta, uint16_t* q_out,
+                                                         uint16_t* kplane, uint16_t* vplane,
+                                                         int num_blocks, int32_t* status) {
+    const int o = blockIdx.y;
     const int half = dh / 2;
-    const int i = threadIdx.x % half;
-    const int grp = threadIdx.x / half;
-    const int ngrp = 256 / half;
+    const int npairs = (Hq + Hkv) * half;          // rotated pairs (q heads, then k heads)
+    const int item = blockIdx.x * 256 + threadIdx.x;
+    if (item >= npairs + Hkv * dh) return;
     const int W = (Hq + 2 * Hkv) * dh;
-    const uint16_t* row = qkv + (size_t)o * W;
-    const int pos = positions[o];
-    const double inv = exp(-(2.0 * i / dh) * log((double)theta));
-    double sd, cd;
-    sincos((double)pos * inv, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
-
-    for (int h = grp; h < Hq; h += ngrp) {
-        const float a = bf2f(row[h * dh + i]);
-        const float b = bf2f(row[h * dh + i + half]);
-        q_out[(size_t)o * Hq * dh + h * dh + i] = f2bf(a * c - b * s);
-        q_out[(size_t)o * Hq * dh + h * dh + i + half] = f2bf(b * c + a * s);
-    }
+    const size_t plane = (size_t)T * W;
+    const float* row = ws + (size_t)o * W;
     const int slot = slots[o];
-    if (slot < 0) return;  // rejected: no KV write
-    if (slot >= num_blocks * PD_PAGE) {
-        if (threadIdx.x == 0) flag(status, PD_STATUS_BAD_PAGE);
-        return;
-    }
+    const bool write = slot >= 0 && slot < num_blocks * PD_PAGE;
+    if (slot >= num_blocks * PD_PAGE && item == 0) flag(status, PD_STATUS_BAD_PAGE);
     const int blk = slot / PD_PAGE, off = slot % PD_PAGE;
-    for (int g = grp; g < Hkv; g += ngrp) {
-        const float a = bf2f(row[(Hq + g) * dh + i]);
-        const float b = bf2f(row[(Hq + g) * dh + i + half]);
-        uint16_t* kp = kplane + ((size_t)blk * Hkv + g) * PD_PAGE * dh + off * dh;
-        kp[i] = f2bf(a * c - b * s);
-        kp[i + half] = f2bf(b * c + a * s);
-    }
-    for (int idx = threadIdx.x; idx < Hkv * dh; idx += 256) {
+    if (item < npairs) {
+        const int h = item / half, i = item % half;   // h < Hq: q head, else k head h - Hq
+        const int c0 = h * dh + i;
+        float a = 0.f, b = 0.f, pa[kMaxSplits], pb[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < S) {
+                pa[sp] = row[sp * plane + c0];
+                pb[sp] = row[sp * plane + c0 + half];
+            }
+        const int pos = positions[o];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < S) { a += pa[sp]; b += pb[sp]; }
+        const double inv = exp(-(2.0 * i / dh) * log((double)theta));
+        double sd, cd;
+        sincos((double)pos * inv, &sd, &cd);
+        const float c = (float)cd, s = (float)sd;
+        const uint16_t r0 = f2bf(a * c - b * s), r1 = f2bf(b * c + a * s);
+        if (h < Hq) {
+            q_out[(size_t)o * Hq * dh + c0] = r0;
+            q_out[(size_t)o * Hq * dh + c0 + half] = r1;
+        } else if (write) {
+            uint16_t* kp = kplane + ((size_t)blk * Hkv + (h - Hq)) * PD_PAGE * dh + off * dh;
+            kp[i] = r0;
+            kp[i + half] = r1;
+        }
+    } else if (write) {
+        const int idx = item - npairs;                 // V element: head idx / dh, dim idx % dh
+        float v = 0.f, pv[kMaxSplits];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < S) pv[sp] = row[sp * plane + (Hq + Hkv) * dh + idx];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplits; ++sp)
+            if (sp < S) v += pv[sp];
         const int g = idx / dh, cc = idx % dh;
-        uint16_t* vp = vplane + ((size_t)blk * Hkv + g) * PD_PAGE * dh;
-        vp[cc * PD_PAGE + off] = row[(Hq + Hkv) * dh + idx];
+        vplane[((size_t)blk * Hkv + g) * PD_PAGE * dh + cc * PD_PAGE + off] = f2bf(v);
     }
 }
 
@@ -157,6 +233,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* amax_v,
     const int m = blockIdx.x;
     float bv = -FLT_MAX;
     int bi = INT_MAX;
+#pragma unroll 8
     for (int t = threadIdx.x; t < ntiles; t += 256)
         better(bv, bi, amax_v[(size_t)m * ntiles + t], amax_i[(size_t)m * ntiles + t]);
 #pragma unroll
@@ -184,30 +261,46 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* amax_v,
 
 }  // namespace
 
-int launch_rmsnorm(const float* x, int ldx, const int32_t* rows, int rows_limit, int nrows,
-                   const uint16_t* gamma, uint16_t* y, int ldy, int d, float eps,
-                   int32_t* status, hipStream_t s) {
-    if (nrows <= 0) return PD_OK;
-    hipLaunchKernelGGL(rmsnorm_kernel, dim3(nrows), dim3(256), 0, s, x, ldx, rows, rows_limit,
-                       gamma, y, ldy, d, eps, status);
-    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
-}
+#define PD_ROW_NC(d, launch) \
+    switch (((d) + 1023) / 1024) {      \
+        case 1: launch(1); break;       \
+        case 2: launch(2); break;       \
+        case 3: launch(3); break;       \
+        case 4: launch(4); break;       \
+        default: return PD_EINVAL;      \
+    }
 
-int launch_layer0_input(const int32_t* ids, const uint16_t* embed, int V, const float* x,
-                        const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T, int d,
-                        float eps, int32_t* status, hipStream_t s) {
+int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
+                      int d, float eps, hipStream_t s) {
     if (T <= 0) return PD_OK;
-    hipLaunchKernelGGL(layer0_input_kernel, dim3(T), dim3(256), 0, s, ids, embed, V, x, g_emb,
-                       g_hid, u, d, eps, status);
+    if (S > kMaxSplits) return PD_EINVAL;
+#define L_(NC) hipLaunchKernelGGL(resid_norm_kernel<NC>, dim3(T), dim3(256), 0, s, ws, S, x, gamma, y, T, d, eps)
+    PD_ROW_NC(d, L_)
+#undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
-int launch_rope_cache(const uint16_t* qkv, const int32_t* positions, const int32_t* slots, int T,
+int launch_layer0_input(const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
+                        float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
+                        int d, float eps, int32_t* status, hipStream_t s) {
+    if (T <= 0) return PD_OK;
+    if (S > kMaxSplits) return PD_EINVAL;
+#define L_(NC) hipLaunchKernelGGL(layer0_input_kernel<NC>, dim3(T), dim3(256), 0, s, ws, S, ids, embed, V, \
+                                  x, g_emb, g_hid, u, T, d, eps, status)
+    PD_ROW_NC(d, L_)
+#undef L_
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
                       int Hq, int Hkv, int dh, float theta, uint16_t* q_out, uint16_t* kplane,
                       uint16_t* vplane, int num_blocks, int32_t* status, hipStream_t s) {
     if (T <= 0) return PD_OK;
-    hipLaunchKernelGGL(rope_cache_kernel, dim3(T), dim3(256), 0, s, qkv, positions, slots, Hq,
-                       Hkv, dh, theta, q_out, kplane, vplane, num_blocks, status);
+    if (S > kMaxSplits) return PD_EINVAL;
+    const int items = (Hq + Hkv) * (dh / 2) + Hkv * dh;
+    hipLaunchKernelGGL(rope_cache_kernel, dim3((items + 255) / 256, T), dim3(256), 0, s, ws, S,
+                       positions, slots, T, Hq, Hkv, dh, theta, q_out, kplane, vplane, num_blocks,
+                       status);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 

@@ -172,7 +172,7 @@ typedef struct pd_handle pd_handle;
  *   h          [host] handle slot: *h == NULL creates the handle (scratch is
  *              allocated then, and again, after a stream synchronize, when a
  *              later call needs more). One handle serves one stream at a time.
- *   m          [host] model; requires d, F, V multiples of 16, hidden3 = 3d,
+ *   m          [host] model; requires d, F, V multiples of 16, d <= 4096, hidden3 = 3d,
  *              Hq % Hkv == 0, dh in {64, 128}, 1 <= N <= PD_MAX_LAYERS,
  *              every weight pointer non-NULL.
  *   dims       [host] the same sizes given to pd_expand_batch; block_size must

@@ -110,7 +110,8 @@ def _model(**kw):
 
 
 @pytest.mark.parametrize("kw", [dict(dh=96), dict(Hq=6, Hkv=4), dict(d=250, hidden3=750), dict(hidden3=700),
-                                dict(N=0), dict(N=17), dict(V=4095), dict(F=690)])
+                                dict(N=0), dict(N=17), dict(V=4095), dict(F=690),
+                                dict(d=4112, hidden3=12336)])
 def test_forward_rejects_bad_model(lib, kw):
     h = ctypes.c_void_p(None)
     m, d, b = _model(**kw), _dims(hidden3=kw.get("hidden3", 768)), _fake_batch()
