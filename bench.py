@@ -93,6 +93,45 @@ def cpu_baseline(w, model_np, b, pool, budget_s: float = 30.0) -> dict:
             "seconds": dt}
 
 
+def copy_calibration(mib: int = 512, reps: int = 4):
+    """A plain device-to-device copy of known size: reads and writes
+    `mib` MiB per launch. Its FETCH_SIZE / WRITE_SIZE counter readings give
+    the factor that turns those counters into HBM bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} x {mib} MiB device copies")
+    print(json.dumps({"copy_calibration_bytes_per_launch": mib * (1 << 20), "launches": reps}))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_g_c1_traffic.md")
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per LM-head launch recorded by the FETCH_SIZE / WRITE_SIZE
+    counter passes (profiles/lmhead_g_c1_traffic.md), or None when they were
+    taken on another workload or on a different GEMM source than the one
+    built now."""
+    import hashlib
+    if workload != "g_c1" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("    ") and ":" in line:
+            k, v = line.strip().split(":", 1)
+            vals[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "drafting_pd_expand_amd", "csrc", "gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if vals.get("gemm_source_sha256_16") != digest or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +139,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="g_c1", choices=sorted(DESCR))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -204,7 +248,7 @@ def main():
         "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": "gemm_skinny_kernel<ARGMAX> (LM head + fused argmax)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload)},
         "cpu_baseline": cpu,
     }
     h.free()

@@ -47,8 +47,11 @@ namespace {
 // dh 128 (register budget); either way one workgroup holds 128 queries.
 // KV is staged through LDS in chunks of chunk_pages() pages, double buffered.
 constexpr float kNegInf = -INFINITY;
-template <int DH> constexpr int tiles_per_wave() { return DH == 64 ? 2 : 1; }
-template <int DH> constexpr int waves_per_wg() { return DH == 64 ? 4 : 8; }
+#ifndef PD_ATTN_TPW64
+#define PD_ATTN_TPW64 2
+#endif
+template <int DH> constexpr int tiles_per_wave() { return DH == 64 ? PD_ATTN_TPW64 : 1; }
+template <int DH> constexpr int waves_per_wg() { return DH == 64 ? 8 / PD_ATTN_TPW64 : 8; }
 template <int DH> constexpr int chunk_pages() { return DH == 64 ? 4 : 2; }
 // Running maxima are raised only when a new score exceeds them by more than
 // this (log2 units); exp2 arguments then stay <= kRescale, the final O / l is
@@ -299,26 +302,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     constexpr int PER = DH / 64;
     const size_t stride = (size_t)a.T * a.Hq;   // between splits, in (row, head) units
     const size_t base = (size_t)row * a.Hq + h;
-    float m0 = kNegInf, m1 = kNegInf;
-    if (lane < ns) m0 = a.part_ml[(lane * stride + base) * 2];
-    if (lane + 64 < ns) m1 = a.part_ml[((lane + 64) * stride + base) * 2];
-    const float M = wave_max(fmaxf(m0, m1));
+    float2 ml0 = make_float2(kNegInf, 0.f), ml1 = make_float2(kNegInf, 0.f);
+    if (lane < ns) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + base) * 2);
+    if (lane + 64 < ns) ml1 = *reinterpret_cast<const float2*>(a.part_ml + ((lane + 64) * stride + base) * 2);
+    const float M = wave_max(fmaxf(ml0.x, ml1.x));
     float w0 = 0.f, w1 = 0.f, L = 0.f;
     if (M != kNegInf) {
-        if (lane < ns) {
-            w0 = exp2f(m0 - M);
-            L += w0 * a.part_ml[(lane * stride + base) * 2 + 1];
-        }
-        if (lane + 64 < ns) {
-            w1 = exp2f(m1 - M);
-            L += w1 * a.part_ml[((lane + 64) * stride + base) * 2 + 1];
-        }
+        w0 = __builtin_amdgcn_exp2f(ml0.x - M);   // -inf -> 0 for missing splits
+        w1 = __builtin_amdgcn_exp2f(ml1.x - M);
+        L = w0 * ml0.y + w1 * ml1.y;
     }
     L = wave_sum(L);
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-#pragma unroll 16
+    // all split loads of a lane are independent: issue them 32 at a time
+#pragma unroll 32
     for (int sp = 0; sp < ns; ++sp) {
         const float w = __shfl(sp < 64 ? w0 : w1, sp & 63, kWave);
         const float* po = a.part_o + (sp * stride + base) * DH;

@@ -224,6 +224,213 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmArgs a) {
 }
 
 // Row groups of W per wave: fewer when more X rows share the registers.
+// ---------------------------------------------------------------------------
+// Tiled kernel for many rows (M > 64): a 128 x 128 output tile per workgroup,
+// K in steps of 64 staged through LDS (double buffered: the next step's
+// global loads are in registers while the current step's MFMAs run), four
+// waves each owning a 64 x 64 quarter (4 x 4 MFMA tiles). W is the A operand
+// and X the B operand, as in the streaming kernel, so the epilogues are the
+// same. For SwiGLU the tile's 128 W rows are 64 gate rows then the same 64 up
+// rows, and each wave takes 32 of each: a lane holds matching gate and up
+// columns.
+constexpr int kTM = 128, kTN = 128, kTK = 64;
+constexpr int kTRow = kTK + 8;   // padded LDS row (elements): 144 B stride, conflict-free 16-byte reads
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    __shared__ __align__(16) uint16_t ws_[2][kTN * kTRow];
+    __shared__ __align__(16) uint16_t xs_[2][kTM * kTRow];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
+    // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs,
+    // so XCD x takes the contiguous tile range [x*chunk, (x+1)*chunk) with the
+    // M blocks innermost: the workgroups sharing a W tile run back to back on
+    // one XCD and find it in that XCD's L2.
+    const int mblocks = (a.M + kTM - 1) / kTM;
+    const int total = a.ntiles * mblocks;
+    const int chunk = (total + 7) / 8;
+    const int tile = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
+    if (tile >= total) return;
+    const int m0 = (tile % mblocks) * kTM;
+    // column base of the tile: 128 W rows, or 64 gate + 64 up rows for SwiGLU
+    const int ntile = tile / mblocks;
+    const int n0 = ntile * (DUAL ? kTN / 2 : kTN);
+
+    // K range of this split (multiples of kTK)
+    const int ksteps = (a.K + kTK - 1) / kTK;
+    const int per = (ksteps + a.splits - 1) / a.splits;
+    const int kb = min(a.K, blockIdx.z * per * kTK);
+    const int ke = min(a.K, (blockIdx.z + 1) * per * kTK);
+
+    // staging: each thread moves 4 W and 4 X 16-byte units per K step
+    const uint16_t* wsrc[4];
+    const uint16_t* xsrc[4];
+    bool wok[4], xok[4];
+    int soff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int u = tid + 256 * j;
+        const int row = u >> 3, c8 = u & 7;
+        soff[j] = row * kTRow + c8 * 8;
+        int wrow;
+        if constexpr (DUAL) {
+            wrow = n0 + (row & 63);
+            wok[j] = wrow < a.N;
+            wsrc[j] = (row < 64 ? a.W : a.W2) + (size_t)(wok[j] ? wrow : 0) * a.K + c8 * 8;
+        } else {
+            wrow = n0 + row;
+            wok[j] = wrow < a.N;
+            wsrc[j] = a.W + (size_t)(wok[j] ? wrow : 0) * a.K + c8 * 8;
+        }
+        const int m = m0 + row;
+        xok[j] = m < a.M;
+        int xr = m;
+        if (xok[j] && a.xrows) {
+            xr = a.xrows[m];
+            if (xr < 0 || xr >= a.xrows_limit) {
+                xok[j] = false;
+                flag(a.status, PD_STATUS_BAD_ROW);
+            }
+        }
+        xsrc[j] = a.X + (size_t)(xok[j] ? xr : 0) * a.ldx + c8 * 8;
+    }
+    uint4 wreg[4], xreg[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + ((tid + 256 * j) & 7) * 8;
+            wreg[j] = (wok[j] && k < ke) ? *reinterpret_cast<const uint4*>(wsrc[j] + k0) : make_uint4(0, 0, 0, 0);
+            xreg[j] = (xok[j] && k < ke) ? *reinterpret_cast<const uint4*>(xsrc[j] + k0) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto sstore = [&](int b) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            *reinterpret_cast<uint4*>(&ws_[b][soff[j]]) = wreg[j];
+            *reinterpret_cast<uint4*>(&xs_[b][soff[j]]) = xreg[j];
+        }
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS rows of this wave's A (W) and B (X) fragments
+    int wrow_l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        wrow_l[i] = DUAL ? (i < 2 ? 32 * wn + 16 * i : 64 + 32 * wn + 16 * (i - 2)) : 64 * wn + 16 * i;
+
+    if (kb < ke) {
+        gload(kb);
+        sstore(0);
+    }
+    __syncthreads();
+    int b = 0;
+    for (int k0 = kb; k0 < ke; k0 += kTK) {
+        const bool more = k0 + kTK < ke;
+        if (more) gload(k0 + kTK);
+#pragma unroll
+        for (int kk = 0; kk < kTK / 32; ++kk) {
+            bf16x8 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(&ws_[b][(wrow_l[i] + r16) * kTRow + 32 * kk + 8 * g4]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8*>(&xs_[b][(64 * wm + 16 * j + r16) * kTRow + 32 * kk + 8 * g4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
+        }
+        if (more) sstore(b ^ 1);
+        __syncthreads();
+        b ^= 1;
+    }
+
+    // lane holds rows m = m0 + 64*wm + 16*j + r16 and 4 consecutive columns per fragment i
+    if constexpr (EPI == EPI_ARGMAX) {
+        __shared__ float s_v[2][kTM];
+        __shared__ int s_i[2][kTM];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ml = 64 * wm + 16 * j + r16;
+            const int m = m0 + ml;
+            float bv = -FLT_MAX;
+            int bi = INT_MAX;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = n0 + 64 * wn + 16 * i + 4 * g4;
+                if (n >= a.N) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) better(bv, bi, acc[i][j][e], n + e);
+                if (a.logits && m < a.M)
+                    *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[i][j];
+            }
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ov = __shfl_xor(bv, off, kWave);
+                const int oi = __shfl_xor(bi, off, kWave);
+                better(bv, bi, ov, oi);
+            }
+            if (g4 == 0) {
+                s_v[wn][ml] = bv;
+                s_i[wn][ml] = bi;
+            }
+        }
+        __syncthreads();
+        if (tid < kTM) {
+            const int m = m0 + tid;
+            float bv = s_v[0][tid];
+            int bi = s_i[0][tid];
+            better(bv, bi, s_v[1][tid], s_i[1][tid]);
+            if (m < a.M) {
+                a.amax_v[(size_t)m * a.ntiles + ntile] = bv;
+                a.amax_i[(size_t)m * a.ntiles + ntile] = bi;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + 64 * wm + 16 * j + r16;
+            if (m >= a.M) continue;
+            if constexpr (EPI == EPI_PARTIAL) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = n0 + 64 * wn + 16 * i + 4 * g4;
+                    if (n < a.N)
+                        *reinterpret_cast<f32x4*>(a.ws + ((size_t)blockIdx.z * a.M + m) * a.N + n) = acc[i][j];
+                }
+            } else {  // SwiGLU: fragments 0,1 = gate, 2,3 = the matching up columns
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int n = n0 + 32 * wn + 16 * i + 4 * g4;
+                    if (n >= a.N) continue;
+                    float h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) h[e] = silu(acc[i][j][e]) * acc[i + 2][j][e];
+                    uint2 pk;
+                    pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
+                    pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
+                    *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
+                }
+            }
+        }
+    }
+}
+
+template <int EPI>
+int launch_tiled(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    const int chunk = (p.ntiles * p.mblocks + 7) / 8;
+    hipLaunchKernelGGL(gemm_tiled_kernel<EPI>, dim3(8 * chunk, 1, p.splits), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
 template <int MT, int EPI>
 constexpr int rows_groups() {
     return EPI == EPI_ARGMAX ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
@@ -247,6 +454,7 @@ int launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    if (p.tiled) return launch_tiled<EPI>(p, a, s);
     switch (p.mt) {
         case 1: return launch_cfg<1, EPI>(p, a, s);
         case 2: return launch_cfg<2, EPI>(p, a, s);
@@ -258,6 +466,27 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 
 GemmPlan plan_gemm(int M, int N, int K, int epi) {
     GemmPlan p;
+    p.tiled = M > 64;
+    if (p.tiled) {
+        // 128 x 128 tiles; K splits (partial planes, summed by the consumer)
+        // only when the tile count leaves most of the 256 CUs idle
+        p.mt = 0;
+        p.rg = 0;
+        p.wk = 4;
+        p.mblocks = (M + kTM - 1) / kTM;
+        const int cols = (epi == EPI_SWIGLU) ? kTN / 2 : kTN;
+        p.ntiles = (N + cols - 1) / cols;
+        p.splits = 1;
+        if (epi == EPI_PARTIAL) {
+            const long tiles = (long)p.ntiles * p.mblocks;
+            const int ksteps = (K + kTK - 1) / kTK;
+            int s = (int)((512 + tiles - 1) / tiles);
+            if (s > 4) s = 4;
+            while (s > 1 && s * 4 > ksteps) --s;
+            p.splits = s < 1 ? 1 : s;
+        }
+        return p;
+    }
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.mblocks = (M + 16 * p.mt - 1) / (16 * p.mt);
     p.rg = p.mt == 1 ? (epi == EPI_ARGMAX ? rows_groups<1, EPI_ARGMAX>() : rows_groups<1, EPI_SWIGLU>())

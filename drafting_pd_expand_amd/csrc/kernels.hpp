@@ -36,6 +36,7 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
+    bool tiled;    // 128 x 128 LDS-tiled kernel (many rows) instead of weight streaming
     int mt;        // 16-row MFMA tiles of X per workgroup (1, 2 or 4)
     int mblocks;   // workgroups along M
     int rg;        // 16-row groups of W per workgroup
