@@ -43,20 +43,27 @@ namespace pd {
 
 namespace {
 
-// Query tiles per wave and waves per workgroup: 2 x 4 for dh 64, 1 x 8 for
-// dh 128 (register budget); either way one workgroup holds 128 queries.
-// KV is staged through LDS in chunks of chunk_pages() pages, double buffered.
 constexpr float kNegInf = -INFINITY;
-#ifndef PD_ATTN_TPW64
-#define PD_ATTN_TPW64 2
-#endif
-template <int DH> constexpr int tiles_per_wave() { return DH == 64 ? PD_ATTN_TPW64 : 1; }
-template <int DH> constexpr int waves_per_wg() { return DH == 64 ? 8 / PD_ATTN_TPW64 : 8; }
-template <int DH> constexpr int chunk_pages() { return DH == 64 ? 4 : 2; }
 // Running maxima are raised only when a new score exceeds them by more than
 // this (log2 units); exp2 arguments then stay <= kRescale, the final O / l is
-// unchanged, and the 4*dh/16 accumulator rescales are skipped on most pages.
+// unchanged, and the accumulator rescales are skipped on most pages.
 constexpr float kRescale = 8.0f;
+constexpr int kBtMax = 512;   // block-table entries of one split cached in LDS
+
+// Per head size: waves per workgroup, query tiles per wave (one workgroup
+// holds 128 queries), pages per LDS stage, stages in the ring, 1 KB loads per
+// page (K then V^T) and per wave per stage.
+template <int DH>
+struct AttnCfg {
+    static constexpr int NW = DH == 64 ? 4 : 8;
+    static constexpr int TPW = DH == 64 ? 2 : 1;
+    static constexpr int CH = DH == 64 ? 4 : 2;
+    static constexpr int NST = 4;
+    static constexpr int LPP = DH / 16;            // 1 KB blocks per page: K DH/32, V DH/32
+    static constexpr int L = CH * LPP / NW;        // loads per wave per stage
+    static constexpr int PE = 16 * DH;             // elements of one page of K (or V)
+    static_assert(CH * LPP % NW == 0, "stage loads split evenly over the waves");
+};
 
 __device__ __forceinline__ int num_splits(int seq, int nsmax, int min_split) {
     const int ns = (seq + min_split - 1) / min_split;
@@ -68,22 +75,34 @@ __device__ __forceinline__ int split_len(int seq, int ns) {
     return (l + PD_PAGE - 1) & ~(PD_PAGE - 1);
 }
 
+// LDS swizzles (element offsets inside one page of the stage): a K row of key
+// `key` keeps its 16-byte chunks XOR-permuted, a V^T row (one dim, 16 keys)
+// keeps its two 16-byte halves swapped on every other group of 8 rows, so the
+// MFMA fragment reads of 16 lanes hit 16 different bank groups.
 template <int DH>
-__global__ __launch_bounds__(64 * waves_per_wg<DH>()) void attn_split_kernel(AttnArgs a) {
+__device__ __forceinline__ int k_lds(int key, int chunk) {
+    const int sw = DH == 64 ? ((key & 7) ^ (key >> 3)) : key;
+    return key * DH + ((chunk ^ sw) << 3);
+}
+__device__ __forceinline__ int v_lds(int row, int unit /* 4-key unit 0..3 */) {
+    const int half = (unit >> 1) ^ ((row >> 3) & 1);
+    return row * PD_PAGE + (half << 3) + ((unit & 1) << 2);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int DH>
+__global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnArgs a) {
+    using Cf = AttnCfg<DH>;
     constexpr int KB = DH / 32;  // 16x16x32 steps over dh for the scores
     constexpr int OT = DH / 16;  // 16-dim output tiles
-    constexpr int TPW = tiles_per_wave<DH>();
-    constexpr int NW = waves_per_wg<DH>();
-    constexpr int NT = 64 * NW;
-    constexpr int CH = chunk_pages<DH>();
-    constexpr int KROW = DH + 8;            // padded K row in LDS (elements): spreads banks
-    constexpr int VROW = PD_PAGE + 8;       // padded V^T row in LDS (elements): 48 B stride
-    constexpr int UPP = 4 * DH;             // 16-byte units per page (K then V)
-    constexpr int UPT = CH * UPP / NT;      // units each thread stages per chunk
-    static_assert(CH * UPP % NT == 0, "staging split");
-    __shared__ __align__(16) uint16_t ks[2][CH * 16 * KROW];
-    __shared__ __align__(16) uint16_t vs[2][CH * DH * VROW];
-    __shared__ int pvalid[2][CH];
+    constexpr int TPW = Cf::TPW, NW = Cf::NW, NT = 64 * NW, CH = Cf::CH, NST = Cf::NST;
+    __shared__ __align__(16) uint16_t kv[NST][CH][2][Cf::PE];   // [stage][page][K, V^T]
+    __shared__ int btc[kBtMax];
+    __shared__ int pv[NST][CH];
 
     const int r = blockIdx.z, g = blockIdx.y, s = blockIdx.x;
     const int tid = threadIdx.x;
@@ -101,55 +120,54 @@ __global__ __launch_bounds__(64 * waves_per_wg<DH>()) void attn_split_kernel(Att
     const int sl = split_len(seq, ns);
     const int kb = s * sl;
     const int ke = min(seq, kb + sl);
-    const int npages = ke > kb ? (ke - kb + PD_PAGE - 1) / PD_PAGE : 0;
+    int npages = ke > kb ? (ke - kb + PD_PAGE - 1) / PD_PAGE : 0;
+    if (npages > kBtMax) {  // the host sizes splits below this; never read past the cache
+        if (tid == 0) flag(a.status, PD_STATUS_BAD_ROW);
+        npages = 0;
+    }
     const int nchunks = (npages + CH - 1) / CH;
     const int G = a.Hq / a.Hkv;
     const int nq = (row1 - row0) * G;
     const int32_t* bt = a.block_table + (size_t)r * a.max_blocks + kb / PD_PAGE;
+    for (int i = tid; i < npages; i += NT) btc[i] = bt[i];
+    __syncthreads();
 
-    uint4 stg[UPT];
-    // global -> registers for chunk c (pages past the split read nothing)
-    auto stage = [&](int c) {
+    // global -> LDS for chunk c into ring slot `slot`: every wave issues exactly
+    // Cf::L 1 KB loads (pages past the split or with a bad block-table entry
+    // read page 0 of the pool and are marked invalid), so vmcnt counts agree
+    auto issue = [&](int c, int slot) {
 #pragma unroll
-        for (int j = 0; j < UPT; ++j) {
-            const int u = tid + j * NT;
-            const int pi = u / UPP, w = u % UPP;
-            const int pg = c * CH + pi;
-            stg[j] = make_uint4(0, 0, 0, 0);
-            if (pg < npages) {
-                const int blk = bt[pg];
-                if (blk >= 0 && blk < a.num_blocks) {
-                    const size_t base = ((size_t)blk * a.Hkv + g) * PD_PAGE * DH;
-                    const uint16_t* src = (w < 2 * DH) ? a.kplane + base + w * 8
-                                                       : a.vplane + base + (w - 2 * DH) * 8;
-                    stg[j] = *reinterpret_cast<const uint4*>(src);
-                }
+        for (int q = 0; q < Cf::L; ++q) {
+            const int inst = wave + NW * q;
+            const int p = inst / Cf::LPP, part = inst % Cf::LPP;
+            const int pg = c * CH + p;
+            const int blk = pg < npages ? btc[pg] : -1;
+            const bool ok = blk >= 0 && blk < a.num_blocks;
+            const size_t pbase = ((size_t)(ok ? blk : 0) * a.Hkv + g) * Cf::PE;
+            const uint16_t* src;
+            uint16_t* dst;
+            if (part < Cf::LPP / 2) {           // K: rows of 64 / DH*2/16 keys per 1 KB block
+                constexpr int KPB = 512 / DH;   // keys per block
+                const int key = KPB * part + lane / (DH / 8);
+                const int chunk = lane % (DH / 8);
+                const int sw = DH == 64 ? ((key & 7) ^ (key >> 3)) : key;
+                src = a.kplane + pbase + key * DH + ((chunk ^ sw) << 3);
+                dst = &kv[slot][p][0][part * 512];
+            } else {                            // V^T: 32 dim rows of 16 keys per 1 KB block
+                const int b = part - Cf::LPP / 2;
+                const int row = 32 * b + lane / 2;
+                const int half = (lane & 1) ^ ((row >> 3) & 1);
+                src = a.vplane + pbase + row * PD_PAGE + (half << 3);
+                dst = &kv[slot][p][1][b * 512];
             }
-        }
-    };
-    // registers -> LDS buffer b; page validity flags alongside
-    auto commit = [&](int c, int b) {
-#pragma unroll
-        for (int j = 0; j < UPT; ++j) {
-            const int u = tid + j * NT;
-            const int pi = u / UPP, w = u % UPP;
-            if (w < 2 * DH) {
-                const int key = w / (DH / 8), c8 = w % (DH / 8);
-                *reinterpret_cast<uint4*>(&ks[b][(pi * 16 + key) * KROW + c8 * 8]) = stg[j];
-            } else {
-                const int vu = w - 2 * DH;  // V^T row vu / 2, keys 8 * (vu % 2) ..
-                *reinterpret_cast<uint4*>(&vs[b][(pi * DH + vu / 2) * VROW + 8 * (vu % 2)]) = stg[j];
-            }
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
         }
         if (tid < CH) {
             const int pg = c * CH + tid;
-            int ok = 0;
-            if (pg < npages) {
-                const int blk = bt[pg];
-                ok = blk >= 0 && blk < a.num_blocks;
-                if (!ok) flag(a.status, PD_STATUS_BAD_PAGE);
-            }
-            pvalid[b][tid] = ok;
+            const int blk = pg < npages ? btc[pg] : -1;
+            const int ok = blk >= 0 && blk < a.num_blocks;
+            if (pg < npages && !ok) flag(a.status, PD_STATUS_BAD_PAGE);
+            pv[slot][tid] = ok;
         }
     };
 
@@ -176,94 +194,98 @@ __global__ __launch_bounds__(64 * waves_per_wg<DH>()) void attn_split_kernel(Att
             mrun[tt] = kNegInf;
             lrun[tt] = 0.f;
         }
+        wait_vmcnt<0>();   // query fragments in registers before the ring starts counting
 
-        if (nchunks > 0) {
-            stage(0);
-            commit(0, 0);
-        }
-        __syncthreads();
+        for (int st = 0; st < NST - 1 && st < nchunks; ++st) issue(st, st);
         for (int c = 0; c < nchunks; ++c) {
-            const int b = c & 1;
-            if (c + 1 < nchunks) stage(c + 1);   // next chunk's loads in flight
-            if (wave_has) {
-                // pages in pairs: 32 keys per softmax step and per PV MFMA
-                for (int pi = 0; pi < CH; pi += 2) {
-                    const int p0 = kb + (c * CH + pi) * PD_PAGE;
-                    if (p0 >= ke) break;
-                    const bool okA = pvalid[b][pi] != 0;
-                    const bool okB = p0 + PD_PAGE < ke && pvalid[b][pi + 1] != 0;
-                    bf16x8 kA[KB], kB[KB], vab[OT];
+            // loads of chunk c done (later chunks may stay in flight), then all waves' loads
+            const int later = min(NST - 2, nchunks - 1 - c);
+            if (later >= 2) wait_vmcnt<2 * Cf::L>();
+            else if (later == 1) wait_vmcnt<Cf::L>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (c + NST - 1 < nchunks) issue(c + NST - 1, (c + NST - 1) % NST);
+            const int b = c % NST;
+            if (!wave_has) continue;
+            // pages in pairs: 32 keys per softmax step and per PV MFMA
+            for (int pi = 0; pi < CH; pi += 2) {
+                const int p0 = kb + (c * CH + pi) * PD_PAGE;
+                if (p0 >= ke) break;
+                const bool okA = pv[b][pi] != 0;
+                const bool okB = p0 + PD_PAGE < ke && pv[b][pi + 1] != 0;
+                const uint16_t* KA = kv[b][pi][0];
+                const uint16_t* KBp = kv[b][pi + 1][0];
+                const uint16_t* VA = kv[b][pi][1];
+                const uint16_t* VBp = kv[b][pi + 1][1];
+                bf16x8 kA[KB], kB[KB], vab[OT];
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) {
+                    kA[kk] = *reinterpret_cast<const bf16x8*>(KA + k_lds<DH>(r16, 4 * kk + g4));
+                    kB[kk] = *reinterpret_cast<const bf16x8*>(KBp + k_lds<DH>(r16, 4 * kk + g4));
+                }
+                // V^T fragments of both pages: k slots 0-3 = page A keys 4*g4.., 4-7 = page B keys 4*g4..
+#pragma unroll
+                for (int j = 0; j < OT; ++j) {
+                    uint2 va = *reinterpret_cast<const uint2*>(VA + v_lds(16 * j + r16, g4));
+                    uint2 vb = *reinterpret_cast<const uint2*>(VBp + v_lds(16 * j + r16, g4));
+                    if (!okA) va = make_uint2(0, 0);
+                    if (!okB) vb = make_uint2(0, 0);
+                    vab[j] = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
+                }
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) {
+                    f32x4 sA = f32x4{0.f, 0.f, 0.f, 0.f}, sB = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < KB; ++kk) {
-                        kA[kk] = *reinterpret_cast<const bf16x8*>(&ks[b][(pi * 16 + r16) * KROW + 32 * kk + 8 * g4]);
-                        kB[kk] = *reinterpret_cast<const bf16x8*>(&ks[b][((pi + 1) * 16 + r16) * KROW + 32 * kk + 8 * g4]);
+                        sA = mfma_16x16x32(kA[kk], qv[tt][kk], sA);
+                        sB = mfma_16x16x32(kB[kk], qv[tt][kk], sB);
                     }
-                    // V^T fragments of both pages: k slots 0-3 = page A keys 4*g4.., 4-7 = page B keys 4*g4..
-#pragma unroll
-                    for (int j = 0; j < OT; ++j) {
-                        uint2 va = *reinterpret_cast<const uint2*>(&vs[b][(pi * DH + 16 * j + r16) * VROW + 4 * g4]);
-                        uint2 vb = *reinterpret_cast<const uint2*>(&vs[b][((pi + 1) * DH + 16 * j + r16) * VROW + 4 * g4]);
-                        if (!okA) va = make_uint2(0, 0);
-                        if (!okB) vb = make_uint2(0, 0);
-                        const uint4 v4 = make_uint4(va.x, va.y, vb.x, vb.y);
-                        vab[j] = __builtin_bit_cast(bf16x8, v4);
-                    }
-#pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) {
-                        f32x4 sA = f32x4{0.f, 0.f, 0.f, 0.f}, sB = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int kk = 0; kk < KB; ++kk) {
-                            sA = mfma_16x16x32(kA[kk], qv[tt][kk], sA);
-                            sB = mfma_16x16x32(kB[kk], qv[tt][kk], sB);
-                        }
-                        // raw scores of keys p0+4*g4+i (page A) and p0+16+4*g4+i (page B)
-                        float sc[8] = {sA[0], sA[1], sA[2], sA[3], sB[0], sB[1], sB[2], sB[3]};
-                        // keys this query may see: t <= lim (invalid queries: no limit, don't care)
-                        const int lim = qok[tt] && qpos[tt] >= 0 ? min(ke - 1, qpos[tt]) : 0x7fffffff;
-                        if (__any(p0 + 2 * PD_PAGE - 1 > lim || !okA || !okB)) {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                const int t = p0 + (i >> 2) * PD_PAGE + 4 * g4 + (i & 3);
-                                const bool ok = (i < 4 ? okA : okB) && t <= lim;
-                                sc[i] = ok ? sc[i] : kNegInf;
-                            }
-                        }
-                        float mx = sc[0];
-#pragma unroll
-                        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-                        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-                        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-                        const float mnew = mx * a.scale_log2;   // -inf stays -inf
-                        const bool raise = mnew > mrun[tt] + kRescale;
-                        if (__any(raise)) {
-                            const float alpha = raise ? __builtin_amdgcn_exp2f(mrun[tt] - mnew) : 1.0f;
-                            if (raise) mrun[tt] = mnew;
-                            lrun[tt] *= alpha;
-#pragma unroll
-                            for (int j = 0; j < OT; ++j) o[tt][j] = o[tt][j] * alpha;
-                        }
-                        const float muse = (mrun[tt] == kNegInf) ? 0.f : mrun[tt];
-                        float p[8], ls = 0.f;
+                    // raw scores of keys p0+4*g4+i (page A) and p0+16+4*g4+i (page B)
+                    float sc[8] = {sA[0], sA[1], sA[2], sA[3], sB[0], sB[1], sB[2], sB[3]};
+                    // keys this query may see: t <= lim (invalid queries: no limit, don't care)
+                    const int lim = qok[tt] && qpos[tt] >= 0 ? min(ke - 1, qpos[tt]) : 0x7fffffff;
+                    if (__any(p0 + 2 * PD_PAGE - 1 > lim || !okA || !okB)) {
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
-                            // raw v_exp_f32: weights below 2^-126 flush to zero
-                            p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -muse));
-                            ls += p[i];
+                            const int t = p0 + (i >> 2) * PD_PAGE + 4 * g4 + (i & 3);
+                            const bool ok = (i < 4 ? okA : okB) && t <= lim;
+                            sc[i] = ok ? sc[i] : kNegInf;
                         }
-                        ls += __shfl_xor(ls, 16, kWave);
-                        ls += __shfl_xor(ls, 32, kWave);
-                        lrun[tt] += ls;
-                        bf16x8 pb;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
-#pragma unroll
-                        for (int j = 0; j < OT; ++j) o[tt][j] = mfma_16x16x32(vab[j], pb, o[tt][j]);
                     }
+                    float mx = sc[0];
+#pragma unroll
+                    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+                    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                    const float mnew = mx * a.scale_log2;   // -inf stays -inf
+                    const bool raise = mnew > mrun[tt] + kRescale;
+                    if (__any(raise)) {
+                        const float alpha = raise ? __builtin_amdgcn_exp2f(mrun[tt] - mnew) : 1.0f;
+                        if (raise) mrun[tt] = mnew;
+                        lrun[tt] *= alpha;
+#pragma unroll
+                        for (int j = 0; j < OT; ++j) o[tt][j] = o[tt][j] * alpha;
+                    }
+                    const float muse = (mrun[tt] == kNegInf) ? 0.f : mrun[tt];
+                    float p[8], ls = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        // raw v_exp_f32: weights below 2^-126 flush to zero
+                        p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -muse));
+                        ls += p[i];
+                    }
+                    ls += __shfl_xor(ls, 16, kWave);
+                    ls += __shfl_xor(ls, 32, kWave);
+                    lrun[tt] += ls;
+                    bf16x8 pb;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
+#pragma unroll
+                    for (int j = 0; j < OT; ++j) o[tt][j] = mfma_16x16x32(vab[j], pb, o[tt][j]);
                 }
             }
-            if (c + 1 < nchunks) commit(c + 1, b ^ 1);
-            __syncthreads();
         }
+        __syncthreads();   // ring slots are free again before a next query pass reuses them
 
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
@@ -332,12 +354,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 
 template <int DH>
 int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    constexpr int NW = AttnCfg<DH>::NW;
     if (e0) (void)hipEventRecord(e0, s);
     // splits a request can have: bounded by nsmax and by the block table's reach
     const int reach = (a.max_blocks * PD_PAGE + a.min_split - 1) / a.min_split;
     const int gx = reach < a.nsmax ? reach : a.nsmax;
-    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3(gx, a.Hkv, a.C), dim3(64 * waves_per_wg<DH>()), 0, s,
-                       a);
+    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3(gx, a.Hkv, a.C), dim3(64 * NW), 0, s, a);
     if (e1) (void)hipEventRecord(e1, s);
     if (hipGetLastError() != hipSuccess) return PD_EHIP;
     hipLaunchKernelGGL(attn_merge_kernel<DH>, dim3((a.T * a.Hq + 3) / 4), dim3(256), 0, s, a);
