@@ -26,6 +26,12 @@ FLAGS = [
 ]
 
 
+# per-source extra flags: the attention kernels keep MFMA operands and
+# accumulators in arch VGPRs (no AGPR <-> VGPR copies around the softmax), and
+# take max/min without NaN canonicalisation (no NaN reaches the softmax)
+FILE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+
+
 def _hipcc() -> str:
     for c in ("/opt/rocm/bin/hipcc", "hipcc"):
         if os.path.isabs(c) and os.path.exists(c):
@@ -53,11 +59,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in SOURCES:
         obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max(1, min(jobs, len(cmds)))) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # -z defs: an unresolved symbol (e.g. a kernel stub that was not emitted)
+    # fails the build instead of the first dlopen
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

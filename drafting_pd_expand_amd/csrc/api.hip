@@ -79,8 +79,9 @@ struct Timed {
 };
 
 struct Layout {
-    size_t x, u, q, ao, act, ws, po, pml, amv, ami, total;
-    int T, R, nsmax, min_split, ntilesV;
+    size_t x, u, q, ao, act, ws, po, pml, plan, amv, ami, total;
+    int T, R, ntilesV;
+    AttnSplit sp;
 };
 
 Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
@@ -91,9 +92,7 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
     L.R = R;
     const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
     const int hd = m->Hq * m->dh;
-    // split-KV: aim for ~2048 workgroups, at least min_split keys per split
-    L.min_split = 128;
-    L.nsmax = std::max(1, std::min(128, (2048 + d->C * m->Hkv - 1) / (d->C * m->Hkv)));
+    L.sp = plan_attn_split(d->C, T, m->Hq, m->Hkv, m->dh, d->max_blocks);
     size_t ws = 0;
     auto need = [&](int M, int N, int K) {
         GemmPlan p = plan_gemm(M, N, K, EPI_PARTIAL);
@@ -113,8 +112,9 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
     L.ao = carve((size_t)T * hd * 2);
     L.act = carve((size_t)T * m->F * 2);
     L.ws = carve(ws * 4);
-    L.po = carve((size_t)L.nsmax * T * hd * 4);
-    L.pml = carve((size_t)L.nsmax * T * m->Hq * 2 * 4);
+    L.po = carve((size_t)L.sp.scap * T * hd * 4);
+    L.pml = carve((size_t)L.sp.scap * T * m->Hq * 2 * 4);
+    L.plan = carve(attn_plan_ints(L.sp) * 4);
     L.amv = carve((size_t)R * L.ntilesV * 4);
     L.ami = carve((size_t)R * L.ntilesV * 4);
     L.total = off;
@@ -215,6 +215,7 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     if (dims->C == 0) return PD_OK;
     if (dims->block_size != PD_PAGE || dims->hidden3 != m->hidden3) return PD_EINVAL;
     if (!block_table || !kv_cache || !draft_ids) return PD_EINVAL;
+    if (dims->max_blocks > PD_MAX_BLOCKS) return PD_EINVAL;
     if ((long long)dims->num_blocks * m->Hkv * PD_PAGE * m->dh * 2 * m->N > (1LL << 40))
         return PD_EINVAL;
     hipStream_t s = (hipStream_t)stream;
@@ -262,6 +263,21 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     };
 #define PD_TRY(expr) do { if ((rc = (expr)) != PD_OK) return rc; } while (0)
     int sp = 1;
+    // attention arguments shared by every layer; the split plan is built once
+    AttnArgs aa;
+    std::memset(&aa, 0, sizeof(aa));
+    aa.positions = b->positions; aa.is_rejected = b->is_rejected;
+    aa.cu_out = b->cu_out; aa.seq_lens = b->seq_lens; aa.block_table = block_table;
+    aa.C = dims->C; aa.T = T; aa.Hq = m->Hq; aa.Hkv = m->Hkv;
+    aa.max_blocks = dims->max_blocks; aa.num_blocks = dims->num_blocks;
+    aa.sp = L.sp; aa.plan = (int32_t*)(S + L.plan);
+    aa.scale_log2 = 1.4426950408889634f / sqrtf((float)m->dh);
+    aa.part_o = (float*)(S + L.po); aa.part_ml = (float*)(S + L.pml);
+    aa.out = ao; aa.status = st;
+    {
+        Timed t(h, PD_KERNEL_OTHER, s);
+        PD_TRY(launch_attn_plan(aa, s));
+    }
 
     // fc projection 3d -> d (starts the residual stream), then the layer-0 input
     PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr, T, d,
@@ -283,16 +299,7 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
             PD_TRY(launch_rope_cache(ws, sp, b->positions, b->slot_mapping, T, m->Hq, m->Hkv, m->dh,
                                      m->rope_theta, q, kpl, vpl, dims->num_blocks, st, s));
         }
-        AttnArgs aa;
         aa.q = q; aa.kplane = kpl; aa.vplane = vpl;
-        aa.positions = b->positions; aa.is_rejected = b->is_rejected;
-        aa.cu_out = b->cu_out; aa.seq_lens = b->seq_lens; aa.block_table = block_table;
-        aa.C = dims->C; aa.T = T; aa.Hq = m->Hq; aa.Hkv = m->Hkv;
-        aa.max_blocks = dims->max_blocks; aa.num_blocks = dims->num_blocks;
-        aa.nsmax = L.nsmax; aa.min_split = L.min_split;
-        aa.scale_log2 = 1.4426950408889634f / sqrtf((float)m->dh);
-        aa.part_o = (float*)(S + L.po); aa.part_ml = (float*)(S + L.pml);
-        aa.out = ao; aa.status = st;
         {
             hipEvent_t e0 = nullptr, e1 = nullptr;
             if (h->prof & (1 << PD_KERNEL_ATTN)) { e0 = take_event(h); e1 = take_event(h); }

@@ -10,31 +10,37 @@
 // score of rotated q and k depends on positions only through their
 // difference, so the cache stores keys already rotated.
 //
-// Work unit = (request, kv head, KV split). All query vectors of the request
-// that share the kv head (GQA group x rows, e.g. 8 x 13 = 104) are packed
-// into 16-wide MFMA tiles (two per wave at dh 64, one at dh 128). For each
-// pair of 16-token pages:
-//   S^T(16 keys x 16 queries) = K_page (16 x dh) * Q^T  -- 16x16x32 MFMA,
-//       the K page is token-major so a lane's 16-byte load is one key's
-//       8 consecutive dims;
-//   online softmax per query column (fp32, exp2 domain; the four lane groups
-//       of a column are combined with two xor shuffles);
-//   O^T(dh x 16 queries) += V^T (dh x 32 keys) * P^T -- one 16x16x32 MFMA
-//       per pair of pages: a lane's S^T accumulators (keys 4*g4..+3 of each
-//       page) are its B operand once the MFMA's k slots are mapped to
-//       (page A keys 4*g4..+3, page B keys 4*g4..+3); the V page is
-//       dim-major so the matching A operand is two 8-byte reads;
-//   softmax bookkeeping per 32 keys: one max and one sum exchange, scores
-//       scaled inside a single FMA, masking and accumulator rescaling only
-//       when a wave vote says some lane needs them.
-// The workgroup stages each chunk of pages into LDS once (all waves share it;
-// the next chunk's global loads are in flight while the current one is
-// used). Nothing is transposed: the LDS layout is the page layout, with K rows
-// padded by 16 bytes and V^T rows to 48 bytes so the fragment reads hit
-// distinct banks. Each split writes an
-// unnormalized partial (O, running max, running sum) per query; a merge
-// kernel combines the splits in order (deterministic) and writes bf16 output.
+// Work split. A plan kernel (once per forward) picks one split length for
+// the whole batch from the total context, so every workgroup streams about
+// the same number of pages whatever the length mix, and lists the
+// (request, split) units. Work unit = (unit, kv head). All query vectors of
+// the request that share the kv head (GQA group x rows, e.g. 8 x 14 = 112)
+// are packed into 16-wide MFMA tiles, two per wave.
+//
+// Per pair of 16-token pages (32 keys), per query tile:
+//   S^T(16 x 16) = K_rows (16 x dh) * Q^T, twice (16x16x32 MFMA). The A
+//     operand rows are picked so that lane group g (lanes 16g..16g+15) ends up
+//     holding the scores of keys 8g..8g+7 of the pair in its 8 accumulators;
+//   online softmax per query column in fp32, exp2 domain, with a lazy running
+//     max: the column max is exchanged (two row-swap permutes) and the accumulators
+//     rescaled only when a wave vote finds a score more than 2^8 above it;
+//   O^T(dh x 16) += V^T (dh x 32 keys) * P^T: a lane's 8 probabilities
+//     (rounded to bf16) are its B operand as they are, and its A operand is
+//     one 16-byte read of the dim-major V page (keys 8g..8g+7 of one dim
+//     row); one more MFMA with an all-ones A operand accumulates the column
+//     sums of the same rounded weights, so no VALU adds or shuffles are
+//     spent on the running sum.
+// Pages are staged global -> LDS directly (global_load_lds, 16 B per lane) in
+// a 4-deep ring of chunks shared by all waves; the LDS layouts are XOR
+// swizzles of the page layout chosen so that every 8-lane group of a 16-byte
+// fragment read touches 8 different bank groups. Pages past the split or
+// with a bad block-table entry are read from a zero page and masked.
+// Each split writes an unnormalized partial (O, running max, running sum);
+// a merge kernel combines the splits in order (deterministic). A request
+// with a single split writes its normalized bf16 output directly.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -48,50 +54,154 @@ constexpr float kNegInf = -INFINITY;
 // this (log2 units); exp2 arguments then stay <= kRescale, the final O / l is
 // unchanged, and the accumulator rescales are skipped on most pages.
 constexpr float kRescale = 8.0f;
-constexpr int kBtMax = 512;   // block-table entries of one split cached in LDS
+constexpr int kBtMax = 512;               // block-table entries of one split cached in LDS
+constexpr int kMaxSplitKeys = kBtMax * PD_PAGE;
+constexpr int kMaxSplits = 128;           // splits of one request the merge combines
 
-// Per head size: waves per workgroup, query tiles per wave (one workgroup
-// holds 128 queries), pages per LDS stage, stages in the ring, 1 KB loads per
+// K and V of pages that are past the split end or invalid come from here
+// (zero-initialised at load; nothing writes it).
+__device__ __align__(16) uint16_t g_zero_page[PD_PAGE * 128];
+
+// Per head size: waves per workgroup, query tiles per wave (one pass covers
+// 128 queries), pages per LDS stage, stages in the ring, 1 KB loads per
 // page (K then V^T) and per wave per stage.
 template <int DH>
 struct AttnCfg {
-    static constexpr int NW = DH == 64 ? 4 : 8;
-    static constexpr int TPW = DH == 64 ? 2 : 1;
+    static constexpr int NW = 4;
+    static constexpr int TPW = 2;
     static constexpr int CH = DH == 64 ? 4 : 2;
     static constexpr int NST = 4;
     static constexpr int LPP = DH / 16;            // 1 KB blocks per page: K DH/32, V DH/32
     static constexpr int L = CH * LPP / NW;        // loads per wave per stage
     static constexpr int PE = 16 * DH;             // elements of one page of K (or V)
     static_assert(CH * LPP % NW == 0, "stage loads split evenly over the waves");
+    static_assert(CH % 2 == 0, "pages are consumed in pairs");
+    static_assert(LPP % NW == 0, "a wave's loads of one page are whole parts");
 };
 
-__device__ __forceinline__ int num_splits(int seq, int nsmax, int min_split) {
-    const int ns = (seq + min_split - 1) / min_split;
-    return ns < nsmax ? ns : nsmax;
-}
+// LDS swizzles (element offsets inside one staged page). A K row keeps its
+// 16-byte chunks XOR-permuted by key_sw(key); the fragment reads of one
+// 8-lane group are keys {0-3, 8-11} (or {4-7, 12-15}) at one chunk, which
+// key_sw maps to 8 distinct chunk positions. A V^T row (one dim, 16 keys)
+// keeps its two 16-byte halves swapped on rows 4-7 of every 8, so the reads
+// of rows 0..7 at one half cover 8 distinct 16-byte positions.
+__device__ __forceinline__ int key_sw(int key) { return (key & 3) | ((key >> 1) & 4); }
+__device__ __forceinline__ int v_half(int row, int half) { return half ^ ((row >> 2) & 1); }
 
-__device__ __forceinline__ int split_len(int seq, int ns) {
-    const int l = (seq + ns - 1) / ns;
-    return (l + PD_PAGE - 1) & ~(PD_PAGE - 1);
-}
-
-// LDS swizzles (element offsets inside one page of the stage): a K row of key
-// `key` keeps its 16-byte chunks XOR-permuted, a V^T row (one dim, 16 keys)
-// keeps its two 16-byte halves swapped on every other group of 8 rows, so the
-// MFMA fragment reads of 16 lanes hit 16 different bank groups.
-template <int DH>
-__device__ __forceinline__ int k_lds(int key, int chunk) {
-    const int sw = DH == 64 ? ((key & 7) ^ (key >> 3)) : key;
-    return key * DH + ((chunk ^ sw) << 3);
-}
-__device__ __forceinline__ int v_lds(int row, int unit /* 4-key unit 0..3 */) {
-    const int half = (unit >> 1) ^ ((row >> 3) & 1);
-    return row * PD_PAGE + (half << 3) + ((unit & 1) << 2);
-}
-
+// The ring's global -> LDS copies are ordered by hand: wait_vmcnt<N> (own
+// copies), then barrier_lds (every wave's copies visible, every wave done
+// with the slot about to be refilled). The LDS destination is passed to the
+// copy as a plain 32-bit address, and the barrier as its own instruction, so
+// that the compiler adds no wait of its own for copies still in flight into
+// other ring slots (it cannot tell the slots apart and would wait for all).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// max over the four lanes l, l^16, l^32, l^48 (one query column of a 16x16
+// MFMA tile): the gfx950 row-swap permutes exchange rows 0<->1, 2<->3 and
+// halves 0<->1 without going through LDS
+__device__ __forceinline__ float col_max(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// LDS address of a pointer into a __shared__ array, as a plain (wave-uniform)
+// 32-bit offset
+__device__ __forceinline__ unsigned lds_addr(void* p) {
+    return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)p);
+}
+
+// One workgroup: reads cu_out / seq_lens of every request, validates them,
+// picks the split length and writes the per-request split counts and the
+// unit records {r, s, ns, row0, row1, kb, ke, 0}.
+__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
+    __shared__ long long s_sum[16];
+    __shared__ int s_max[16];
+    __shared__ int s_cnt[16];
+    const int r = threadIdx.x, lane = r & 63, w = r >> 6;
+    int seq = 0, row0 = 0, row1 = 0;
+    if (r < a.C) {
+        row0 = a.cu_out[r];
+        row1 = a.cu_out[r + 1];
+        seq = a.seq_lens[r];
+        const bool ok = row0 >= 0 && row1 <= a.T && row1 >= row0 && seq >= 1 &&
+                        seq <= a.max_blocks * PD_PAGE;
+        if (!ok) flag(a.status, PD_STATUS_BAD_ROW);
+        if (!ok || row1 == row0) seq = 0;   // no work
+    }
+    long long sv = seq;
+    int mv = seq;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sv += __shfl_xor(sv, o, kWave);
+        mv = max(mv, __shfl_xor(mv, o, kWave));
+    }
+    if (lane == 0) {
+        s_sum[w] = sv;
+        s_max[w] = mv;
+    }
+    __syncthreads();
+    long long total = 0;
+    int mx = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        total += s_sum[i];
+        mx = max(mx, s_max[i]);
+    }
+    const long long tw = a.sp.target_wg;
+    long long sl = (total * a.Hkv + tw - 1) / tw;
+    sl = max(sl, (long long)a.sp.min_split);
+    sl = max(sl, (long long)((mx + a.sp.scap - 1) / a.sp.scap));
+    sl = (sl + PD_PAGE - 1) / PD_PAGE * PD_PAGE;
+    const int split_len = (int)min(sl, (long long)kMaxSplitKeys);
+    int ns = seq > 0 ? (seq + split_len - 1) / split_len : 0;
+    if (ns > a.sp.scap) {   // excluded by the host's choice of scap; never write past it
+        flag(a.status, PD_STATUS_BAD_ROW);
+        ns = 0;
+    }
+    // exclusive prefix of ns over the block
+    int incl = ns;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_cnt[w] = incl;
+    __syncthreads();
+    int before = 0, units = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        before += i < w ? s_cnt[i] : 0;
+        units += s_cnt[i];
+    }
+    const int first = before + incl - ns;
+    if (r < a.C) {
+        a.plan[kPlanNs + r] = ns;
+        for (int s = 0; s < ns; ++s) {
+            const int u = first + s;
+            if (u >= a.sp.max_units) {   // excluded by the host's bound on units
+                flag(a.status, PD_STATUS_BAD_ROW);
+                break;
+            }
+            const int kb = s * split_len;
+            const int ke = min(seq, kb + split_len);
+            int4* rec = reinterpret_cast<int4*>(a.plan + kPlanUnits + (size_t)u * kPlanRec);
+            rec[0] = make_int4(r, s, ns, row0);
+            rec[1] = make_int4(row1, kb, ke, 0);
+        }
+    }
+    if (r == 0) {
+        a.plan[0] = min(units, a.sp.max_units);
+        a.plan[1] = split_len;
+    }
 }
 
 template <int DH>
@@ -101,98 +211,121 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
     constexpr int OT = DH / 16;  // 16-dim output tiles
     constexpr int TPW = Cf::TPW, NW = Cf::NW, NT = 64 * NW, CH = Cf::CH, NST = Cf::NST;
     __shared__ __align__(16) uint16_t kv[NST][CH][2][Cf::PE];   // [stage][page][K, V^T]
-    __shared__ int btc[kBtMax];
+    __shared__ int btc[kBtMax + Cf::CH];
     __shared__ int pv[NST][CH];
 
-    const int r = blockIdx.z, g = blockIdx.y, s = blockIdx.x;
+    const int g = blockIdx.x % a.Hkv, u = blockIdx.x / a.Hkv;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int r16 = lane & 15, g4 = lane >> 4;
 
-    const int row0 = a.cu_out[r], row1 = a.cu_out[r + 1];
-    const int seq = a.seq_lens[r];
-    if (row0 < 0 || row1 > a.T || row1 < row0 || seq < 1 || seq > a.max_blocks * PD_PAGE) {
-        if (s == 0 && g == 0 && tid == 0) flag(a.status, PD_STATUS_BAD_ROW);
-        return;
-    }
-    const int ns = num_splits(seq, a.nsmax, a.min_split);
-    if (s >= ns) return;
-    const int sl = split_len(seq, ns);
-    const int kb = s * sl;
-    const int ke = min(seq, kb + sl);
-    int npages = ke > kb ? (ke - kb + PD_PAGE - 1) / PD_PAGE : 0;
-    if (npages > kBtMax) {  // the host sizes splits below this; never read past the cache
-        if (tid == 0) flag(a.status, PD_STATUS_BAD_ROW);
-        npages = 0;
-    }
+    const int nunits = a.plan[0];
+    const int4* recp = reinterpret_cast<const int4*>(a.plan + kPlanUnits + (size_t)u * kPlanRec);
+    const int4 ra = recp[0], rb = recp[1];   // in bounds for every u < max_units
+    if (u >= nunits) return;
+    const int r = ra.x, s = ra.y, ns = ra.z, row0 = ra.w;
+    const int row1 = rb.x, kb = rb.y, ke = rb.z;
+    const int npages = (ke - kb + PD_PAGE - 1) / PD_PAGE;   // 1 .. kBtMax
     const int nchunks = (npages + CH - 1) / CH;
     const int G = a.Hq / a.Hkv;
     const int nq = (row1 - row0) * G;
-    const int32_t* bt = a.block_table + (size_t)r * a.max_blocks + kb / PD_PAGE;
-    for (int i = tid; i < npages; i += NT) btc[i] = bt[i];
-    __syncthreads();
+    const float scale = a.scale_log2, inv_scale = 1.0f / a.scale_log2;
 
-    // global -> LDS for chunk c into ring slot `slot`: every wave issues exactly
-    // Cf::L 1 KB loads (pages past the split or with a bad block-table entry
-    // read page 0 of the pool and are marked invalid), so vmcnt counts agree
-    auto issue = [&](int c, int slot) {
-#pragma unroll
-        for (int q = 0; q < Cf::L; ++q) {
-            const int inst = wave + NW * q;
-            const int p = inst / Cf::LPP, part = inst % Cf::LPP;
-            const int pg = c * CH + p;
-            const int blk = pg < npages ? btc[pg] : -1;
-            const bool ok = blk >= 0 && blk < a.num_blocks;
-            const size_t pbase = ((size_t)(ok ? blk : 0) * a.Hkv + g) * Cf::PE;
-            const uint16_t* src;
-            uint16_t* dst;
-            if (part < Cf::LPP / 2) {           // K: rows of 64 / DH*2/16 keys per 1 KB block
-                constexpr int KPB = 512 / DH;   // keys per block
-                const int key = KPB * part + lane / (DH / 8);
-                const int chunk = lane % (DH / 8);
-                const int sw = DH == 64 ? ((key & 7) ^ (key >> 3)) : key;
-                src = a.kplane + pbase + key * DH + ((chunk ^ sw) << 3);
-                dst = &kv[slot][p][0][part * 512];
-            } else {                            // V^T: 32 dim rows of 16 keys per 1 KB block
-                const int b = part - Cf::LPP / 2;
-                const int row = 32 * b + lane / 2;
-                const int half = (lane & 1) ^ ((row >> 3) & 1);
-                src = a.vplane + pbase + row * PD_PAGE + (half << 3);
-                dst = &kv[slot][p][1][b * 512];
-            }
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-        }
-        if (tid < CH) {
-            const int pg = c * CH + tid;
-            const int blk = pg < npages ? btc[pg] : -1;
-            const int ok = blk >= 0 && blk < a.num_blocks;
-            if (pg < npages && !ok) flag(a.status, PD_STATUS_BAD_PAGE);
-            pv[slot][tid] = ok;
-        }
-    };
-
-    for (int qbase = 0; qbase < nq; qbase += NW * TPW * 16) {
-        const bool wave_has = qbase + wave * 16 < nq;   // wave-uniform
-        bf16x8 qv[TPW][KB];
-        int qpos[TPW], qrow[TPW], qh[TPW];
-        bool qok[TPW];
-        f32x4 o[TPW][OT];
-        float mrun[TPW], lrun[TPW];
+    bf16x8 qv[TPW][KB];
+    int qrow[TPW], qh[TPW], lim[TPW];
+    bool qok[TPW], qrej[TPW];
+    auto load_q = [&](int qbase) {
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const int qi = qbase + (wave + NW * tt) * 16 + r16;
             qok[tt] = qi < nq;
             qrow[tt] = row0 + (qok[tt] ? qi / G : 0);
             qh[tt] = g * G + (qok[tt] ? qi % G : 0);
-            qpos[tt] = (qok[tt] && !a.is_rejected[qrow[tt]]) ? a.positions[qrow[tt]] : -1;
+            // row0 <= qrow < row1 <= T: both loads are in bounds for every lane
+            const bool rej = a.is_rejected[qrow[tt]] != 0;
+            const int pos = a.positions[qrow[tt]];
+            qrej[tt] = !qok[tt] || rej;
+            // keys this query may see: t <= lim (rejected / padding queries: no limit, not used)
+            lim[tt] = qrej[tt] ? 0x7fffffff : min(ke - 1, pos);
             const uint16_t* qp = a.q + ((size_t)qrow[tt] * a.Hq + qh[tt]) * DH;
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk)
                 qv[tt][kk] = qok[tt] ? ld_bf16x8(qp + 32 * kk + 8 * g4) : zero_bf16x8();
+        }
+    };
+    load_q(0);
+    // block-table entries of the split, padded with -1 to whole chunks
+    const int32_t* bt = a.block_table + (size_t)r * a.max_blocks + kb / PD_PAGE;
+    for (int i = tid; i < nchunks * CH; i += NT) btc[i] = i < npages ? bt[i] : -1;
+    __syncthreads();
+
+    // Load assignment: the wave's qd-th 1 KB load of a chunk is block
+    // qd*NW + wave of the chunk's CH*LPP blocks, i.e. page qd*NW/LPP (known at
+    // compile time) and part (qd*NW) % LPP + wave of that page (wave-uniform).
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint16_t* zp = g_zero_page;
+    int loff[Cf::L];   // per-lane source offset (elements) inside the page
+#pragma unroll
+    for (int qd = 0; qd < Cf::L; ++qd) {
+        const int part = (qd * NW) % Cf::LPP + wv;
+        if (part < Cf::LPP / 2) {               // K: 512 / DH keys per 1 KB block
+            const int key = (512 / DH) * part + lane / (DH / 8);
+            loff[qd] = key * DH + (((lane % (DH / 8)) ^ key_sw(key)) << 3);
+        } else {                                // V^T: 32 dim rows of 16 keys per 1 KB block
+            const int row = 32 * (part - Cf::LPP / 2) + lane / 2;
+            loff[qd] = row * PD_PAGE + (v_half(row, lane & 1) << 3);
+        }
+    }
+    // global -> LDS for chunk c into ring slot `slot`: every wave issues exactly
+    // Cf::L 1 KB loads (pages past the split or with a bad block-table entry
+    // read the zero page and are marked invalid), so vmcnt counts agree
+    auto issue = [&](int c, int slot) {
+#pragma unroll
+        for (int qd = 0; qd < Cf::L; ++qd) {
+            const int p = qd * NW / Cf::LPP;
+            const int part = (qd * NW) % Cf::LPP + wv;
+            const int blk = __builtin_amdgcn_readfirstlane(btc[c * CH + p]);
+            const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
+            const bool isk = part < Cf::LPP / 2;
+            const uint16_t* base =
+                ok ? (isk ? a.kplane : a.vplane) + ((size_t)blk * a.Hkv + g) * Cf::PE : zp;
+            uint16_t* dst = &kv[slot][p][isk ? 0 : 1][(isk ? part : part - Cf::LPP / 2) * 512];
+            __builtin_amdgcn_global_load_lds((void*)(base + loff[qd]),
+                                             (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr(dst),
+                                             16, 0, 0);
+        }
+        if (tid < CH) {
+            const int pg = c * CH + tid;
+            const int blk = btc[pg];
+            const int ok = (unsigned)blk < (unsigned)a.num_blocks;
+            if (pg < npages && !ok) flag(a.status, PD_STATUS_BAD_PAGE);
+            pv[slot][tid] = ok;
+        }
+    };
+
+    // fragment read offsets (elements) inside a staged page pair
+    const int kpage = r16 >> 3;                              // A-operand row -> page of the pair
+    const int key0 = (r16 & 3) | ((r16 & 4) << 1);           // keys 0-3, 8-11 (+4 for the second MFMA)
+    const int ksw = r16 & 7;                                 // key_sw(key0) == key_sw(key0 + 4)
+    const int vpage = g4 >> 1;                               // lane group -> page of its 8 keys
+    const int voff = r16 * PD_PAGE + (v_half(r16, g4 & 1) << 3);
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+    for (int qbase = 0; qbase < nq; qbase += NW * TPW * 16) {
+        if (qbase > 0) load_q(qbase);
+        const bool wave_has = qbase + wave * 16 < nq;   // wave-uniform
+        f32x4 o[TPW][OT], lacc[TPW];
+        float mrun[TPW], mb[TPW], thr[TPW];
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
             for (int j = 0; j < OT; ++j) o[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             mrun[tt] = kNegInf;
-            lrun[tt] = 0.f;
+            mb[tt] = 0.f;
+            thr[tt] = kNegInf;
+            lacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         wait_vmcnt<0>();   // query fragments in registers before the ring starts counting
 
@@ -203,85 +336,67 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
             if (later >= 2) wait_vmcnt<2 * Cf::L>();
             else if (later == 1) wait_vmcnt<Cf::L>();
             else wait_vmcnt<0>();
-            __syncthreads();
+            barrier_lds();
             if (c + NST - 1 < nchunks) issue(c + NST - 1, (c + NST - 1) % NST);
             const int b = c % NST;
             if (!wave_has) continue;
-            // pages in pairs: 32 keys per softmax step and per PV MFMA
+#pragma unroll
             for (int pi = 0; pi < CH; pi += 2) {
                 const int p0 = kb + (c * CH + pi) * PD_PAGE;
                 if (p0 >= ke) break;
-                const bool okA = pv[b][pi] != 0;
-                const bool okB = p0 + PD_PAGE < ke && pv[b][pi + 1] != 0;
-                const uint16_t* KA = kv[b][pi][0];
-                const uint16_t* KBp = kv[b][pi + 1][0];
-                const uint16_t* VA = kv[b][pi][1];
-                const uint16_t* VBp = kv[b][pi + 1][1];
-                bf16x8 kA[KB], kB[KB], vab[OT];
+                const bool pgok = pv[b][pi + vpage] != 0;   // this lane group's page
+                const uint16_t* Kp = kv[b][pi + kpage][0];
+                const uint16_t* Vp = kv[b][pi + vpage][1];
+                bf16x8 k0[KB], k1[KB], vf[OT];
 #pragma unroll
                 for (int kk = 0; kk < KB; ++kk) {
-                    kA[kk] = *reinterpret_cast<const bf16x8*>(KA + k_lds<DH>(r16, 4 * kk + g4));
-                    kB[kk] = *reinterpret_cast<const bf16x8*>(KBp + k_lds<DH>(r16, 4 * kk + g4));
+                    const int ch = ((4 * kk + g4) ^ ksw) << 3;
+                    k0[kk] = *reinterpret_cast<const bf16x8*>(Kp + key0 * DH + ch);
+                    k1[kk] = *reinterpret_cast<const bf16x8*>(Kp + (key0 + 4) * DH + ch);
                 }
-                // V^T fragments of both pages: k slots 0-3 = page A keys 4*g4.., 4-7 = page B keys 4*g4..
 #pragma unroll
-                for (int j = 0; j < OT; ++j) {
-                    uint2 va = *reinterpret_cast<const uint2*>(VA + v_lds(16 * j + r16, g4));
-                    uint2 vb = *reinterpret_cast<const uint2*>(VBp + v_lds(16 * j + r16, g4));
-                    if (!okA) va = make_uint2(0, 0);
-                    if (!okB) vb = make_uint2(0, 0);
-                    vab[j] = __builtin_bit_cast(bf16x8, make_uint4(va.x, va.y, vb.x, vb.y));
-                }
+                for (int j = 0; j < OT; ++j)
+                    vf[j] = *reinterpret_cast<const bf16x8*>(Vp + 16 * PD_PAGE * j + voff);
+                const int t0 = p0 + 8 * g4;   // keys t0 .. t0+7 in this lane's scores
 #pragma unroll
                 for (int tt = 0; tt < TPW; ++tt) {
-                    f32x4 sA = f32x4{0.f, 0.f, 0.f, 0.f}, sB = f32x4{0.f, 0.f, 0.f, 0.f};
+                    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kk = 0; kk < KB; ++kk) {
-                        sA = mfma_16x16x32(kA[kk], qv[tt][kk], sA);
-                        sB = mfma_16x16x32(kB[kk], qv[tt][kk], sB);
+                        s0 = mfma_16x16x32(k0[kk], qv[tt][kk], s0);
+                        s1 = mfma_16x16x32(k1[kk], qv[tt][kk], s1);
                     }
-                    // raw scores of keys p0+4*g4+i (page A) and p0+16+4*g4+i (page B)
-                    float sc[8] = {sA[0], sA[1], sA[2], sA[3], sB[0], sB[1], sB[2], sB[3]};
-                    // keys this query may see: t <= lim (invalid queries: no limit, don't care)
-                    const int lim = qok[tt] && qpos[tt] >= 0 ? min(ke - 1, qpos[tt]) : 0x7fffffff;
-                    if (__any(p0 + 2 * PD_PAGE - 1 > lim || !okA || !okB)) {
+                    float sc[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                    const int vis = lim[tt] - t0;   // key t0+e is visible iff e <= vis
+                    if (__any(!pgok || vis < 7)) {
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const int t = p0 + (i >> 2) * PD_PAGE + 4 * g4 + (i & 3);
-                            const bool ok = (i < 4 ? okA : okB) && t <= lim;
-                            sc[i] = ok ? sc[i] : kNegInf;
-                        }
+                        for (int e = 0; e < 8; ++e) sc[e] = (pgok && e <= vis) ? sc[e] : kNegInf;
                     }
-                    float mx = sc[0];
-#pragma unroll
-                    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-                    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-                    const float mnew = mx * a.scale_log2;   // -inf stays -inf
-                    const bool raise = mnew > mrun[tt] + kRescale;
-                    if (__any(raise)) {
+                    const float lm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+                    if (__any(lm > thr[tt])) {
+                        // the column max (4 lane groups), raised only by more than kRescale
+                        const float mnew = col_max(lm) * scale;   // -inf stays -inf
+                        const bool raise = mnew > mrun[tt] + kRescale;
                         const float alpha = raise ? __builtin_amdgcn_exp2f(mrun[tt] - mnew) : 1.0f;
-                        if (raise) mrun[tt] = mnew;
-                        lrun[tt] *= alpha;
+                        if (raise) {
+                            mrun[tt] = mnew;
+                            mb[tt] = -mnew;
+                            thr[tt] = (mnew + kRescale) * inv_scale;
+                        }
+                        lacc[tt] = lacc[tt] * alpha;
 #pragma unroll
                         for (int j = 0; j < OT; ++j) o[tt][j] = o[tt][j] * alpha;
                     }
-                    const float muse = (mrun[tt] == kNegInf) ? 0.f : mrun[tt];
-                    float p[8], ls = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        // raw v_exp_f32: weights below 2^-126 flush to zero
-                        p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -muse));
-                        ls += p[i];
-                    }
-                    ls += __shfl_xor(ls, 16, kWave);
-                    ls += __shfl_xor(ls, 32, kWave);
-                    lrun[tt] += ls;
                     bf16x8 pb;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) pb[i] = (__bf16)p[i];
+                    for (int e = 0; e < 8; ++e)   // raw v_exp_f32: weights below 2^-126 flush to zero
+                        pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[e], scale, mb[tt]));
 #pragma unroll
-                    for (int j = 0; j < OT; ++j) o[tt][j] = mfma_16x16x32(vab[j], pb, o[tt][j]);
+                    for (int j = 0; j < OT; ++j) o[tt][j] = mfma_16x16x32(vf[j], pb, o[tt][j]);
+                    // running sums of the same rounded weights: an all-ones A operand makes
+                    // every row of the product the column sum over the pair's 32 keys
+                    lacc[tt] = mfma_16x16x32(ones, pb, lacc[tt]);
                 }
             }
         }
@@ -289,14 +404,24 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
 
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
+            const float l = lacc[tt][0];
             if (!qok[tt]) continue;
-            const size_t base = ((size_t)s * a.T + qrow[tt]) * a.Hq + qh[tt];
+            if (ns == 1) {
+                // the only split: normalized bf16 output (rejected rows: zeros)
+                const float inv = (!qrej[tt] && l > 0.f) ? 1.0f / l : 0.f;
+                uint16_t* op = a.out + ((size_t)qrow[tt] * a.Hq + qh[tt]) * DH + 4 * g4;
 #pragma unroll
-            for (int j = 0; j < OT; ++j)
-                *reinterpret_cast<f32x4*>(a.part_o + base * DH + 16 * j + 4 * g4) = o[tt][j];
-            if (g4 == 0) {
-                a.part_ml[base * 2] = mrun[tt];
-                a.part_ml[base * 2 + 1] = lrun[tt];
+                for (int j = 0; j < OT; ++j) {
+                    const uint32_t lo = f2bf(o[tt][j][0] * inv) | (uint32_t(f2bf(o[tt][j][1] * inv)) << 16);
+                    const uint32_t hi = f2bf(o[tt][j][2] * inv) | (uint32_t(f2bf(o[tt][j][3] * inv)) << 16);
+                    *reinterpret_cast<uint2*>(op + 16 * j) = make_uint2(lo, hi);
+                }
+            } else {
+                const size_t base = ((size_t)s * a.T + qrow[tt]) * a.Hq + qh[tt];
+#pragma unroll
+                for (int j = 0; j < OT; ++j)
+                    *reinterpret_cast<f32x4*>(a.part_o + base * DH + 16 * j + 4 * g4) = o[tt][j];
+                if (g4 == 0) *reinterpret_cast<float2*>(a.part_ml + base * 2) = make_float2(mrun[tt], l);
             }
         }
     }
@@ -304,7 +429,8 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
 
 // out[row][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in
 // order. One wave per (row, q head): the split weights are formed across
-// lanes, then each lane accumulates its dims over the splits.
+// lanes, then each lane accumulates its dims over the splits. Requests with
+// one split were written by the split kernel.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -317,10 +443,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
         if (a.cu_out[mid] <= row) lo = mid; else hi = mid - 1;
     }
     const int r = lo;
-    const int seq = a.seq_lens[r];
-    const bool ok = !a.is_rejected[row] && seq >= 1 && seq <= a.max_blocks * PD_PAGE &&
-                    a.cu_out[r] <= row && row < a.cu_out[r + 1];
-    const int ns = ok ? num_splits(seq, a.nsmax, a.min_split) : 0;  // <= 128
+    const bool inr = a.cu_out[r] <= row && row < a.cu_out[r + 1];
+    const int nsr = a.plan[kPlanNs + r];
+    if (inr && nsr == 1) return;
+    const int ns = (inr && !a.is_rejected[row]) ? min(nsr, kMaxSplits) : 0;
     constexpr int PER = DH / 64;
     const size_t stride = (size_t)a.T * a.Hq;   // between splits, in (row, head) units
     const size_t base = (size_t)row * a.Hq + h;
@@ -338,9 +464,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     float acc[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    // all split loads of a lane are independent: issue them 32 at a time
-#pragma unroll 32
-    for (int sp = 0; sp < ns; ++sp) {
+    // all split loads of a lane are independent: issue them in groups
+    int sp = 0;
+    for (; sp + 8 <= ns; sp += 8) {
+        float v[8][PER];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float* po = a.part_o + ((sp + k) * stride + base) * DH;
+#pragma unroll
+            for (int i = 0; i < PER; ++i) v[k][i] = po[lane + 64 * i];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float w = __shfl(sp + k < 64 ? w0 : w1, (sp + k) & 63, kWave);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) acc[i] += w * v[k][i];
+        }
+    }
+    for (; sp < ns; ++sp) {
         const float w = __shfl(sp < 64 ? w0 : w1, sp & 63, kWave);
         const float* po = a.part_o + (sp * stride + base) * DH;
 #pragma unroll
@@ -356,10 +497,8 @@ template <int DH>
 int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     constexpr int NW = AttnCfg<DH>::NW;
     if (e0) (void)hipEventRecord(e0, s);
-    // splits a request can have: bounded by nsmax and by the block table's reach
-    const int reach = (a.max_blocks * PD_PAGE + a.min_split - 1) / a.min_split;
-    const int gx = reach < a.nsmax ? reach : a.nsmax;
-    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3(gx, a.Hkv, a.C), dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3((unsigned)a.sp.max_units * a.Hkv), dim3(64 * NW), 0,
+                       s, a);
     if (e1) (void)hipEventRecord(e1, s);
     if (hipGetLastError() != hipSuccess) return PD_EHIP;
     hipLaunchKernelGGL(attn_merge_kernel<DH>, dim3((a.T * a.Hq + 3) / 4), dim3(256), 0, s, a);
@@ -367,6 +506,31 @@ int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
 }
 
 }  // namespace
+
+AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks) {
+    AttnSplit p;
+    p.min_split = 128;
+    p.target_wg = 2048;
+    const long long reach = (long long)max_blocks * PD_PAGE;
+    // a split never exceeds the LDS block-table cache: enough workgroups for
+    // the longest batch the block table can describe
+    const long long need = ((long long)C * reach * Hkv + kMaxSplitKeys - 1) / kMaxSplitKeys;
+    if (need > p.target_wg) p.target_wg = (int)std::min<long long>(need, 1LL << 30);
+    // partial planes: about 1 GiB at most, but enough splits that the longest
+    // request fits kMaxSplitKeys per split
+    const long long plane = (long long)T * Hq * (dh + 2) * 4;
+    long long scap = plane > 0 ? (1LL << 30) / plane : kMaxSplits;
+    scap = std::max(scap, (reach + kMaxSplitKeys - 1) / kMaxSplitKeys);
+    p.scap = (int)std::max(1LL, std::min(scap, (long long)kMaxSplits));
+    p.max_units = (p.target_wg + Hkv - 1) / Hkv + C;
+    return p;
+}
+
+int launch_attn_plan(const AttnArgs& a, hipStream_t s) {
+    if (a.C <= 0) return PD_OK;
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
 
 int launch_attention(int dh, const AttnArgs& a, hipStream_t s, hipEvent_t split_begin,
                      hipEvent_t split_end) {

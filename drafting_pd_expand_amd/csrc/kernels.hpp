@@ -64,6 +64,27 @@ int launch_argmax_reduce(const float* amax_v, const int* amax_i, int M, int ntil
                          int32_t* status, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
+// Split-KV plan, computed on the device once per forward from seq_lens:
+// split_len = max(min_split, ceil(sum_r seq_r * Hkv / target_wg),
+// ceil(max_r seq_r / scap)) rounded up to a page; request r gets
+// ns_r = ceil(seq_r / split_len) units of work (one workgroup per unit and kv
+// head). The host sizes everything from bounds it knows without a sync.
+struct AttnSplit {
+    int min_split;   // keys per split at least (multiple of 16)
+    int target_wg;   // workgroups the split length aims at
+    int scap;        // splits per request at most (partial planes allocated)
+    int max_units;   // capacity of the unit list = grid x of the split kernel
+};
+AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks);
+// int32 words of the plan: [units, split_len, -, -, ns[PD_MAX_C],
+// unit records[max_units][kPlanRec]]
+constexpr int kPlanNs = 4;
+constexpr int kPlanUnits = 4 + PD_MAX_C;
+constexpr int kPlanRec = 8;
+inline size_t attn_plan_ints(const AttnSplit& p) {
+    return (size_t)kPlanUnits + (size_t)p.max_units * kPlanRec;
+}
+
 struct AttnArgs {
     const uint16_t* q;            // bf16 [T][Hq][dh] (rotated)
     const uint16_t* kplane;       // this layer's K plane [num_blocks][Hkv][16][dh]
@@ -74,14 +95,17 @@ struct AttnArgs {
     const int32_t* seq_lens;      // [C]
     const int32_t* block_table;   // [C][max_blocks]
     int C, T, Hq, Hkv, max_blocks, num_blocks;
-    int nsmax, min_split;         // split-KV: ns_r = min(nsmax, ceil(seq_r / min_split))
+    AttnSplit sp;
+    int32_t* plan;                // attn_plan_ints(sp) words, written by launch_attn_plan
     float scale_log2;             // log2(e) / sqrt(dh)
-    float* part_o;                // [nsmax][T][Hq][dh]
-    float* part_ml;               // [nsmax][T][Hq][2]  (running max in log2 units, sum)
-    uint16_t* out;                // bf16 [T][Hq][dh] (merge output)
+    float* part_o;                // [scap][T][Hq][dh]
+    float* part_ml;               // [scap][T][Hq][2]  (running max in log2 units, sum)
+    uint16_t* out;                // bf16 [T][Hq][dh]
     int32_t* status;
 };
 
+// Once per forward (the plan only depends on cu_out / seq_lens).
+int launch_attn_plan(const AttnArgs& a, hipStream_t s);
 int launch_attention(int dh, const AttnArgs& a, hipStream_t s, hipEvent_t split_begin,
                      hipEvent_t split_end);
 

@@ -44,6 +44,7 @@ extern "C" {
 #define PD_MAX_K      16    /* draft depth; the blog's drafter predicts up to 10 tokens */
 #define PD_MAX_LAYERS 16
 #define PD_PAGE       16    /* KV page size (tokens) the forward's cache layout uses */
+#define PD_MAX_BLOCKS 65536 /* block-table columns pd_draft_forward accepts (1,048,576 keys) */
 
 /* Device status bits (ORed into a caller- or handle-owned int32). */
 #define PD_STATUS_BAD_COUNTS   1  /* n_r < 1, rho_r outside [0, n_r), or sum(n_r) != T_in   */
@@ -176,7 +177,7 @@ typedef struct pd_handle pd_handle;
  *              Hq % Hkv == 0, dh in {64, 128}, 1 <= N <= PD_MAX_LAYERS,
  *              every weight pointer non-NULL.
  *   dims       [host] the same sizes given to pd_expand_batch; block_size must
- *              be PD_PAGE.
+ *              be PD_PAGE and max_blocks <= PD_MAX_BLOCKS.
  *   batch      [host] struct of [dev] pointers written by pd_expand_batch
  *              (status may be NULL).
  *   block_table[dev] [C][max_blocks].
