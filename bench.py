@@ -246,7 +246,7 @@ def main():
                    "T_in": b["T_in"], "T_out": b["T_in"] + w.C * (w.K - 1)},
         "drafted_tok_per_s": steps_s * R,
         "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "gemm_skinny_kernel<ARGMAX> (LM head + fused argmax)",
+        "roofline": {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload)},
         "cpu_baseline": cpu,

@@ -4,29 +4,25 @@
 // [Paper] = "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training" summary
 // page, sec. 2 architecture; [arXiv] = its ScienceStack page, Figure 2) see
 // few rows per step: the draft batch has v_r + K - 1 computed rows per
-// request and the LM head C*K rows. At low concurrency every projection is a
-// stream of its weight matrix, so this kernel is built to stream W at HBM
-// speed:
+// request and the LM head C*K rows. Two kernels:
 //
-//  * a wave owns RG groups of 16 W rows (the A operand of
-//    v_mfma_f32_16x16x32_bf16) and up to 64 X rows (the B operand), so each
-//    lane ends with 4 consecutive output columns of one row;
-//  * in every 128-wide K step, lane group g (lanes 16g..16g+15) takes
-//    k = 32j + 8g .. +7 for j = 0..3: each load instruction reads 64
-//    contiguous bytes of each of the 16 rows, and 4 such loads per row group
-//    are in flight; the next step's W loads are issued before the current
-//    step's MFMAs (register double buffering);
-//  * a workgroup has WK waves that split its K range; their partial tiles are
-//    summed through LDS inside the workgroup;
-//  * projections with few output columns are further split over S
-//    workgroups along K. Those splits never meet inside this kernel: each
-//    writes an fp32 partial plane, and the row kernel that consumes the
-//    projection (layer-0 input, RoPE + KV write, residual + RMSNorm) sums the
-//    planes in split order. No workgroup ever waits on another, so no
-//    device-wide fence is needed, and the result is deterministic.
-//  * epilogues: fp32 partial plane, SwiGLU on a pair of matrices (gate and up
-//    rows streamed side by side, one bf16 rounding), and LM-head max/argmax per
-//    column tile (lowest index on ties) with optional fp32 logits.
+//  * M <= 64 rows (low concurrency): every projection is a stream of its
+//    weight matrix. A persistent ring kernel (one workgroup per CU) copies W
+//    and the matching X columns straight from HBM into a ring of LDS stages
+//    and runs v_mfma_f32_16x16x32_bf16 on them (W rows are the A operand, X
+//    rows the B operand, so a lane ends with 4 consecutive output columns of
+//    one row);
+//  * M > 64 rows: 128 x 128 output tiles staged through LDS.
+//
+// Projections with few output columns are split over workgroups along K.
+// Those splits never meet inside the GEMM: each writes an fp32 partial plane,
+// and the row kernel that consumes the projection (layer-0 input, RoPE + KV
+// write, residual + RMSNorm) sums the planes in split order. No workgroup ever
+// waits on another, so no device-wide fence is needed, and the result is
+// deterministic. Epilogues: fp32 partial plane, SwiGLU on a pair of matrices
+// (gate and up rows streamed side by side, one bf16 rounding), and LM-head
+// max/argmax per column group (lowest index on ties) with optional fp32
+// logits.
 #include <float.h>
 #include <limits.h>
 
@@ -37,8 +33,6 @@ namespace pd {
 
 namespace {
 
-constexpr int kU = 4;             // 16-byte loads per lane per row group per K step
-constexpr int kKStep = 32 * kU;   // 128 reduction elements per K step
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -46,173 +40,237 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
     if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
 }
 
-template <int MT, int RG, int WK, int EPI>
-__global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmArgs a) {
-    constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    constexpr int NM = DUAL ? 2 : 1;  // matrices streamed side by side
-    const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
-    const int r16 = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16 * RG;
-    const int m0 = blockIdx.z * 16 * MT;
+// ---------------------------------------------------------------------------
+// Persistent ring kernel for few rows (M <= 64): the weight stream goes
+// straight from HBM into LDS (global_load_lds, 16 B per lane) through a ring
+// of NST stages of 128 reduction elements, so each CU keeps ~100 KB of
+// weights in flight with a single workgroup and no staging registers. A
+// stage holds the workgroup's W rows (16 output columns per wave, one row
+// group per matrix) and the matching X columns of all M rows; the waves read
+// their MFMA fragments from it (W is the A operand, X the B operand, as in the
+// streaming kernel, so the epilogues are the same). Rows are stored with
+// their 16-byte chunks XOR-permuted by (row & 7): the 8 lanes of one 16-byte
+// fragment read hit 8 different bank groups. Workgroups are persistent: each
+// walks the work items (column tile, K split) blockIdx.x, +gridDim.x, ... and
+// the ring runs on across item boundaries, so a CU never waits for a new
+// workgroup's first loads.
+constexpr int kRS = 128;   // reduction elements per ring stage (256 B of each row)
 
-    // K range of this wave: part (split * WK + wave) of S*WK equal parts, in K steps
-    const int ksteps = (a.K + kKStep - 1) / kKStep;
-    const int parts = a.splits * WK;
-    const int per = (ksteps + parts - 1) / parts;
-    const int part = blockIdx.y * WK + wk;
-    const int kb = min(a.K, part * per * kKStep);
-    const int ke = min(a.K, (part + 1) * per * kKStep);
+// 16 zero bytes: the source of out-of-range chunks (zero-initialised at load)
+__device__ __align__(16) uint16_t g_gemm_zero[8];
 
-    f32x4 acc[NM][MT][RG];
-#pragma unroll
-    for (int q = 0; q < NM; ++q)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < RG; ++r) acc[q][t][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+template <int WN, int NM, int MT>
+struct RingCfg {
+    static constexpr int NT = 64 * WN;
+    static constexpr int WR = 16 * WN * NM;   // W rows per stage
+    static constexpr int XR = 16 * MT;        // X rows per stage
+    static constexpr int WL = WR * 16 / NT;   // 16-byte W loads per thread per stage
+    static constexpr int XL = XR * 16 / NT;   // 16-byte X loads per thread per stage
+    static constexpr int L = WL + XL;
+    static constexpr int SE = (WR + XR) * kRS;   // elements per stage
+    static constexpr int NST = MT == 1 ? 6 : (MT == 2 ? 5 : 4);
+    static_assert(WL * NT == WR * 16 && XL * NT == XR * 16, "whole loads per thread");
+};
 
-    // operand rows of this lane
-    const uint16_t* wp[NM][RG];
-    bool rok[RG];
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-        rok[r] = n0 + 16 * r < a.N;
-        const size_t row = (size_t)(rok[r] ? n0 + 16 * r + r16 : 0) * a.K;
-        wp[0][r] = a.W + row;
-        if constexpr (DUAL) wp[NM - 1][r] = a.W2 + row;
+template <int N>
+__device__ __forceinline__ void ring_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `later` stages of L loads each are still in flight
+template <int L, int MAXN>
+__device__ __forceinline__ void ring_wait_later(int later) {
+    if constexpr (MAXN == 0) {
+        ring_wait<0>();
+    } else {
+        if (later >= MAXN) ring_wait<L * MAXN>();
+        else ring_wait_later<L, MAXN - 1>(later);
     }
-    const uint16_t* xp[MT];
-    bool xok[MT];
+}
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// LDS address of a pointer into a __shared__ array as a wave-uniform 32-bit
+// offset: the copies into the ring are then ordered only by the explicit
+// waits above (the compiler would otherwise wait for all of them at every
+// LDS read, not knowing the ring slots apart)
+__device__ __forceinline__ unsigned ring_lds(void* p) {
+    return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)p);
+}
+
+template <int WN, int NM, int MT, int EPI>
+__global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
+    using Cf = RingCfg<WN, NM, MT>;
+    constexpr int NT = Cf::NT, NST = Cf::NST, L = Cf::L, WL = Cf::WL, XL = Cf::XL;
+    __shared__ __align__(16) uint16_t ring[NST * Cf::SE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = lane >> 4;
+
+    const int ksteps = (a.K + kRS - 1) / kRS;
+    const int per = (ksteps + a.splits - 1) / a.splits;
+    const int ntn = (a.N + 16 * WN - 1) / (16 * WN);   // column tiles
+    const int nitems = ntn * a.splits;
+    const int G = gridDim.x;
+
+    // this thread's fixed share of every stage: W (row within the tile,
+    // chunk) and X (row pointer, chunk)
+    int wrr[WL], wch[WL], wofs[WL];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        const int m = m0 + 16 * t + r16;
-        xok[t] = m < a.M;
+    for (int j = 0; j < WL; ++j) {
+        const int u = tid + NT * j, wr = u >> 4;
+        wrr[j] = wr % (16 * WN);
+        wch[j] = ((u & 15) ^ (wr & 7)) * 8;
+        wofs[j] = wrr[j] * a.K + wch[j];   // element offset from the tile's first row, k = 0
+    }
+    const uint16_t* xp[XL];
+    int xch[XL];
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+        const int u = tid + NT * j, m = u >> 4;
+        xch[j] = ((u & 15) ^ (m & 7)) * 8;
         int row = m;
-        if (xok[t] && a.xrows) {
+        bool ok = m < a.M;
+        if (ok && a.xrows) {
             row = a.xrows[m];
             if (row < 0 || row >= a.xrows_limit) {
-                xok[t] = false;
+                ok = false;
                 flag(a.status, PD_STATUS_BAD_ROW);
             }
         }
-        xp[t] = a.X + (size_t)(xok[t] ? row : 0) * a.ldx;
+        xp[j] = ok ? a.X + (size_t)row * a.ldx : nullptr;
+    }
+    const uint16_t* zp = g_gemm_zero;
+    const unsigned lds0 = ring_lds(ring);
+
+    // stages this workgroup consumes, item by item
+    int total = 0;
+    for (int it = blockIdx.x; it < nitems; it += G) {
+        const int sp = it / ntn;
+        total += max(0, min(ksteps, (sp + 1) * per) - sp * per);
     }
 
-    if (kb < ke) {
-        bf16x8 w[NM][RG][kU];
+    // issue cursor: (item, stage) of the next stage to load
+    int iitem = blockIdx.x, iks = 0, ike = 0;
+    if (iitem < nitems) {
+        const int sp = iitem / ntn;
+        iks = sp * per;
+        ike = min(ksteps, (sp + 1) * per);
+    }
+    auto issue = [&](int slot) {
+        // skip items without stages (not produced by the planner)
+        while (iitem < nitems && iks >= ike) {
+            iitem += G;
+            if (iitem < nitems) {
+                const int sp = iitem / ntn;
+                iks = sp * per;
+                ike = min(ksteps, (sp + 1) * per);
+            }
+        }
+        const int n0 = (iitem % ntn) * 16 * WN;
+        const int k0 = iks * kRS;
+        const unsigned sbase = lds0 + (unsigned)(slot * Cf::SE) * 2u;
+        // whole tile inside N and whole stage inside K: no per-lane bounds
+        const bool inner = n0 + 16 * WN <= a.N && k0 + kRS <= a.K;
 #pragma unroll
-        for (int q = 0; q < NM; ++q)
+        for (int j = 0; j < WL; ++j) {
+            const int q = j * NT / (16 * 16 * WN);   // matrix of this load (compile-time)
+            const uint16_t* tile = (q == 0 ? a.W : a.W2) + (size_t)n0 * a.K + k0;
+            const uint16_t* src;
+            if (inner) {
+                src = tile + wofs[j];
+            } else {
+                const int n = n0 + wrr[j], k = k0 + wch[j];
+                src = (n < a.N && k < a.K) ? tile + wofs[j] : zp;
+            }
+            __builtin_amdgcn_global_load_lds((void*)src,
+                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
+                16, 0, 0);
+        }
 #pragma unroll
-            for (int r = 0; r < RG; ++r)
+        for (int j = 0; j < XL; ++j) {
+            const int k = k0 + xch[j];
+            const uint16_t* src = (xp[j] && (inner || k < a.K)) ? xp[j] + k : zp;
+            __builtin_amdgcn_global_load_lds((void*)src,
+                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(Cf::WR * kRS * 2) +
+                                                                      (unsigned)(wave * 64 + NT * j) * 16u),
+                16, 0, 0);
+        }
+        ++iks;
+    };
+
+    ring_wait<0>();   // row gathers done before the ring starts counting
+    for (int st = 0; st < NST - 1 && st < total; ++st) issue(st);
+
+    int qc = 0;   // stages consumed
+    for (int it = blockIdx.x; it < nitems; it += G) {
+        const int sp = it / ntn;
+        const int kb = sp * per, ke = min(ksteps, (sp + 1) * per);
+        if (kb >= ke) continue;
+        f32x4 acc[MT][NM];
 #pragma unroll
-                for (int j = 0; j < kU; ++j) {
-                    const int k = kb + 32 * j + 8 * g;
-                    w[q][r][j] = (rok[r] && k < ke) ? ld_bf16x8(wp[q][r] + k) : zero_bf16x8();
-                }
-        for (int kk = kb; kk < ke; kk += kKStep) {
-            const bool more = kk + kKStep < ke;
-            bf16x8 nx[NM][RG][kU];
-            if (more) {
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < NM; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = kb; ks < ke; ++ks, ++qc) {
+            // loads of stage qc done (later stages may stay in flight), then every wave's
+            ring_wait_later<L, NST - 2>(min(NST - 2, total - 1 - qc));
+            ring_barrier();
+            if (qc + NST - 1 < total) issue((qc + NST - 1) % NST);
+            const uint16_t* Ws = ring + (qc % NST) * Cf::SE;
+            const uint16_t* Xs = Ws + Cf::WR * kRS;
+#pragma unroll
+            for (int j = 0; j < kRS / 32; ++j) {
+                const int pos = ((4 * j + g4) ^ (r16 & 7)) * 8;
+                bf16x8 wf[NM];
 #pragma unroll
                 for (int q = 0; q < NM; ++q)
+                    wf[q] = *reinterpret_cast<const bf16x8*>(Ws + (q * 16 * WN + 16 * wave + r16) * kRS + pos);
 #pragma unroll
-                    for (int r = 0; r < RG; ++r)
+                for (int t = 0; t < MT; ++t) {
+                    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(Xs + (16 * t + r16) * kRS + pos);
 #pragma unroll
-                        for (int j = 0; j < kU; ++j) {
-                            const int k = kk + kKStep + 32 * j + 8 * g;
-                            nx[q][r][j] = (rok[r] && k < ke) ? ld_bf16x8(wp[q][r] + k) : zero_bf16x8();
-                        }
+                    for (int q = 0; q < NM; ++q) acc[t][q] = mfma_16x16x32(wf[q], xf, acc[t][q]);
+                }
             }
+        }
+
+        // lane holds rows m = 16t + r16 and columns n .. n+3
+        const int n = (it % ntn) * 16 * WN + 16 * wave + 4 * g4;
+        if constexpr (EPI == EPI_ARGMAX) {
+            const int tile = (it % ntn) * WN + wave;   // 16-column group
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-                bf16x8 x[kU];
+                const int m = 16 * t + r16;
+                float bv = -FLT_MAX;
+                int bi = INT_MAX;
+                if (n < a.N) {
 #pragma unroll
-                for (int j = 0; j < kU; ++j) {
-                    const int k = kk + 32 * j + 8 * g;
-                    x[j] = (xok[t] && k < ke) ? ld_bf16x8(xp[t] + k) : zero_bf16x8();
+                    for (int e = 0; e < 4; ++e) better(bv, bi, acc[t][0][e], n + e);
+                    if (a.logits && m < a.M)
+                        *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[t][0];
                 }
 #pragma unroll
-                for (int q = 0; q < NM; ++q)
-#pragma unroll
-                    for (int r = 0; r < RG; ++r)
-#pragma unroll
-                        for (int j = 0; j < kU; ++j) acc[q][t][r] = mfma_16x16x32(w[q][r][j], x[j], acc[q][t][r]);
+                for (int off = 16; off <= 32; off <<= 1) {
+                    const float ov = __shfl_xor(bv, off, kWave);
+                    const int oi = __shfl_xor(bi, off, kWave);
+                    better(bv, bi, ov, oi);
+                }
+                if (g4 == 0 && m < a.M && 16 * tile < a.N) {
+                    a.amax_v[(size_t)m * a.ntiles + tile] = bv;
+                    a.amax_i[(size_t)m * a.ntiles + tile] = bi;
+                }
             }
-            if (more) {
+        } else {
 #pragma unroll
-                for (int q = 0; q < NM; ++q)
-#pragma unroll
-                    for (int r = 0; r < RG; ++r)
-#pragma unroll
-                        for (int j = 0; j < kU; ++j) w[q][r][j] = nx[q][r][j];
-            }
-        }
-    }
-
-    // sum the WK waves' partial tiles through LDS (wave 0 keeps the result)
-    if constexpr (WK > 1) {
-        __shared__ f32x4 red[WK - 1][NM * MT * RG][64];
-        if (wk > 0) {
-#pragma unroll
-            for (int q = 0; q < NM; ++q)
-#pragma unroll
-                for (int t = 0; t < MT; ++t)
-#pragma unroll
-                    for (int r = 0; r < RG; ++r) red[wk - 1][(q * MT + t) * RG + r][lane] = acc[q][t][r];
-        }
-        __syncthreads();
-        if (wk > 0) return;
-        for (int w = 0; w < WK - 1; ++w)
-#pragma unroll
-            for (int q = 0; q < NM; ++q)
-#pragma unroll
-                for (int t = 0; t < MT; ++t)
-#pragma unroll
-                    for (int r = 0; r < RG; ++r) acc[q][t][r] = acc[q][t][r] + red[w][(q * MT + t) * RG + r][lane];
-    }
-
-    // wave 0: lane holds rows m0+16t+r16, columns n0+16r+4g .. +3
-    if constexpr (EPI == EPI_ARGMAX) {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int m = m0 + 16 * t + r16;
-            float bv = -FLT_MAX;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                if (!rok[r]) continue;
-                const int n = n0 + 16 * r + 4 * g;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) better(bv, bi, acc[0][t][r][i], n + i);
-                if (a.logits && m < a.M)
-                    *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[0][t][r];
-            }
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                const float ov = __shfl_xor(bv, off, kWave);
-                const int oi = __shfl_xor(bi, off, kWave);
-                better(bv, bi, ov, oi);
-            }
-            if (g == 0 && m < a.M) {
-                a.amax_v[(size_t)m * a.ntiles + blockIdx.x] = bv;
-                a.amax_i[(size_t)m * a.ntiles + blockIdx.x] = bi;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int m = m0 + 16 * t + r16;
-            if (m >= a.M) continue;
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                if (!rok[r]) continue;
-                const int n = n0 + 16 * r + 4 * g;
+            for (int t = 0; t < MT; ++t) {
+                const int m = 16 * t + r16;
+                if (m >= a.M || n >= a.N) continue;
                 if constexpr (EPI == EPI_PARTIAL) {
-                    *reinterpret_cast<f32x4*>(a.ws + ((size_t)blockIdx.y * a.M + m) * a.N + n) = acc[0][t][r];
-                } else if constexpr (EPI == EPI_SWIGLU) {
+                    *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[t][0];
+                } else {
                     float h[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) h[i] = silu(acc[0][t][r][i]) * acc[NM - 1][t][r][i];
+                    for (int e = 0; e < 4; ++e) h[e] = silu(acc[t][0][e]) * acc[t][NM - 1][e];
                     uint2 pk;
                     pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
                     pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
@@ -223,7 +281,6 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmArgs a) {
     }
 }
 
-// Row groups of W per wave: fewer when more X rows share the registers.
 // ---------------------------------------------------------------------------
 // Tiled kernel for many rows (M > 64): a 128 x 128 output tile per workgroup,
 // K in steps of 64 staged through LDS (double buffered: the next step's
@@ -431,35 +488,23 @@ int launch_tiled(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
-template <int MT, int EPI>
-constexpr int rows_groups() {
-    return EPI == EPI_ARGMAX ? (MT == 1 ? 4 : (MT == 2 ? 2 : 1))
-                             : (EPI == EPI_SWIGLU ? (MT == 1 ? 2 : 1) : 1);
-}
-
-template <int MT, int EPI>
-int launch_cfg(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-    constexpr int RG = rows_groups<MT, EPI>();
-    dim3 grid(p.ntiles, p.splits, p.mblocks);
-    if (p.rg != RG) return PD_EINVAL;
-    if constexpr (EPI == EPI_PARTIAL) {
-        if (p.wk == 8) {
-            hipLaunchKernelGGL((gemm_stream_kernel<MT, RG, 8, EPI>), grid, dim3(512), 0, s, a);
-            return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
-        }
+template <int EPI>
+int launch_ring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    constexpr int WN = EPI == EPI_SWIGLU ? 2 : 4;
+    constexpr int NM = EPI == EPI_SWIGLU ? 2 : 1;
+    if (p.wn != WN) return PD_EINVAL;
+    switch (p.mt) {
+        case 1: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 1, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 2, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 4, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
+        default: return PD_EINVAL;
     }
-    hipLaunchKernelGGL((gemm_stream_kernel<MT, RG, 4, EPI>), grid, dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
 template <int EPI>
 int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-    if (p.tiled) return launch_tiled<EPI>(p, a, s);
-    switch (p.mt) {
-        case 1: return launch_cfg<1, EPI>(p, a, s);
-        case 2: return launch_cfg<2, EPI>(p, a, s);
-        default: return launch_cfg<4, EPI>(p, a, s);
-    }
+    return p.tiled ? launch_tiled<EPI>(p, a, s) : launch_ring<EPI>(p, a, s);
 }
 
 }  // namespace
@@ -467,16 +512,15 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 GemmPlan plan_gemm(int M, int N, int K, int epi) {
     GemmPlan p;
     p.tiled = M > 64;
+    p.splits = 1;
     if (p.tiled) {
         // 128 x 128 tiles; K splits (partial planes, summed by the consumer)
         // only when the tile count leaves most of the 256 CUs idle
         p.mt = 0;
-        p.rg = 0;
-        p.wk = 4;
+        p.wn = 4;
         p.mblocks = (M + kTM - 1) / kTM;
         const int cols = (epi == EPI_SWIGLU) ? kTN / 2 : kTN;
         p.ntiles = (N + cols - 1) / cols;
-        p.splits = 1;
         if (epi == EPI_PARTIAL) {
             const long tiles = (long)p.ntiles * p.mblocks;
             const int ksteps = (K + kTK - 1) / kTK;
@@ -485,28 +529,30 @@ GemmPlan plan_gemm(int M, int N, int K, int epi) {
             while (s > 1 && s * 4 > ksteps) --s;
             p.splits = s < 1 ? 1 : s;
         }
+        p.grid = 8 * (int)((p.ntiles * (long)p.mblocks + 7) / 8);
         return p;
     }
+    // persistent LDS ring: 16 output columns per wave, 4 waves (2 for the
+    // gate/up pair); K splits (partial planes) chosen to minimise the stages
+    // the busiest of the <= 256 workgroups streams
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    p.mblocks = (M + 16 * p.mt - 1) / (16 * p.mt);
-    p.rg = p.mt == 1 ? (epi == EPI_ARGMAX ? rows_groups<1, EPI_ARGMAX>() : rows_groups<1, EPI_SWIGLU>())
-         : p.mt == 2 ? (epi == EPI_ARGMAX ? rows_groups<2, EPI_ARGMAX>() : rows_groups<2, EPI_SWIGLU>())
-                     : (epi == EPI_ARGMAX ? rows_groups<4, EPI_ARGMAX>() : rows_groups<4, EPI_SWIGLU>());
-    if (epi == EPI_PARTIAL) p.rg = 1;
-    p.wk = 4;
-    p.ntiles = (N + 16 * p.rg - 1) / (16 * p.rg);
-    p.splits = 1;
+    p.mblocks = 1;
+    p.wn = (epi == EPI_SWIGLU) ? 2 : 4;
+    const int ntn = (N + 16 * p.wn - 1) / (16 * p.wn);
+    const int ksteps = (K + kRS - 1) / kRS;
     if (epi == EPI_PARTIAL) {
-        // 8 waves per workgroup along K, and enough K splits across
-        // workgroups for ~6000 waves (short projections are latency-bound)
-        p.wk = 8;
-        const int ksteps = (K + kKStep - 1) / kKStep;
-        const long base = (long)p.ntiles * p.mblocks * p.wk;
-        int s = (int)((6000 + base - 1) / base);
-        if (s > 8) s = 8;
-        while (s > 1 && s * p.wk > ksteps) --s;
-        p.splits = s < 1 ? 1 : s;
+        long best = -1;
+        for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
+            const int per = (ksteps + sp - 1) / sp;
+            if ((sp - 1) * per >= ksteps) continue;   // no empty split
+            const long items = (long)ntn * sp;
+            const long span = ((items + 255) / 256) * per;
+            if (best < 0 || span < best) { best = span; p.splits = sp; }
+        }
     }
+    p.ntiles = (epi == EPI_ARGMAX) ? (N + 15) / 16 : ntn;
+    const long items = (long)ntn * p.splits;
+    p.grid = (int)(items < 256 ? items : 256);
     return p;
 }
 

@@ -36,13 +36,13 @@ struct GemmArgs {
 };
 
 struct GemmPlan {
-    bool tiled;    // 128 x 128 LDS-tiled kernel (many rows) instead of weight streaming
-    int mt;        // 16-row MFMA tiles of X per workgroup (1, 2 or 4)
-    int mblocks;   // workgroups along M
-    int rg;        // 16-row groups of W per workgroup
-    int wk;        // waves per workgroup, splitting its K range
-    int ntiles;    // workgroups along N
-    int splits;    // workgroups along K
+    bool tiled;    // 128 x 128 LDS-tiled kernel (many rows); else the persistent ring (M <= 64)
+    int mt;        // ring: 16-row X tiles (1, 2 or 4)
+    int mblocks;   // tiled: workgroups along M
+    int wn;        // waves per workgroup (ring: 16 output columns each)
+    int ntiles;    // column tiles (ARGMAX: groups of the max/argmax partial results per row)
+    int splits;    // K splits (EPI_PARTIAL: one fp32 plane each)
+    int grid;      // workgroups launched
 };
 
 GemmPlan plan_gemm(int M, int N, int K, int epi);
