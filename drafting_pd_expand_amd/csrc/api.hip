@@ -79,7 +79,7 @@ struct Timed {
 };
 
 struct Layout {
-    size_t x, u, q, ao, act, ws, po, pml, plan, amv, ami, total;
+    size_t x, u, q, ao, act, ws, po, pml, plan, xg, amv, ami, total;
     int T, R, ntilesV;
     AttnSplit sp;
 };
@@ -115,6 +115,7 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
     L.po = carve((size_t)L.sp.scap * T * hd * 4);
     L.pml = carve((size_t)L.sp.scap * T * m->Hq * 2 * 4);
     L.plan = carve(attn_plan_ints(L.sp) * 4);
+    L.xg = carve((size_t)R * m->d * 2);
     L.amv = carve((size_t)R * L.ntilesV * 4);
     L.ami = carve((size_t)R * L.ntilesV * 4);
     L.total = off;
@@ -232,6 +233,7 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     uint16_t* q = (uint16_t*)(S + L.q);
     uint16_t* ao = (uint16_t*)(S + L.ao);
     uint16_t* act = (uint16_t*)(S + L.act);
+    uint16_t* xg = (uint16_t*)(S + L.xg);
     float* ws = (float*)(S + L.ws);
     const int T = L.T, R = L.R, d = m->d;
     const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
@@ -318,16 +320,29 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, act, m->F, nullptr, 0, m->w_down[l], nullptr, T, d,
                     m->F, nullptr, 0, &sp));
         {
-            // next layer's input norm, or the final norm after the last layer
-            const uint16_t* gamma = (l + 1 < m->N) ? m->norm_in[l + 1] : m->norm_final;
             Timed t(h, PD_KERNEL_OTHER, s);
-            PD_TRY(launch_resid_norm(ws, sp, x, gamma, u, T, d, m->rms_eps, s));
+            if (l + 1 < m->N) {
+                // next layer's input norm
+                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_in[l + 1], u, T, d, m->rms_eps, s));
+            } else if (h->dbg) {
+                // the residual snapshot needs every row's final x
+                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, u, T, d, m->rms_eps, s));
+            } else {
+                // final norm of the K sampled rows of every request, packed for the LM head
+                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, xg, T, d, m->rms_eps, s,
+                                         b->new_token_indices, R, st));
+            }
         }
         PD_TRY(dbg(l + 1));
     }
-    // LM head on the K sampled rows of every request (gathered), greedy argmax
-    PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, u, d, b->new_token_indices, T, m->lm_head, nullptr, R,
-                m->V, d, nullptr, 0, nullptr));
+    if (h->dbg) {
+        Timed t(h, PD_KERNEL_OTHER, s);
+        PD_TRY(launch_resid_norm(nullptr, 0, x, m->norm_final, xg, T, d, m->rms_eps, s,
+                                 b->new_token_indices, R, st));
+    }
+    // LM head on the packed sampled rows, greedy argmax
+    PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, xg, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
+                nullptr, 0, nullptr));
     {
         Timed t(h, PD_KERNEL_OTHER, s);
         PD_TRY(launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV,

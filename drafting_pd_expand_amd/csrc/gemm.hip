@@ -47,10 +47,11 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
 // weights in flight with a single workgroup and no staging registers. A
 // stage holds the workgroup's W rows (16 output columns per wave, one row
 // group per matrix) and the matching X columns of all M rows; the waves read
-// their MFMA fragments from it (W is the A operand, X the B operand, as in the
-// streaming kernel, so the epilogues are the same). Rows are stored with
-// their 16-byte chunks XOR-permuted by (row & 7): the 8 lanes of one 16-byte
-// fragment read hit 8 different bank groups. Workgroups are persistent: each
+// their MFMA fragments from it (W is the A operand, X the B operand, in every
+// kernel of this file, so the epilogues agree). Rows are stored with
+// their 16-byte chunks XOR-permuted by (row & 15): the 16 lanes that one LDS
+// cycle serves (rows r..r+15, one chunk) read 16 different 16-byte slots of
+// the 256-byte bank line. Workgroups are persistent: each
 // walks the work items (column tile, K split) blockIdx.x, +gridDim.x, ... and
 // the ring runs on across item boundaries, so a CU never waits for a new
 // workgroup's first loads.
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
     for (int j = 0; j < WL; ++j) {
         const int u = tid + NT * j, wr = u >> 4;
         wrr[j] = wr % (16 * WN);
-        wch[j] = ((u & 15) ^ (wr & 7)) * 8;
+        wch[j] = ((u & 15) ^ (wr & 15)) * 8;
         wofs[j] = wrr[j] * a.K + wch[j];   // element offset from the tile's first row, k = 0
     }
     const uint16_t* xp[XL];
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
         const int u = tid + NT * j, m = u >> 4;
-        xch[j] = ((u & 15) ^ (m & 7)) * 8;
+        xch[j] = ((u & 15) ^ (m & 15)) * 8;
         int row = m;
         bool ok = m < a.M;
         if (ok && a.xrows) {
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             const uint16_t* Xs = Ws + Cf::WR * kRS;
 #pragma unroll
             for (int j = 0; j < kRS / 32; ++j) {
-                const int pos = ((4 * j + g4) ^ (r16 & 7)) * 8;
+                const int pos = ((4 * j + g4) ^ r16) * 8;
                 bf16x8 wf[NM];
 #pragma unroll
                 for (int q = 0; q < NM; ++q)
@@ -285,11 +286,11 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 // Tiled kernel for many rows (M > 64): a 128 x 128 output tile per workgroup,
 // K in steps of 64 staged through LDS (double buffered: the next step's
 // global loads are in registers while the current step's MFMAs run), four
-// waves each owning a 64 x 64 quarter (4 x 4 MFMA tiles). W is the A operand
-// and X the B operand, as in the streaming kernel, so the epilogues are the
-// same. For SwiGLU the tile's 128 W rows are 64 gate rows then the same 64 up
-// rows, and each wave takes 32 of each: a lane holds matching gate and up
-// columns.
+// waves each owning a 64 x 64 quarter (4 x 4 MFMA tiles); two workgroups fit
+// a CU. Used for 64 < M < 384 rows, where the 256-row tiles below would
+// mostly be padding. For SwiGLU the tile's 128 W rows are 64 gate rows then
+// the same 64 up rows, and each wave takes 32 of each: a lane holds matching
+// gate and up columns.
 constexpr int kTM = 128, kTN = 128, kTK = 64;
 constexpr int kTRow = kTK + 8;   // padded LDS row (elements): 144 B stride, conflict-free 16-byte reads
 
@@ -481,6 +482,225 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     }
 }
 
+// Persistent big-tile kernel for many rows (M > 64). A workgroup of 8 waves
+// (two per SIMD: one wave per SIMD cannot keep the matrix core busy) owns a
+// 256 (W rows = output columns) x 256 (X rows = output rows) tile; each wave
+// computes 128 x 64 of it (8 x 4 MFMA tiles), which keeps the LDS fragment
+// reads at 3 bytes per flop-pair lower than 64 x 64 wave tiles. W and X tiles
+// of 32 reduction elements go straight from HBM/L2 into a 4-stage LDS ring
+// (global_load_lds, 32 KB per stage); each of <= 256 workgroups walks its work
+// items (tile, K split) without restarting the ring. Rows are 64 B in LDS
+// with their 16-byte chunks XOR-permuted by ((row >> 2) & 3): the 16 lanes
+// that one LDS cycle serves (rows r..r+15, one chunk) then read 16 different
+// 16-byte slots of the 256-byte bank line. Items are dealt so that in
+// every round each XCD takes a contiguous run of tiles (M blocks innermost):
+// tiles sharing a W tile and K range meet in one L2. For SwiGLU a tile's W
+// rows are 128 gate rows then the same 128 up rows; a wave takes 64 of each.
+// X rows are read directly (no row gather).
+constexpr int kBT = 256;                 // tile rows of W and of X
+constexpr int kBS = 32;                  // reduction elements per stage (64 B of each row)
+constexpr int kBNST = 4;                 // ring stages
+constexpr int kBSE = 2 * kBT * kBS;      // elements per stage: W tile rows, then X tile rows
+
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
+    constexpr bool DUAL = (EPI == EPI_SWIGLU);
+    constexpr int L = 4;                      // 16-byte loads per thread per stage: 2 of W, 2 of X
+    constexpr int COLS = DUAL ? kBT / 2 : kBT;   // output columns per tile
+    __shared__ __align__(16) uint16_t ring[kBNST * kBSE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int wn = wave & 1, wm = wave >> 1;   // 2 column halves x 4 row quarters
+
+    const int mblocks = (a.M + kBT - 1) / kBT;
+    const int ntn = (a.N + COLS - 1) / COLS;
+    const int tiles = ntn * mblocks;
+    const int ksteps = (a.K + kBS - 1) / kBS;
+    const int per = (ksteps + a.splits - 1) / a.splits;
+    const int nitems = tiles * a.splits;
+    const int G = gridDim.x;
+    const int rpos = (G % 8 == 0) ? (blockIdx.x & 7) * (G / 8) + (blockIdx.x >> 3) : blockIdx.x;
+
+    // this thread's fixed share of every stage: units u = tid + 512 j; j = 0, 1
+    // are W rows u / 4, j = 2, 3 are X rows (u - 1024) / 4; chunk u % 4
+    int rowrel[4], ch[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int u = tid + 512 * j;
+        const int r = (j < 2 ? u : u - 1024) >> 2;
+        rowrel[j] = r;
+        ch[j] = ((u & 3) ^ ((r >> 2) & 3)) * 8;
+    }
+    const uint16_t* zp = g_gemm_zero;
+    const unsigned lds0 = ring_lds(ring);
+
+    int total = 0;
+    for (int it = rpos; it < nitems; it += G) {
+        const int sp = it / tiles;
+        total += max(0, min(ksteps, (sp + 1) * per) - sp * per);
+    }
+    int iitem = rpos, iks = 0, ike = 0;
+    if (iitem < nitems) {
+        const int sp = iitem / tiles;
+        iks = sp * per;
+        ike = min(ksteps, (sp + 1) * per);
+    }
+    auto issue = [&](int slot) {
+        while (iitem < nitems && iks >= ike) {
+            iitem += G;
+            if (iitem < nitems) {
+                const int sp = iitem / tiles;
+                iks = sp * per;
+                ike = min(ksteps, (sp + 1) * per);
+            }
+        }
+        const int tile = iitem % tiles;
+        const int m0 = (tile % mblocks) * kBT;
+        const int n0 = (tile / mblocks) * COLS;
+        const int k0 = iks * kBS;
+        const unsigned sbase = lds0 + (unsigned)(slot * kBSE) * 2u;
+        const bool kin = k0 + kBS <= a.K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t* src;
+            if (j < 2) {
+                const int r = rowrel[j];
+                const int n = n0 + (DUAL ? (r & (COLS - 1)) : r);
+                const uint16_t* base = (DUAL && r >= COLS) ? a.W2 : a.W;
+                src = (n < a.N && (kin || k0 + ch[j] < a.K)) ? base + (size_t)n * a.K + k0 + ch[j] : zp;
+            } else {
+                const int m = m0 + rowrel[j];
+                src = (m < a.M && (kin || k0 + ch[j] < a.K)) ? a.X + (size_t)m * a.ldx + k0 + ch[j] : zp;
+            }
+            __builtin_amdgcn_global_load_lds((void*)src,
+                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + 512 * j) * 16u),
+                16, 0, 0);
+        }
+        ++iks;
+    };
+
+    // LDS rows of this wave's fragments: W rows for the 8 column groups, X rows for 4
+    int wrow[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        wrow[i] = DUAL ? (i < 4 ? 64 * wn + 16 * i : COLS + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
+    const int rsw = (r16 >> 2) & 3;
+
+    for (int st = 0; st < kBNST - 1 && st < total; ++st) issue(st);
+
+    int qc = 0;
+    for (int it = rpos; it < nitems; it += G) {
+        const int sp = it / tiles;
+        const int kb = sp * per, ke = min(ksteps, (sp + 1) * per);
+        if (kb >= ke) continue;
+        const int tile = it % tiles;
+        const int m0 = (tile % mblocks) * kBT;
+        const int ntile = tile / mblocks;
+        const int n0 = ntile * COLS;
+        f32x4 acc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = kb; ks < ke; ++ks, ++qc) {
+            ring_wait_later<L, kBNST - 2>(min(kBNST - 2, total - 1 - qc));
+            ring_barrier();
+            if (qc + kBNST - 1 < total) issue((qc + kBNST - 1) % kBNST);
+            const uint16_t* Ws = ring + (qc % kBNST) * kBSE;
+            const uint16_t* Xs = Ws + kBT * kBS;
+            const int pos = (g4 ^ rsw) * 8;
+            bf16x8 af[8], bfr[4];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wrow[i] + r16) * kBS + pos);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(Xs + (64 * wm + 16 * j + r16) * kBS + pos);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
+        }
+
+        // lane holds rows m = m0 + 64*wm + 16*j + r16 and 4 consecutive columns per group i
+        if constexpr (EPI == EPI_ARGMAX) {
+            __shared__ float s_v[2][kBT];
+            __shared__ int s_i[2][kBT];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int ml = 64 * wm + 16 * j + r16;
+                const int m = m0 + ml;
+                float bv = -FLT_MAX;
+                int bi = INT_MAX;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int n = n0 + 128 * wn + 16 * i + 4 * g4;
+                    if (n >= a.N) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) better(bv, bi, acc[i][j][e], n + e);
+                    if (a.logits && m < a.M)
+                        *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[i][j];
+                }
+#pragma unroll
+                for (int off = 16; off <= 32; off <<= 1) {
+                    const float ov = __shfl_xor(bv, off, kWave);
+                    const int oi = __shfl_xor(bi, off, kWave);
+                    better(bv, bi, ov, oi);
+                }
+                if (g4 == 0) {
+                    s_v[wn][ml] = bv;
+                    s_i[wn][ml] = bi;
+                }
+            }
+            ring_barrier();   // (no wait on the ring's copies in flight)
+            if (tid < kBT) {
+                const int m = m0 + tid;
+                float bv = s_v[0][tid];
+                int bi = s_i[0][tid];
+                better(bv, bi, s_v[1][tid], s_i[1][tid]);
+                if (m < a.M) {
+                    a.amax_v[(size_t)m * a.ntiles + ntile] = bv;
+                    a.amax_i[(size_t)m * a.ntiles + ntile] = bi;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int m = m0 + 64 * wm + 16 * j + r16;
+                if (m >= a.M) continue;
+                if constexpr (EPI == EPI_PARTIAL) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int n = n0 + 128 * wn + 16 * i + 4 * g4;
+                        if (n < a.N)
+                            *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[i][j];
+                    }
+                } else {  // SwiGLU: groups 0..3 = gate, 4..7 = the matching up columns
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int n = n0 + 64 * wn + 16 * i + 4 * g4;
+                        if (n >= a.N) continue;
+                        float h[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) h[e] = silu(acc[i][j][e]) * acc[i + 4][j][e];
+                        uint2 pk;
+                        pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
+                        pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
+                        *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int EPI>
+int launch_big(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    if (a.xrows) return PD_EINVAL;   // many-row GEMMs read X rows directly
+    hipLaunchKernelGGL(gemm_big_kernel<EPI>, dim3(p.grid), dim3(512), 0, s, a);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
 template <int EPI>
 int launch_tiled(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     const int chunk = (p.ntiles * p.mblocks + 7) / 8;
@@ -504,18 +724,50 @@ int launch_ring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 
 template <int EPI>
 int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-    return p.tiled ? launch_tiled<EPI>(p, a, s) : launch_ring<EPI>(p, a, s);
+    switch (p.kind) {
+        case GEMM_RING: return launch_ring<EPI>(p, a, s);
+        case GEMM_TILED: return launch_tiled<EPI>(p, a, s);
+        default: return launch_big<EPI>(p, a, s);
+    }
 }
 
 }  // namespace
 
 GemmPlan plan_gemm(int M, int N, int K, int epi) {
     GemmPlan p;
-    p.tiled = M > 64;
+    p.kind = M <= 64 ? GEMM_RING : (M < 384 ? GEMM_TILED : GEMM_BIG);
     p.splits = 1;
-    if (p.tiled) {
-        // 128 x 128 tiles; K splits (partial planes, summed by the consumer)
-        // only when the tile count leaves most of the 256 CUs idle
+    p.grid = 0;
+    if (p.kind == GEMM_BIG) {
+        // persistent 256 x 256 tiles; K splits (partial planes, summed by the
+        // consumer) chosen to minimise the stages of the busiest of the <= 256
+        // workgroups
+        p.mt = 0;
+        p.wn = 8;
+        p.mblocks = (M + kBT - 1) / kBT;
+        const int cols = (epi == EPI_SWIGLU) ? kBT / 2 : kBT;
+        const int ntn = (N + cols - 1) / cols;
+        const long tiles = (long)ntn * p.mblocks;
+        const int ksteps = (K + kBS - 1) / kBS;
+        if (epi == EPI_PARTIAL) {
+            long best = -1;
+            for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
+                const int per = (ksteps + sp - 1) / sp;
+                if ((sp - 1) * per >= ksteps) continue;
+                const long span = ((tiles * sp + 255) / 256) * per;
+                if (best < 0 || span < best) { best = span; p.splits = sp; }
+            }
+        }
+        p.ntiles = ntn;
+        const long items = tiles * p.splits;
+        long g = items < 256 ? items : 256;
+        if (g >= 8) g -= g % 8;   // whole rounds of 8 XCDs
+        p.grid = (int)g;
+        return p;
+    }
+    if (p.kind == GEMM_TILED) {
+        // 128 x 128 tiles, two workgroups per CU; K splits only when the tile
+        // count leaves most of the 256 CUs idle
         p.mt = 0;
         p.wn = 4;
         p.mblocks = (M + kTM - 1) / kTM;
@@ -529,7 +781,6 @@ GemmPlan plan_gemm(int M, int N, int K, int epi) {
             while (s > 1 && s * 4 > ksteps) --s;
             p.splits = s < 1 ? 1 : s;
         }
-        p.grid = 8 * (int)((p.ntiles * (long)p.mblocks + 7) / 8);
         return p;
     }
     // persistent LDS ring: 16 output columns per wave, 4 waves (2 for the

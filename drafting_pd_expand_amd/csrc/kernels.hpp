@@ -35,14 +35,20 @@ struct GemmArgs {
     int32_t* status;
 };
 
+enum GemmKind : int {
+    GEMM_RING = 0,    // M <= 64: persistent LDS-ring weight streaming
+    GEMM_TILED = 1,   // 64 < M < 384: 128 x 128 tiles, two workgroups per CU
+    GEMM_BIG = 2,     // M >= 384: persistent 256 x 256 tiles, 8 waves
+};
+
 struct GemmPlan {
-    bool tiled;    // 128 x 128 LDS-tiled kernel (many rows); else the persistent ring (M <= 64)
+    int kind;      // GemmKind
     int mt;        // ring: 16-row X tiles (1, 2 or 4)
-    int mblocks;   // tiled: workgroups along M
+    int mblocks;   // tiled / big: workgroups along M
     int wn;        // waves per workgroup (ring: 16 output columns each)
     int ntiles;    // column tiles (ARGMAX: groups of the max/argmax partial results per row)
     int splits;    // K splits (EPI_PARTIAL: one fp32 plane each)
-    int grid;      // workgroups launched
+    int grid;      // ring / big: persistent workgroups
 };
 
 GemmPlan plan_gemm(int M, int N, int K, int epi);
@@ -55,8 +61,10 @@ int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 int launch_layer0_input(const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
                         float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
                         int d, float eps, int32_t* status, hipStream_t s);
+// rows != nullptr: output row o = norm of row rows[o] (o < nrows), x untouched.
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
-                      int d, float eps, hipStream_t s);
+                      int d, float eps, hipStream_t s, const int32_t* rows = nullptr, int nrows = 0,
+                      int32_t* status = nullptr);
 int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
                       int Hq, int Hkv, int dh, float theta, uint16_t* q_out, uint16_t* kplane,
                       uint16_t* vplane, int num_blocks, int32_t* status, hipStream_t s);

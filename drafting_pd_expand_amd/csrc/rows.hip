@@ -57,16 +57,29 @@ __device__ __forceinline__ void load_row_sum(float4 (&v)[NC], const float* xr, c
 
 // Residual stream update and the next RMSNorm, one row per workgroup:
 // x += sum_s ws[s] (the projection's split planes, in order), then
-// y = bf16(gamma * x / sqrt(mean(x^2) + eps)).
+// y = bf16(gamma * x / sqrt(mean(x^2) + eps)). With a row list, output row o
+// is the norm of row rows[o] (the rows the LM head samples, packed) and x is
+// left as it is; a list entry outside [0, T) is flagged and gives a zero row.
 template <int NC>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int S, float* x,
                                                          const uint16_t* gamma, uint16_t* y, int T,
-                                                         int d, float eps) {
+                                                         int d, float eps, const int32_t* rows,
+                                                         int32_t* status) {
     __shared__ float red[4];
     const int o = blockIdx.x;
-    float* xr = x + (size_t)o * d;
+    int i = o;
+    bool ok = true;
+    if (rows) {
+        i = rows[o];
+        if (i < 0 || i >= T) {
+            if (threadIdx.x == 0) flag(status, PD_STATUS_BAD_ROW);
+            ok = false;
+            i = 0;
+        }
+    }
+    float* xr = x + (size_t)i * d;
     float4 v[NC];
-    load_row_sum<NC>(v, xr, ws, S, (size_t)T * d, (size_t)o * d, d, true);
+    load_row_sum<NC>(v, xr, ws, S, (size_t)T * d, (size_t)i * d, d, true);
     uint2 gb[NC];
     float ss = 0.f;
 #pragma unroll
@@ -74,12 +87,12 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int S,
         const int c = threadIdx.x * 4 + 1024 * n;
         if (c < d) {
             gb[n] = *reinterpret_cast<const uint2*>(gamma + c);
-            if (S > 0) *reinterpret_cast<float4*>(xr + c) = v[n];
+            if (S > 0 && !rows) *reinterpret_cast<float4*>(xr + c) = v[n];
             ss += v[n].x * v[n].x + v[n].y * v[n].y + v[n].z * v[n].z + v[n].w * v[n].w;
         }
     }
     ss = block_sum_256(ss, red);
-    const float rs = 1.0f / sqrtf(ss / (float)d + eps);
+    const float rs = ok ? 1.0f / sqrtf(ss / (float)d + eps) : 0.f;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
         const int c = threadIdx.x * 4 + 1024 * n;
@@ -271,10 +284,12 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* amax_v,
     }
 
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
-                      int d, float eps, hipStream_t s) {
-    if (T <= 0) return PD_OK;
+                      int d, float eps, hipStream_t s, const int32_t* rows, int nrows, int32_t* status) {
+    const int nout = rows ? nrows : T;
+    if (nout <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
-#define L_(NC) hipLaunchKernelGGL(resid_norm_kernel<NC>, dim3(T), dim3(256), 0, s, ws, S, x, gamma, y, T, d, eps)
+#define L_(NC) hipLaunchKernelGGL(resid_norm_kernel<NC>, dim3(nout), dim3(256), 0, s, ws, S, x, gamma, y, T, d, \
+                                  eps, rows, status)
     PD_ROW_NC(d, L_)
 #undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
