@@ -51,6 +51,27 @@ def lm_head_bytes(dm, R: int) -> int:
     return dm.V * dm.d * 2 + R * dm.d * 2 + R * 4
 
 
+def attn_bytes(dm, b, K: int) -> int:
+    """Algorithmic bytes of one attention launch (one layer): every visible
+    cached K and V row once per kv head, the rotated queries in and the bf16
+    outputs out."""
+    v = b["num_tokens"] - b["num_rejected"]
+    seq = b["context_lens"] + v + K - 1
+    T_out = b["T_in"] + b["C"] * (K - 1)
+    return int(seq.sum()) * dm.Hkv * dm.dh * 2 * 2 + 2 * T_out * dm.Hq * dm.dh * 2
+
+
+def gemm_flops(dm, b, K: int) -> int:
+    """GEMM flops of one step on the T_eff computed rows (rejected rows earn
+    no credit) plus the LM head on C*K rows."""
+    v = b["num_tokens"] - b["num_rejected"]
+    T_eff = int((v + K - 1).sum())
+    per_row = dm.d * dm.hidden3
+    for l in range(dm.N):
+        per_row += dm.qkv_out * dm.qkv_in(l) + dm.d * dm.Hq * dm.dh + 3 * dm.F * dm.d
+    return 2 * T_eff * per_row + 2 * b["C"] * K * dm.V * dm.d
+
+
 def step_bytes(dm, b, K: int) -> int:
     """Algorithmic bytes of one whole step (weights once, visible KV once per
     layer and kv head, KV writes, hidden rows in and out, ids)."""
@@ -186,41 +207,111 @@ def main():
     h = pdx.Handle()
     stream = torch.cuda.current_stream()
 
-    def step():
-        pdx.pd_expand_batch(dims, inp, out, stream)
-        pdx.pd_draft_forward(h, mdev, dims, out, inp["block_table"], cache, draft, None, stream)
+    def step(strm):
+        pdx.pd_expand_batch(dims, inp, out, strm)
+        pdx.pd_draft_forward(h, mdev, dims, out, inp["block_table"], cache, draft, None, strm)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        step()
+        step(stream)
     torch.cuda.synchronize()
     st = h.status() | int(out["status"].item())
     if st:
         raise SystemExit(f"device status {st} after warmup")
-    h.profile(1 << pdx.KERNEL_LMHEAD)
+    eager_ids = draft.clone()
+
+    # breakdown pass (not the timed region): events around every kernel class
+    nb = min(5, args.steps)
+    h.profile((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_GEMM) | (1 << pdx.KERNEL_ATTN) | (1 << pdx.KERNEL_OTHER))
+    for _ in range(nb):
+        step(stream)
     torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    cls_us = {}
+    for name, k in (("lm_head", pdx.KERNEL_LMHEAD), ("gemm", pdx.KERNEL_GEMM), ("attention", pdx.KERNEL_ATTN),
+                    ("other", pdx.KERNEL_OTHER)):
+        t_ms, n = h.profile_read(k)
+        cls_us[name] = {"us_per_step": t_ms * 1000.0 / nb, "launches_per_step": n // nb,
+                        "us_per_launch": t_ms * 1000.0 / max(n, 1)}
+    h.profile(0)
+    # the dominant single kernel: the LM head (one launch) or the attention kernel (one per layer)
+    dom = "lm_head" if cls_us["lm_head"]["us_per_launch"] >= cls_us["attention"]["us_per_launch"] else "attention"
+    dom_cls = pdx.KERNEL_LMHEAD if dom == "lm_head" else pdx.KERNEL_ATTN
+
+    # timed region: plain launches; HIP events around the dominant kernel only
+    h.profile(1 << dom_cls)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps (plain launches)")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1)
-    lm_ms, lm_n = h.profile_read(pdx.KERNEL_LMHEAD)
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
+    ms = evs[0].elapsed_time(evs[-1])
+    k_ms, k_n = h.profile_read(dom_cls)
     h.profile(0)
     ms_step = ms / args.steps
     steps_s = 1000.0 / ms_step
-    lm_avg_s = lm_ms / max(lm_n, 1) / 1000.0
-    lm_b = lm_head_bytes(dm, R)
-    achieved = lm_b / lm_avg_s / 1e9
+    k_avg_s = k_ms / max(k_n, 1) / 1000.0
+
+    # the same step as one hipGraph replayed; every replay's draft ids must equal the eager ones
+    graph = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step(cap)   # warm the capture stream (no allocation happens: the handle is sized)
+            cap.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                step(cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        ok = True
+        for _ in range(3):
+            draft.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            ok = ok and bool(torch.equal(draft, eager_ids))
+        ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ge0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ge1.record(stream)
+        torch.cuda.synchronize()
+        g_ms = ge0.elapsed_time(ge1) / args.steps
+        graph = {"steps_per_s": 1000.0 / g_ms, "ms_per_step": g_ms, "replays_match_eager": ok}
+        log(f"[bench] hipGraph replay {g_ms * 1000:.1f} us/step, draft ids match eager: {ok}")
+        del g
+    except Exception as ex:  # graph capture is a report extra; the plain-launch number stands
+        log(f"[bench] hipGraph replay skipped: {ex}")
+        graph = {"error": str(ex)[:200]}
+
+    R = b["C"] * w.K
+    if dom == "lm_head":
+        if R <= 64:   # weight-streaming ring kernel: HBM-bound
+            roof = {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
+                    "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        else:         # many rows: MFMA-bound
+            kname = "gemm_tiled_kernel<ARGMAX>" if R < 384 else "gemm_big_kernel<ARGMAX>"
+            roof = {"bound": "mfma", "kernel": f"{kname} (LM head + fused argmax)",
+                    "achieved": 2.0 * R * dm.V * dm.d / k_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "kernel": f"attn_split_kernel<{dm.dh}> (paged split-KV attention)",
+                "achieved": attn_bytes(dm, b, w.K) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(args.workload) if dom == "lm_head" and R <= 64 else None
+    roof["us_per_launch"] = k_avg_s * 1e6
     sb = step_bytes(dm, b, w.K)
+    gf = gemm_flops(dm, b, w.K)
+    gemm_us = cls_us["gemm"]["us_per_step"] + cls_us["lm_head"]["us_per_step"]
     log(f"[bench] {ms_step * 1000:.1f} us/step ({steps_s:.1f} steps/s, wall {wall * 1000 / args.steps:.1f} us/step); "
-        f"LM head {lm_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s; whole step {sb / 1e9:.3f} GB algorithmic = "
-        f"{sb / (ms_step / 1000) / 1e9:.0f} GB/s")
+        f"dominant {dom} {k_avg_s * 1e6:.1f} us = {roof['achieved']:.0f} {roof['unit']}; whole step "
+        f"{sb / 1e9:.3f} GB algorithmic = {sb / (ms_step / 1000) / 1e9:.0f} GB/s; GEMMs {gemm_us:.0f} us = "
+        f"{gf / (gemm_us * 1e-6) / 1e12:.0f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -245,10 +336,13 @@ def main():
         "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "C": w.C, "K": w.K,
                    "T_in": b["T_in"], "T_out": b["T_in"] + w.C * (w.K - 1)},
         "drafted_tok_per_s": steps_s * R,
+        "ms_per_step_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
         "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(args.workload)},
+        "step_algorithmic_bytes": sb,
+        "gemm_mfma_frac": gf / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+        "kernel_classes_us_per_step": {k: round(v["us_per_step"], 1) for k, v in cls_us.items()},
+        "hipgraph": graph,
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     h.free()

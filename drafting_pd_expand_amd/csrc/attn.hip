@@ -510,7 +510,10 @@ int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
 AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks) {
     AttnSplit p;
     p.min_split = 128;
-    p.target_wg = 2048;
+    // workgroups the split length aims at: dh 128 moves twice the bytes per
+    // key and per partial, and runs best with ~4x fewer, longer splits
+    // (measured on the 16 x 20000-key batch: 142 us at 512 vs 177 us at 2048)
+    p.target_wg = dh == 64 ? 2048 : 512;
     const long long reach = (long long)max_blocks * PD_PAGE;
     // a split never exceeds the LDS block-table cache: enough workgroups for
     // the longest batch the block table can describe

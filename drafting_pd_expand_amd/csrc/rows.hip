@@ -238,16 +238,17 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
 
 // Greedy draft token: argmax over the per-tile (max, index) pairs of one
 // row, lowest index on exact ties.
-__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* amax_v, const int* amax_i,
-                                                            int ntiles, int32_t* out,
-                                                            int32_t* status) {
-    __shared__ float sv[4];
-    __shared__ int si[4];
+__global__ __launch_bounds__(1024) void argmax_reduce_kernel(const float* amax_v, const int* amax_i,
+                                                             int ntiles, int32_t* out,
+                                                             int32_t* status) {
+    __shared__ float sv[16];
+    __shared__ int si[16];
     const int m = blockIdx.x;
     float bv = -FLT_MAX;
     int bi = INT_MAX;
-#pragma unroll 8
-    for (int t = threadIdx.x; t < ntiles; t += 256)
+    // a row's partials (up to ~12.6k) in one round of independent loads per thread
+#pragma unroll 16
+    for (int t = threadIdx.x; t < ntiles; t += 1024)
         better(bv, bi, amax_v[(size_t)m * ntiles + t], amax_i[(size_t)m * ntiles + t]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* amax_v,
     if (threadIdx.x == 0) {
         float v = sv[0];
         int ix = si[0];
-        for (int w = 1; w < 4; ++w) better(v, ix, sv[w], si[w]);
+        for (int w = 1; w < 16; ++w) better(v, ix, sv[w], si[w]);
         if (ix == INT_MAX) {
             flag(status, PD_STATUS_BAD_ROW);
             ix = 0;
@@ -322,7 +323,7 @@ int launch_rope_cache(const float* ws, int S, const int32_t* positions, const in
 int launch_argmax_reduce(const float* amax_v, const int* amax_i, int M, int ntiles, int32_t* out,
                          int32_t* status, hipStream_t s) {
     if (M <= 0) return PD_OK;
-    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(256), 0, s, amax_v, amax_i, ntiles,
+    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(M), dim3(1024), 0, s, amax_v, amax_i, ntiles,
                        out, status);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
