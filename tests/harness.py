@@ -224,4 +224,8 @@ def check_case(case: Case, requests=None, check_cache=True, check_layers=False):
             rms = np.sqrt(np.mean(xo * xo, axis=1))
             err = np.max(np.abs(xg - xo), axis=1)
             assert np.all(err <= LOGIT_TOL * rms), f"residual after stage {l}: error/RMS {np.max(err / rms):.4f}"
-    return {"worst_logit_ratio": worst, "argmax_checked": n_checked, "rows": len(sel)}
+    res = {"worst_logit_ratio": worst, "argmax_checked": n_checked, "rows": len(sel)}
+    # one line per checked case (visible with pytest -s): the observed error budget use
+    print(f"[parity] {case.w.name}: rows {len(sel)}, worst logit err/RMS "
+          f"{'-' if worst is None else f'{worst:.4f}'}, argmax checked {n_checked}", flush=True)
+    return res
