@@ -8,6 +8,10 @@ Plain, slow, float64 NumPy definitions of what the drafting step computes:
   * ``draft_forward`` -- fc projection, the N decoder layers (RMSNorm, RoPE,
                          paged causal GQA attention, SwiGLU MLP), final norm,
                          LM head and greedy argmax.
+  * ``ar_advance``    -- the next pass of autoregressive EAGLE-style drafting
+                         (one row per request, fed back token and hidden), and
+  * ``ar_draft``      -- K such serial passes: the baseline that parallel
+                         drafting replaces.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. The product path (the HIP library and
@@ -28,8 +32,8 @@ library causal-attention forward on prefill, brute-force softmax, invariants
 (a)-(e) and request independence. Full-forward logits at random init have no
 printed values on the pages: beyond those pins they are "parity unpinned".
 """
-from .expand import expand
-from .forward import draft_forward, rope_rotate, rms_norm, silu
+from .expand import expand, ar_advance
+from .forward import draft_forward, ar_draft, rope_rotate, rms_norm, silu
 from .bf16 import bf16_to_f64
 
-__all__ = ["expand", "draft_forward", "rope_rotate", "rms_norm", "silu", "bf16_to_f64"]
+__all__ = ["expand", "ar_advance", "draft_forward", "ar_draft", "rope_rotate", "rms_norm", "silu", "bf16_to_f64"]

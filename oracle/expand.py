@@ -120,3 +120,42 @@ def expand(num_tokens, num_rejected, target_ids, target_pos, target_hidden,
         "hidden_state_mapping": i32(hmap), "new_token_indices": i32(new_idx),
         "cu_out": i32(cu_out), "seq_lens": i32(seq_lens), "hidden": hidden,
     }
+
+
+def ar_advance(prev: dict, K_prev: int, draft_ids, block_table, block_size: int) -> dict:
+    """The next pass of autoregressive (EAGLE-style) drafting, one row per request.
+
+    [Blog] "background and motivation": autoregressive EAGLE drafts K tokens
+    with K serial forward passes of the drafter. [Blog] "P-EAGLE core method"
+    and [arXiv] Figure 2 caption: the NTP position (pass 1) is exactly the
+    autoregressive case; the later positions lack inputs in the parallel
+    drafter because, autoregressively, they would come from the previous pass.
+
+    Reading (the pages leave the fed-back state open): pass k >= 2 has one row
+    per request, at the position after the previous pass's last sampled row;
+    its token is the token that pass sampled, and its hidden input is the
+    drafter's own final hidden state of that sampled row (d wide, so it does
+    not go through fc; the forward's ``hidden_d`` rows). Rows are never
+    rejected and every row is sampled.
+
+    prev: the previous pass's batch (an ``expand`` result or an earlier
+    ``ar_advance`` result); K_prev: its draft depth; draft_ids: the tokens it
+    sampled, request-major [C * K_prev].
+    """
+    C = len(prev["cu_out"]) - 1
+    new_idx = np.asarray(prev["new_token_indices"], np.int64)
+    pos_prev = np.asarray(prev["positions"], np.int64)
+    ids = np.asarray(draft_ids, np.int64)
+    bt = np.asarray(block_table, np.int64)
+    last = [r * K_prev + K_prev - 1 for r in range(C)]   # the last sampled row of each request
+    positions = np.array([pos_prev[new_idx[i]] + 1 for i in last], np.int32)
+    return {
+        "input_ids": np.array([ids[i] for i in last], np.int32),
+        "positions": positions,
+        "slot_mapping": np.array([_slot(bt[r], int(positions[r]), block_size) for r in range(C)], np.int32),
+        "is_rejected": np.zeros(C, np.uint8),
+        "is_masked": np.zeros(C, np.uint8),
+        "new_token_indices": np.arange(C, dtype=np.int32),
+        "cu_out": np.arange(C + 1, dtype=np.int32),
+        "seq_lens": (positions + 1).astype(np.int32),
+    }

@@ -35,6 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 from .bf16 import bf16_to_f64
+from .expand import ar_advance as _ar_advance
 
 
 def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
@@ -82,10 +83,14 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
            bits (uint16) or float values.
     requests: subset of request indices to compute (requests are independent),
            default all.
+    exp may carry "hidden_d" ([T_out][d] float) with "use_hidden_d" ([T_out]
+    bool): those rows take hidden_d as their projected hidden input directly
+    (no fc) -- the drafter's own hidden state fed back in autoregressive
+    passes (see expand.ar_advance).
     Returns logits [R][V] and draft_ids [R] for the K sampled rows of each
-    requested request (request-major, NTP row first), the K/V each layer
-    wrote (slots, k, v), and optionally the residual stream after fc and
-    after every layer.
+    requested request (request-major, NTP row first), hidden_out [R][d] (their
+    final residual, before the final norm), the K/V each layer wrote (slots,
+    k, v), and optionally the residual stream after fc and after every layer.
     """
     m = model["dims"]
     eps, theta = m.rms_eps, m.rope_theta
@@ -118,9 +123,15 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
     all_slots = np.unique(np.concatenate([read_slots[r] for r in reqs] + [slots]))
     local = lambda s: np.searchsorted(all_slots, s)
 
-    # fc projection of the 3d-wide hidden rows, token embeddings
-    h = bf16_to_f64(np.asarray(exp["hidden"])[rows])
-    x = h @ bf16_to_f64(model["fc"]).T
+    # fc projection of the 3d-wide hidden rows (or the given d-wide rows), token embeddings
+    use_d = (np.asarray(exp["use_hidden_d"], bool)[rows] if "use_hidden_d" in exp
+             else np.zeros(nrow, bool))
+    x = np.empty((nrow, m.d))
+    if (~use_d).any():
+        h = bf16_to_f64(np.asarray(exp["hidden"])[rows[~use_d]])
+        x[~use_d] = h @ bf16_to_f64(model["fc"]).T
+    if use_d.any():
+        x[use_d] = np.asarray(exp["hidden_d"], np.float64)[rows[use_d]]
     e = bf16_to_f64(np.asarray(model["embed"])[ids])
     layers_out = [x.copy()] if return_layers else None
     written = []
@@ -168,13 +179,54 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
     new_idx = np.asarray(exp["new_token_indices"], np.int64)
     sampled = np.concatenate([new_idx[r * K:(r + 1) * K] for r in reqs]) if reqs else np.zeros(0, np.int64)
     where = {int(o): i for i, o in enumerate(rows)}
-    z = rms_norm(x[[where[int(o)] for o in sampled]], bf16_to_f64(model["norm_final"]), eps)
+    xs = x[[where[int(o)] for o in sampled]]
+    z = rms_norm(xs, bf16_to_f64(model["norm_final"]), eps)
     logits = z @ bf16_to_f64(model["lm_head"]).T
     out = {
         "requests": reqs, "rows": rows, "sampled_rows": sampled,
         "logits": logits, "draft_ids": np.argmax(logits, axis=1).astype(np.int32),
-        "kv_written": written,
+        "hidden_out": xs, "kv_written": written,
     }
     if return_layers:
         out["layers"] = layers_out
+    return out
+
+
+def ar_draft(model: dict, exp1: dict, block_table, kv: dict, K: int, block_size: int = 16,
+             tokens=None) -> list:
+    """Autoregressive EAGLE-style drafting of K tokens per request: K serial
+    drafter passes ([Blog] "background and motivation"), the baseline that
+    parallel drafting replaces.
+
+    exp1 is the K = 1 expansion of the verify batch (pass 1 = the NTP
+    position, [Blog] "P-EAGLE core method"). Pass k >= 2 runs the one-row batch
+    of ``ar_advance``: the previous pass's sampled token with the drafter's own
+    final hidden state of that row as the (already d-wide) hidden input. Every
+    pass writes its K/V to the cache before the next reads it.
+
+    tokens: optional [K][C] tokens to feed forward instead of this function's
+    own argmax (a caller comparing against another implementation feeds its
+    choices so both take the same path through near-ties).
+    Returns the K pass results of ``draft_forward`` (logits, draft_ids,
+    hidden_out, ...) and the batches they ran on ("batch").
+    """
+    m = model["dims"]
+    kvf = {"k": [_as_f64(kv["k"][l]).copy() for l in range(m.N)],
+           "v": [_as_f64(kv["v"][l]).copy() for l in range(m.N)]}
+    out, batch = [], exp1
+    for k in range(K):
+        res = draft_forward(model, batch, block_table, kvf, 1, block_size=block_size)
+        res["batch"] = batch
+        out.append(res)
+        for l, (sl, kk, vv) in enumerate(res["kv_written"]):
+            kvf["k"][l][sl] = kk
+            kvf["v"][l][sl] = vv
+        if k + 1 == K:
+            break
+        ids = res["draft_ids"] if tokens is None else np.asarray(tokens[k])
+        nxt = _ar_advance(batch, 1, ids, block_table, block_size)
+        C = len(nxt["cu_out"]) - 1
+        nxt["hidden_d"] = res["hidden_out"]
+        nxt["use_hidden_d"] = np.ones(C, bool)
+        batch = nxt
     return out

@@ -28,6 +28,9 @@ MUTATIONS = [
     ("expand.py", "slot[o] = -1 if is_rej[o] else _slot(bt[r], int(pos[o]), block_size)",
      "slot[o] = _slot(bt[r], int(pos[o]), block_size)"),                                       # -1 for rejected
     ("expand.py", "new_idx[r * K] = out_start + v - 1", "new_idx[r * K] = out_start + v"),     # NTP index
+    ("forward.py", 'kvf["k"][l][sl] = kk', "pass"),                                           # AR: no KV carry-over
+    ("expand.py", "pos_prev[new_idx[i]] + 1 for i in last", "pos_prev[new_idx[i]] + 2 for i in last"),  # AR position
+    ("forward.py", 'nxt["hidden_d"] = res["hidden_out"]', 'nxt["hidden_d"] = 0 * res["hidden_out"]'),  # AR feedback
 ]
 
 
@@ -41,6 +44,7 @@ def test_planted_mistake_is_caught(tmp_path, fname, old, new):
     (dst / fname).write_text(src.replace(old, new))
     env = dict(os.environ, PD_ORACLE_MUTANT_DIR=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_expand.py", "tests/test_oracle_forward.py"],
+                        "tests/test_oracle_expand.py", "tests/test_oracle_forward.py",
+                        "tests/test_oracle_ar.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "the oracle pins did not catch: " + new + "\n" + r.stdout[-2000:]
