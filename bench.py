@@ -153,6 +153,60 @@ def recorded_traffic(workload: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
+def ar_baseline(pdx, mdev, b, w, inp, cache, par_draft, stream, steps: int) -> dict:
+    """The autoregressive K-pass baseline on the same kernels and inputs
+    ([Blog] "background and motivation"): expand with K = 1, then K drafter
+    passes, pass k >= 2 on one row per request (pd_ar_advance +
+    pd_draft_forward_ex fed the previous pass's final hidden state). One
+    "step" drafts the same K tokens per request as one parallel step. Every
+    pass writes its KV rows, which the next pass (and step) overwrites."""
+    import torch
+    dev = torch.device("cuda:0")
+    dm, C, K = w.model, b["C"], w.K
+    dims1 = pdx.batch_dims(C, 1, b["T_in"], b["mask_id"], dm.hidden3, b["max_blocks"], b["num_blocks"])
+    nd = dict(dims1, K=1, T_in=C)
+    out1 = pdx.alloc_batch(dims1, dev)
+    nxt = [pdx.alloc_batch(nd, dev) for _ in range(K - 1)]
+    draft = [torch.empty(C, dtype=torch.int32, device=dev) for _ in range(K)]
+    hid = [torch.empty((C, dm.d), dtype=torch.bfloat16, device=dev) for _ in range(K)]
+    ha = pdx.Handle()
+    bt = inp["block_table"]
+
+    def ar_step():
+        pdx.pd_expand_batch(dims1, inp, out1, stream)
+        pdx.pd_draft_forward(ha, mdev, dims1, out1, bt, cache, draft[0], None, stream, hidden_out=hid[0])
+        prev, pd = out1, dims1
+        for k in range(1, K):
+            pdx.pd_ar_advance(pd, prev, draft[k - 1], bt, nxt[k - 1], stream)
+            pdx.pd_draft_forward(ha, mdev, nd, nxt[k - 1], bt, cache, draft[k], None, stream,
+                                 hidden_d=hid[k - 1], hidden_out=hid[k])
+            prev, pd = nxt[k - 1], nd
+
+    for _ in range(3):
+        ar_step()
+    torch.cuda.synchronize()
+    st = ha.status() | int(out1["status"].item())
+    for t in nxt:
+        st |= int(t["status"].item())
+    if st:
+        raise SystemExit(f"device status {st} in the autoregressive baseline")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(1, steps // 2)
+    e0.record(stream)
+    for _ in range(n):
+        ar_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    # pass 1 computes the parallel step's NTP rows; near-ties may round either way
+    ntp = par_draft.view(C, K)[:, 0]
+    agree = float((ntp == draft[0]).float().mean().item())
+    ha.free()
+    log(f"[bench] autoregressive baseline: {ms * 1000:.1f} us per {K}-token step")
+    return {"ms_per_step": ms, "steps_per_s": 1000.0 / ms, "drafted_tok_per_s": 1000.0 / ms * C * K,
+            "passes": K, "steps_timed": n, "pass1_equals_parallel_ntp_frac": agree}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +344,9 @@ def main():
         log(f"[bench] hipGraph replay skipped: {ex}")
         graph = {"error": str(ex)[:200]}
 
+    ar = ar_baseline(pdx, mdev, b, w, inp, cache, draft, stream, args.steps)
+    ar["parallel_speedup"] = ar["ms_per_step"] / ms_step
+
     R = b["C"] * w.K
     if dom == "lm_head":
         if R <= 64:   # weight-streaming ring kernel: HBM-bound
@@ -342,6 +399,7 @@ def main():
         "gemm_mfma_frac": gf / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
         "kernel_classes_us_per_step": {k: round(v["us_per_step"], 1) for k, v in cls_us.items()},
         "hipgraph": graph,
+        "ar_baseline": ar,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "PD_OK", "PD_EINVAL", "PD_ENOMEM", "PD_EHIP", "PD_PAGE", "PD_MAX_LAYERS",
     "KERNEL_LMHEAD", "KERNEL_GEMM", "KERNEL_ATTN", "KERNEL_OTHER",
-    "PdError", "library_path", "load", "pd_expand_batch", "pd_draft_forward", "pd_free",
+    "PdError", "library_path", "load", "pd_expand_batch", "pd_draft_forward", "pd_ar_advance", "pd_free",
     "Handle", "batch_dims", "alloc_batch", "device_model", "pack_kv_cache",
     "unpack_kv_cache", "kv_cache_elems",
 ]
@@ -68,6 +68,10 @@ class Batch(ctypes.Structure):
 _L = c_void_p * PD_MAX_LAYERS
 
 
+class ForwardOpts(ctypes.Structure):
+    _fields_ = [("hidden_d", c_void_p), ("hidden_out", c_void_p)]
+
+
 class Model(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("d", "Hq", "Hkv", "dh", "F", "N", "V", "hidden3")] + [
         ("rms_eps", c_float), ("rope_theta", c_float),
@@ -93,6 +97,13 @@ def load():
     lib.pd_draft_forward.argtypes = [POINTER(c_void_p), POINTER(Model), POINTER(BatchDims),
                                      POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.pd_draft_forward.restype = c_int
+    lib.pd_draft_forward_ex.argtypes = [POINTER(c_void_p), POINTER(Model), POINTER(BatchDims),
+                                        POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p,
+                                        POINTER(ForwardOpts), c_void_p]
+    lib.pd_draft_forward_ex.restype = c_int
+    lib.pd_ar_advance.argtypes = [POINTER(BatchDims), POINTER(Batch), c_void_p, c_void_p, POINTER(Batch),
+                                  c_void_p]
+    lib.pd_ar_advance.restype = c_int
     lib.pd_free.argtypes = [c_void_p]
     lib.pd_free.restype = None
     lib.pd_strerror.argtypes = [c_int]
@@ -175,7 +186,7 @@ def alloc_batch(dims: dict, device) -> dict:
     }
 
 
-def _batch_struct(b: dict, dims: dict, device=None) -> Batch:
+def _batch_struct(b: dict, dims: dict, device=None, hidden_optional: bool = False) -> Batch:
     C, K, T_in = dims["C"], dims["K"], dims["T_in"]
     T_out = T_in + C * (K - 1)
     sizes = {"input_ids": T_out, "positions": T_out, "slot_mapping": T_out, "is_rejected": T_out,
@@ -185,7 +196,7 @@ def _batch_struct(b: dict, dims: dict, device=None) -> Batch:
     aligns = {"is_rejected": 1, "is_masked": 1}
     vals = []
     for n in _BATCH_FIELDS:
-        if n == "status" and b.get("status") is None:
+        if (n == "status" or (n == "hidden" and hidden_optional)) and b.get(n) is None:
             vals.append(None)
             continue
         vals.append(_dev(b[n], n, types.get(n, (torch.int32,)), sizes[n], device, aligns.get(n)))
@@ -280,9 +291,12 @@ def _model_struct(m: dict) -> Model:
 
 
 def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block_table, kv_cache,
-                     draft_ids, logits=None, stream=None) -> None:
-    """Enqueue the drafter pass (include/pd.h: pd_draft_forward). `model` is a
-    dict made by device_model(); `batch` holds the expanded-batch tensors."""
+                     draft_ids, logits=None, stream=None, hidden_d=None, hidden_out=None) -> None:
+    """Enqueue the drafter pass (include/pd.h: pd_draft_forward, or
+    pd_draft_forward_ex when hidden_d / hidden_out are given). `model` is a
+    dict made by device_model(); `batch` holds the expanded-batch tensors.
+    hidden_d: bf16 [T_out][d] projected hidden rows (fc skipped);
+    hidden_out: bf16 [C*K][d] receives the sampled rows' final residual."""
     lib = load()
     dm = model["dims"]
     C, K = dims["C"], dims["K"]
@@ -292,15 +306,45 @@ def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block
     ms = model.get("_struct")
     if ms is None:
         ms = model["_struct"] = _model_struct(model)
-    bs = _batch_struct(batch, dims, dev)
+    T_out = dims["T_in"] + C * (K - 1)
+    if hidden_d is not None:
+        batch = dict(batch)
+        batch.setdefault("hidden", None)
+    bs = _batch_struct(batch, dims, dev, hidden_optional=hidden_d is not None)
     d = _dims_struct(dims)
     bt = _dev(block_table, "block_table", (torch.int32,), C * dims["max_blocks"], dev)
     kv = _dev(kv_cache, "kv_cache", _BF16, kv_cache_elems(dm, dims["num_blocks"]), dev)
     di = _dev(draft_ids, "draft_ids", (torch.int32,), C * K, dev)
     lg = _dev(logits, "logits", (torch.float32,), C * K * dm.V, dev) if logits is not None else None
-    _check(lib.pd_draft_forward(ctypes.byref(handle.ptr), ctypes.byref(ms), ctypes.byref(d),
-                                ctypes.byref(bs), c_void_p(bt), c_void_p(kv), c_void_p(di),
-                                c_void_p(lg), c_void_p(_stream_ptr(stream))), "pd_draft_forward")
+    args = (ctypes.byref(handle.ptr), ctypes.byref(ms), ctypes.byref(d), ctypes.byref(bs), c_void_p(bt),
+            c_void_p(kv), c_void_p(di), c_void_p(lg))
+    if hidden_d is None and hidden_out is None:
+        _check(lib.pd_draft_forward(*args, c_void_p(_stream_ptr(stream))), "pd_draft_forward")
+        return
+    opts = ForwardOpts(
+        _dev(hidden_d, "hidden_d", _BF16, T_out * dm.d, dev) if hidden_d is not None else None,
+        _dev(hidden_out, "hidden_out", _BF16, C * K * dm.d, dev) if hidden_out is not None else None)
+    _check(lib.pd_draft_forward_ex(*args, ctypes.byref(opts), c_void_p(_stream_ptr(stream))),
+           "pd_draft_forward_ex")
+
+
+def pd_ar_advance(dims_prev: dict, prev: dict, draft_ids, block_table, nxt: dict, stream=None) -> None:
+    """Enqueue the next autoregressive pass's batch (include/pd.h: pd_ar_advance).
+    `nxt` is a batch allocated for {C, K = 1, T_in = C}; its hidden rows are
+    not written."""
+    lib = load()
+    C, K = dims_prev["C"], dims_prev["K"]
+    if C == 0:
+        return
+    dev = prev["input_ids"].device
+    pb = _batch_struct(prev, dims_prev, dev, hidden_optional=True)
+    nd = dict(dims_prev, K=1, T_in=C)
+    nb = _batch_struct(dict(nxt, hidden=None), nd, dev, hidden_optional=True)
+    d = _dims_struct(dims_prev)
+    di = _dev(draft_ids, "draft_ids", (torch.int32,), C * K, dev)
+    bt = _dev(block_table, "block_table", (torch.int32,), C * dims_prev["max_blocks"], dev)
+    _check(lib.pd_ar_advance(ctypes.byref(d), ctypes.byref(pb), c_void_p(di), c_void_p(bt), ctypes.byref(nb),
+                             c_void_p(_stream_ptr(stream))), "pd_ar_advance")
 
 
 def pd_free(handle: Handle) -> None:

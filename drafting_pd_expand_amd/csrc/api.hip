@@ -176,10 +176,10 @@ bool model_ok(const pd_model* m) {
     return true;
 }
 
-bool batch_ok(const pd_batch* b) {
+bool batch_ok(const pd_batch* b, bool hidden_optional = false) {
     return b && b->input_ids && b->positions && b->slot_mapping && b->is_rejected &&
            b->is_masked && b->hidden_state_mapping && b->new_token_indices && b->cu_out &&
-           b->seq_lens && b->hidden;
+           b->seq_lens && (b->hidden || hidden_optional);
 }
 
 }  // namespace
@@ -212,7 +212,18 @@ int pd_expand_batch(const pd_batch_dims* dims, const pd_expand_in* in, const pd_
 int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
                      const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
                      int32_t* draft_ids, float* logits, void* stream) {
-    if (!hp || !model_ok(m) || !dims_ok(dims) || !batch_ok(b)) return PD_EINVAL;
+    return pd_draft_forward_ex(hp, m, dims, b, block_table, kv_cache, draft_ids, logits, nullptr,
+                               stream);
+}
+
+int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
+                        const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
+                        int32_t* draft_ids, float* logits, const pd_forward_opts* opts,
+                        void* stream) {
+    const uint16_t* hidden_d = opts ? opts->hidden_d : nullptr;
+    uint16_t* hidden_out = opts ? opts->hidden_out : nullptr;
+    if (!hp || !model_ok(m) || !dims_ok(dims) || !batch_ok(b, hidden_d != nullptr)) return PD_EINVAL;
+    if (((uintptr_t)hidden_d | (uintptr_t)hidden_out) & 15) return PD_EINVAL;
     if (dims->C == 0) return PD_OK;
     if (dims->block_size != PD_PAGE || dims->hidden3 != m->hidden3) return PD_EINVAL;
     if (!block_table || !kv_cache || !draft_ids) return PD_EINVAL;
@@ -281,13 +292,15 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
         PD_TRY(launch_attn_plan(aa, s));
     }
 
-    // fc projection 3d -> d (starts the residual stream), then the layer-0 input
-    PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr, T, d,
-                m->hidden3, nullptr, 0, &sp));
+    // fc projection 3d -> d (starts the residual stream; skipped when the
+    // projected rows are given), then the layer-0 input
+    if (!hidden_d)
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr, T,
+                    d, m->hidden3, nullptr, 0, &sp));
     {
         Timed t(h, PD_KERNEL_OTHER, s);
-        PD_TRY(launch_layer0_input(ws, sp, b->input_ids, m->embed, m->V, x, m->norm_emb, m->norm_hid,
-                                   u, T, d, m->rms_eps, st, s));
+        PD_TRY(launch_layer0_input(hidden_d, ws, sp, b->input_ids, m->embed, m->V, x, m->norm_emb,
+                                   m->norm_hid, u, T, d, m->rms_eps, st, s));
     }
     PD_TRY(dbg(0));
     for (int l = 0; l < m->N; ++l) {
@@ -303,10 +316,12 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
         }
         aa.q = q; aa.kplane = kpl; aa.vplane = vpl;
         {
-            hipEvent_t e0 = nullptr, e1 = nullptr;
+            hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr, e3 = nullptr;
             if (h->prof & (1 << PD_KERNEL_ATTN)) { e0 = take_event(h); e1 = take_event(h); }
-            rc = launch_attention(m->dh, aa, s, e0, e1);
+            if (h->prof & (1 << PD_KERNEL_OTHER)) { e2 = take_event(h); e3 = take_event(h); }
+            rc = launch_attention(m->dh, aa, s, e0, e1, e2, e3);
             if (e0 && e1) h->ev[PD_KERNEL_ATTN].emplace_back(e0, e1);
+            if (e2 && e3) h->ev[PD_KERNEL_OTHER].emplace_back(e2, e3);
             if (rc != PD_OK) return rc;
         }
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, ao, hd, nullptr, 0, m->w_o[l], nullptr, T, d, hd,
@@ -330,7 +345,7 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
             } else {
                 // final norm of the K sampled rows of every request, packed for the LM head
                 PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, xg, T, d, m->rms_eps, s,
-                                         b->new_token_indices, R, st));
+                                         b->new_token_indices, R, st, hidden_out));
             }
         }
         PD_TRY(dbg(l + 1));
@@ -338,7 +353,7 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     if (h->dbg) {
         Timed t(h, PD_KERNEL_OTHER, s);
         PD_TRY(launch_resid_norm(nullptr, 0, x, m->norm_final, xg, T, d, m->rms_eps, s,
-                                 b->new_token_indices, R, st));
+                                 b->new_token_indices, R, st, hidden_out));
     }
     // LM head on the packed sampled rows, greedy argmax
     PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, xg, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
@@ -350,6 +365,18 @@ int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dim
     }
 #undef PD_TRY
     return PD_OK;
+}
+
+int pd_ar_advance(const pd_batch_dims* dims_prev, const pd_batch* prev, const int32_t* draft_ids,
+                  const int32_t* block_table, const pd_batch* next, void* stream) {
+    if (!dims_ok(dims_prev) || !prev || !next || !draft_ids || !block_table) return PD_EINVAL;
+    if (dims_prev->C == 0) return PD_OK;
+    if (!prev->positions || !prev->new_token_indices) return PD_EINVAL;
+    if (!next->input_ids || !next->positions || !next->slot_mapping || !next->is_rejected ||
+        !next->is_masked || !next->hidden_state_mapping || !next->new_token_indices ||
+        !next->cu_out || !next->seq_lens)
+        return PD_EINVAL;
+    return launch_ar_advance(*dims_prev, *prev, draft_ids, block_table, *next, (hipStream_t)stream);
 }
 
 void pd_free(pd_handle* h) {

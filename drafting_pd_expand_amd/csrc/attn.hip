@@ -494,14 +494,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 }
 
 template <int DH>
-int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1, hipEvent_t e2,
+              hipEvent_t e3) {
     constexpr int NW = AttnCfg<DH>::NW;
     if (e0) (void)hipEventRecord(e0, s);
     hipLaunchKernelGGL(attn_split_kernel<DH>, dim3((unsigned)a.sp.max_units * a.Hkv), dim3(64 * NW), 0,
                        s, a);
     if (e1) (void)hipEventRecord(e1, s);
     if (hipGetLastError() != hipSuccess) return PD_EHIP;
+    if (e2) (void)hipEventRecord(e2, s);
     hipLaunchKernelGGL(attn_merge_kernel<DH>, dim3((a.T * a.Hq + 3) / 4), dim3(256), 0, s, a);
+    if (e3) (void)hipEventRecord(e3, s);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
@@ -536,10 +539,10 @@ int launch_attn_plan(const AttnArgs& a, hipStream_t s) {
 }
 
 int launch_attention(int dh, const AttnArgs& a, hipStream_t s, hipEvent_t split_begin,
-                     hipEvent_t split_end) {
+                     hipEvent_t split_end, hipEvent_t merge_begin, hipEvent_t merge_end) {
     if (a.C <= 0 || a.T <= 0) return PD_OK;
-    if (dh == 64) return launch_dh<64>(a, s, split_begin, split_end);
-    if (dh == 128) return launch_dh<128>(a, s, split_begin, split_end);
+    if (dh == 64) return launch_dh<64>(a, s, split_begin, split_end, merge_begin, merge_end);
+    if (dh == 128) return launch_dh<128>(a, s, split_begin, split_end, merge_begin, merge_end);
     return PD_EINVAL;
 }
 

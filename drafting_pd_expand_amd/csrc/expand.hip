@@ -180,7 +180,69 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
     }
 }
 
+// Next pass of autoregressive (EAGLE-style) drafting, one row per request
+// ([Blog] "background and motivation": K serial drafter passes): the token
+// the previous pass sampled at its last sampled row, at that row's position
+// + 1, with its slot through the block table. One thread per request.
+struct AdvanceArgs {
+    pd_batch_dims d;   // the previous pass's sizes
+    pd_batch prev;
+    const int32_t* draft;
+    const int32_t* bt;
+    pd_batch next;
+};
+
+__global__ __launch_bounds__(256) void ar_advance_kernel(AdvanceArgs a) {
+    const int C = a.d.C, K = a.d.K;
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r > C) return;
+    if (r == C) {
+        a.next.cu_out[C] = C;
+        return;
+    }
+    int32_t* status = a.next.status;
+    const int T_prev = a.d.T_in + C * (K - 1);
+    const int i = r * K + K - 1;
+    const int row = a.prev.new_token_indices[i];
+    int pos = -1, slot = -1;
+    if (row < 0 || row >= T_prev) {
+        flag(status, PD_STATUS_BAD_ROW);
+    } else {
+        pos = a.prev.positions[row] + 1;
+        const int bs = a.d.block_size;
+        if (pos < 1 || pos / bs >= a.d.max_blocks) {
+            flag(status, PD_STATUS_BAD_POSITION);
+            pos = -1;
+        } else {
+            const int page = a.bt[(size_t)r * a.d.max_blocks + pos / bs];
+            if (page < 0 || page >= a.d.num_blocks) flag(status, PD_STATUS_BAD_PAGE);
+            else slot = page * bs + pos % bs;
+        }
+    }
+    a.next.input_ids[r] = a.draft[i];
+    a.next.positions[r] = pos < 0 ? 0 : pos;
+    a.next.slot_mapping[r] = slot;
+    a.next.is_rejected[r] = pos < 0 ? 1 : 0;   // an unusable row is computed as rejected
+    a.next.is_masked[r] = 0;
+    a.next.new_token_indices[r] = r;
+    a.next.hidden_state_mapping[r] = r;
+    a.next.cu_out[r] = r;
+    a.next.seq_lens[r] = pos < 0 ? 1 : pos + 1;
+}
+
 }  // namespace
+
+int launch_ar_advance(const pd_batch_dims& d, const pd_batch& prev, const int32_t* draft_ids,
+                      const int32_t* block_table, const pd_batch& next, hipStream_t s) {
+    AdvanceArgs a;
+    a.d = d;
+    a.prev = prev;
+    a.draft = draft_ids;
+    a.bt = block_table;
+    a.next = next;
+    hipLaunchKernelGGL(ar_advance_kernel, dim3((d.C + 1 + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
 
 int launch_expand(const pd_batch_dims& d, const pd_expand_in& in, const pd_batch& out,
                   hipStream_t s) {

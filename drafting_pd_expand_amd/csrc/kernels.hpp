@@ -11,6 +11,8 @@ namespace pd {
 // ---------------------------------------------------------------- expansion
 int launch_expand(const pd_batch_dims& d, const pd_expand_in& in, const pd_batch& out,
                   hipStream_t s);
+int launch_ar_advance(const pd_batch_dims& d, const pd_batch& prev, const int32_t* draft_ids,
+                      const int32_t* block_table, const pd_batch& next, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM
 enum Epi : int {
@@ -58,13 +60,16 @@ int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 // ---------------------------------------------------------------- row kernels
 // Every consumer of a projection sums its fp32 partial planes
 // (ws[s][T][width], s < S) in split order.
-int launch_layer0_input(const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
-                        float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
-                        int d, float eps, int32_t* status, hipStream_t s);
-// rows != nullptr: output row o = norm of row rows[o] (o < nrows), x untouched.
+// xin != nullptr: the projected hidden rows given directly (bf16 [T][d]); ws / S unused.
+int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32_t* ids,
+                        const uint16_t* embed, int V, float* x, const uint16_t* g_emb,
+                        const uint16_t* g_hid, uint16_t* u, int T, int d, float eps,
+                        int32_t* status, hipStream_t s);
+// rows != nullptr: output row o = norm of row rows[o] (o < nrows), x untouched;
+// xout (row-list mode) also gets the bf16 residual row itself.
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
                       int d, float eps, hipStream_t s, const int32_t* rows = nullptr, int nrows = 0,
-                      int32_t* status = nullptr);
+                      int32_t* status = nullptr, uint16_t* xout = nullptr);
 int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
                       int Hq, int Hkv, int dh, float theta, uint16_t* q_out, uint16_t* kplane,
                       uint16_t* vplane, int num_blocks, int32_t* status, hipStream_t s);
@@ -114,7 +119,9 @@ struct AttnArgs {
 
 // Once per forward (the plan only depends on cu_out / seq_lens).
 int launch_attn_plan(const AttnArgs& a, hipStream_t s);
+// Optional events around the split kernel and around the merge kernel.
 int launch_attention(int dh, const AttnArgs& a, hipStream_t s, hipEvent_t split_begin,
-                     hipEvent_t split_end);
+                     hipEvent_t split_end, hipEvent_t merge_begin = nullptr,
+                     hipEvent_t merge_end = nullptr);
 
 }  // namespace pd

@@ -60,11 +60,13 @@ __device__ __forceinline__ void load_row_sum(float4 (&v)[NC], const float* xr, c
 // y = bf16(gamma * x / sqrt(mean(x^2) + eps)). With a row list, output row o
 // is the norm of row rows[o] (the rows the LM head samples, packed) and x is
 // left as it is; a list entry outside [0, T) is flagged and gives a zero row.
+// xout (row-list mode): also the row's residual itself, bf16 (the drafter's
+// final hidden state, fed back by autoregressive passes).
 template <int NC>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int S, float* x,
                                                          const uint16_t* gamma, uint16_t* y, int T,
                                                          int d, float eps, const int32_t* rows,
-                                                         int32_t* status) {
+                                                         int32_t* status, uint16_t* xout) {
     __shared__ float red[4];
     const int o = blockIdx.x;
     int i = o;
@@ -88,6 +90,9 @@ __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int S,
         if (c < d) {
             gb[n] = *reinterpret_cast<const uint2*>(gamma + c);
             if (S > 0 && !rows) *reinterpret_cast<float4*>(xr + c) = v[n];
+            if (xout)   // the row's residual itself (bf16), before the norm
+                *reinterpret_cast<uint2*>(xout + (size_t)o * d + c) =
+                    pack4(ok ? v[n].x : 0.f, ok ? v[n].y : 0.f, ok ? v[n].z : 0.f, ok ? v[n].w : 0.f);
             ss += v[n].x * v[n].x + v[n].y * v[n].y + v[n].z * v[n].z + v[n].w * v[n].w;
         }
     }
@@ -111,7 +116,8 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int 
                                                            const uint16_t* embed, int V, float* x,
                                                            const uint16_t* g_emb,
                                                            const uint16_t* g_hid, uint16_t* u, int T,
-                                                           int d, float eps, int32_t* status) {
+                                                           int d, float eps, int32_t* status,
+                                                           const uint16_t* xin) {
     __shared__ float red[4];
     const int o = blockIdx.x;
     int id = ids[o];
@@ -132,7 +138,19 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int 
             gh[n] = *reinterpret_cast<const uint2*>(g_hid + c);
         }
     }
-    load_row_sum<NC>(v, xr, ws, S, (size_t)T * d, (size_t)o * d, d, false);
+    if (xin) {   // the projected hidden row given directly (bf16, d wide)
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const int c = threadIdx.x * 4 + 1024 * n;
+            v[n] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < d) {
+                const uint2 hb = *reinterpret_cast<const uint2*>(xin + (size_t)o * d + c);
+                v[n] = make_float4(bf2f(hb.x & 0xffff), bf2f(hb.x >> 16), bf2f(hb.y & 0xffff), bf2f(hb.y >> 16));
+            }
+        }
+    } else {
+        load_row_sum<NC>(v, xr, ws, S, (size_t)T * d, (size_t)o * d, d, false);
+    }
     float se = 0.f, sx = 0.f;
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
@@ -285,24 +303,25 @@ __global__ __launch_bounds__(1024) void argmax_reduce_kernel(const float* amax_v
     }
 
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
-                      int d, float eps, hipStream_t s, const int32_t* rows, int nrows, int32_t* status) {
+                      int d, float eps, hipStream_t s, const int32_t* rows, int nrows, int32_t* status,
+                      uint16_t* xout) {
     const int nout = rows ? nrows : T;
     if (nout <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
 #define L_(NC) hipLaunchKernelGGL(resid_norm_kernel<NC>, dim3(nout), dim3(256), 0, s, ws, S, x, gamma, y, T, d, \
-                                  eps, rows, status)
+                                  eps, rows, status, xout)
     PD_ROW_NC(d, L_)
 #undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
-int launch_layer0_input(const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
+int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
                         float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
                         int d, float eps, int32_t* status, hipStream_t s) {
     if (T <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
 #define L_(NC) hipLaunchKernelGGL(layer0_input_kernel<NC>, dim3(T), dim3(256), 0, s, ws, S, ids, embed, V, \
-                                  x, g_emb, g_hid, u, T, d, eps, status)
+                                  x, g_emb, g_hid, u, T, d, eps, status, xin)
     PD_ROW_NC(d, L_)
 #undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;

@@ -200,6 +200,51 @@ int pd_draft_forward(pd_handle** h, const pd_model* m, const pd_batch_dims* dims
  * work to finish). Never frees caller memory. */
 void pd_free(pd_handle* h);
 
+/* ---- autoregressive baseline ------------------------------------------------
+ *
+ * [Blog] "background and motivation": autoregressive EAGLE drafts K tokens
+ * with K serial drafter passes, which parallel drafting replaces by one pass.
+ * [Blog] "P-EAGLE core method" / [arXiv] Figure 2 caption: the NTP position
+ * works exactly like the autoregressive case. These two calls run that
+ * baseline on the same kernels: pass 1 = pd_expand_batch with K = 1 +
+ * pd_draft_forward_ex; pass k >= 2 = pd_ar_advance + pd_draft_forward_ex on
+ * one row per request whose hidden input is the drafter's own final hidden
+ * state of the previous pass (d wide, so fc is skipped). The pages leave that
+ * fed-back state open; this is the reading taken.
+ */
+
+/* Options of pd_draft_forward_ex. [host] struct, [dev] pointers. */
+typedef struct {
+    const uint16_t* hidden_d;   /* bf16 [T_out][d]: every row's projected hidden input given
+                                   directly (fc is skipped, batch->hidden is not read and may be
+                                   NULL), or NULL for fc(batch->hidden)                        */
+    uint16_t*       hidden_out; /* bf16 [C*K][d] out: the final residual (before the final norm)
+                                   of every sampled row, request-major, or NULL                */
+} pd_forward_opts;
+
+/* pd_draft_forward with options (opts NULL = pd_draft_forward). Same
+ * arguments, ownership and errors; hidden_d / hidden_out must be 16-byte
+ * aligned. */
+int pd_draft_forward_ex(pd_handle** h, const pd_model* m, const pd_batch_dims* dims,
+                        const pd_batch* batch, const int32_t* block_table,
+                        uint16_t* kv_cache, int32_t* draft_ids, float* logits,
+                        const pd_forward_opts* opts, void* stream);
+
+/* Build the next autoregressive pass's batch, one row per request, from the
+ * previous pass (dims_prev: its C, K, T_in and the block table sizes; prev:
+ * its batch; draft_ids [dev] [C*K]: the tokens it sampled). Row r of `next`
+ * is request r: input_ids = the token sampled at the previous pass's last
+ * sampled row, positions = that row's position + 1, slot_mapping through
+ * block_table (-1 and PD_STATUS_BAD_POSITION / _BAD_PAGE if outside it),
+ * is_rejected = is_masked = 0, new_token_indices = hidden_state_mapping = r,
+ * cu_out = 0..C, seq_lens = position + 1. next->hidden is not written (the
+ * next pass reads pd_forward_opts.hidden_d). The next pass's dims are
+ * {C, K = 1, T_in = C}. Errors: PD_EINVAL for bad dims or NULL pointers,
+ * PD_EHIP; a bad new-token index of `prev` sets PD_STATUS_BAD_ROW in
+ * next->status (if given) and gives a row with slot -1. */
+int pd_ar_advance(const pd_batch_dims* dims_prev, const pd_batch* prev, const int32_t* draft_ids,
+                  const int32_t* block_table, const pd_batch* next, void* stream);
+
 /* ---- extras ---------------------------------------------------------------- */
 
 /* Text for a PD_* return code. */
@@ -218,7 +263,7 @@ int pd_set_debug_resid(pd_handle* h, float* dst);
 #define PD_KERNEL_LMHEAD  0   /* LM-head GEMM with the fused argmax partials     */
 #define PD_KERNEL_GEMM    1   /* every other GEMM (fc, QKV, O, gate/up, down)    */
 #define PD_KERNEL_ATTN    2   /* split-KV paged attention (not the merge)         */
-#define PD_KERNEL_OTHER   3   /* norms, RoPE+cache, merge, argmax reduce          */
+#define PD_KERNEL_OTHER   3   /* norms, RoPE+cache, split plan, merge, argmax reduce */
 #define PD_KERNEL_CLASSES 4
 /* class_mask != 0 starts recording an event pair around every launch of the
  * kernel classes whose bit (1 << PD_KERNEL_*) is set, for later

@@ -193,7 +193,7 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
 
 
 def ar_draft(model: dict, exp1: dict, block_table, kv: dict, K: int, block_size: int = 16,
-             tokens=None) -> list:
+             tokens=None, hidden=None) -> list:
     """Autoregressive EAGLE-style drafting of K tokens per request: K serial
     drafter passes ([Blog] "background and motivation"), the baseline that
     parallel drafting replaces.
@@ -207,6 +207,10 @@ def ar_draft(model: dict, exp1: dict, block_table, kv: dict, K: int, block_size:
     tokens: optional [K][C] tokens to feed forward instead of this function's
     own argmax (a caller comparing against another implementation feeds its
     choices so both take the same path through near-ties).
+    hidden: optional [K-1][C][d] fed-back hidden states to use instead of this
+    function's own ``hidden_out`` (so such a caller can hold each pass to a
+    single pass's error budget instead of letting the fed state's error
+    compound over the passes).
     Returns the K pass results of ``draft_forward`` (logits, draft_ids,
     hidden_out, ...) and the batches they ran on ("batch").
     """
@@ -226,7 +230,7 @@ def ar_draft(model: dict, exp1: dict, block_table, kv: dict, K: int, block_size:
         ids = res["draft_ids"] if tokens is None else np.asarray(tokens[k])
         nxt = _ar_advance(batch, 1, ids, block_table, block_size)
         C = len(nxt["cu_out"]) - 1
-        nxt["hidden_d"] = res["hidden_out"]
+        nxt["hidden_d"] = res["hidden_out"] if hidden is None else np.asarray(hidden[k], np.float64)
         nxt["use_hidden_d"] = np.ones(C, bool)
         batch = nxt
     return out

@@ -158,3 +158,24 @@ def test_binding_rejects_host_tensors(lib):
     inp["h_shared"] = torch.zeros(16, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pdx.pd_expand_batch(dims, inp, {})
+
+
+def test_forward_ex_and_ar_advance_reject_bad_calls(lib):
+    h = ctypes.c_void_p(None)
+    m, b = _model(), _fake_batch()
+    d = _dims(hidden3=768)
+    opts = pdx.ForwardOpts(FAKE + 8, None)   # misaligned hidden_d
+    assert lib.pd_draft_forward_ex(ctypes.byref(h), ctypes.byref(m), ctypes.byref(d), ctypes.byref(b),
+                                   FAKE, FAKE, FAKE, None, ctypes.byref(opts), None) == pdx.PD_EINVAL
+    b2 = _fake_batch()
+    b2.hidden = None                          # no 3d rows: only allowed with hidden_d
+    assert lib.pd_draft_forward_ex(ctypes.byref(h), ctypes.byref(m), ctypes.byref(d), ctypes.byref(b2),
+                                   FAKE, FAKE, FAKE, None, None, None) == pdx.PD_EINVAL
+    assert h.value is None
+    assert lib.pd_ar_advance(ctypes.byref(d), ctypes.byref(b), None, FAKE, ctypes.byref(b), None) == pdx.PD_EINVAL
+    assert lib.pd_ar_advance(ctypes.byref(d), None, FAKE, FAKE, ctypes.byref(b), None) == pdx.PD_EINVAL
+    b3 = _fake_batch()
+    b3.seq_lens = None
+    assert lib.pd_ar_advance(ctypes.byref(d), ctypes.byref(b), FAKE, FAKE, ctypes.byref(b3), None) == pdx.PD_EINVAL
+    assert lib.pd_ar_advance(ctypes.byref(_dims(C=0, T_in=0)), ctypes.byref(b), FAKE, FAKE,
+                             ctypes.byref(b), None) == 0

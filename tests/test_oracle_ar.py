@@ -106,6 +106,15 @@ def test_forced_tokens_equal_own_choice():
                              tokens=[p["draft_ids"] for p in own[:-1]])
     for a, b in zip(own, forced):
         assert np.array_equal(a["logits"], b["logits"])
+    # feeding the run's own hidden states back reproduces it too; other states change the later passes
+    fed = oracle.ar_draft(model, exp1, args["block_table"], pool, K, block_size=bs,
+                          hidden=[p["hidden_out"] for p in own[:-1]])
+    for a, b in zip(own, fed):
+        assert np.array_equal(a["logits"], b["logits"])
+    alt = oracle.ar_draft(model, exp1, args["block_table"], pool, K, block_size=bs,
+                          hidden=[0.5 * p["hidden_out"] for p in own[:-1]])
+    assert np.array_equal(alt[0]["logits"], own[0]["logits"])
+    assert not np.allclose(alt[1]["logits"], own[1]["logits"])
     # pass k >= 2 rows sit right after the previous pass's sampled row, one row per request
     for k in range(1, K):
         bk = own[k]["batch"]
