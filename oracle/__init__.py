@@ -12,6 +12,10 @@ Plain, slow, float64 NumPy definitions of what the drafting step computes:
                          (one row per request, fed back token and hidden), and
   * ``ar_draft``      -- K such serial passes: the baseline that parallel
                          drafting replaces.
+  * ``seq_partition`` -- the training-side sequence partitioning: every kept
+                         (depth, position) of a long sequence assigned to a
+                         segment with its dependencies, plus each segment's
+                         causal-completion context.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package. The product path (the HIP library and
@@ -35,5 +39,7 @@ printed values on the pages: beyond those pins they are "parity unpinned".
 from .expand import expand, ar_advance
 from .forward import draft_forward, ar_draft, rope_rotate, rms_norm, silu
 from .bf16 import bf16_to_f64
+from .partition import seq_partition, equal_boundaries
 
-__all__ = ["expand", "ar_advance", "draft_forward", "ar_draft", "rope_rotate", "rms_norm", "silu", "bf16_to_f64"]
+__all__ = ["expand", "ar_advance", "draft_forward", "ar_draft", "rope_rotate", "rms_norm", "silu", "bf16_to_f64",
+           "seq_partition", "equal_boundaries"]

@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "ModelDims", "Workload", "WORKLOADS", "MODELS", "get_workload",
-    "make_model", "make_batch", "make_kv_pool", "f32_to_bf16_bits",
+    "make_model", "make_batch", "make_kv_pool", "make_cod_keep", "f32_to_bf16_bits",
 ]
 
 _CHUNK = 1 << 22
@@ -253,3 +253,26 @@ def make_kv_pool(m: ModelDims, num_blocks: int, seed: int, block_size: int = 16)
     shape = (m.N, num_blocks * block_size, m.Hkv, m.dh)
     return {"k": _fill(shape, seed, 21, "normal", 1.0),
             "v": _fill(shape, seed, 22, "normal", 1.0)}
+
+
+def make_cod_keep(B: int, n: int, K: int, r: float, seed: int, lengths=None) -> np.ndarray:
+    """Kept-position masks of B training sequences, uint8 [B][K][n] (1 = kept).
+
+    Stand-in for COD sampling's output ([Paper] sec. 3 challenge analysis:
+    deeper depths keep positions with geometric decay r): depth 0 keeps every
+    position below the sequence's length; position p is kept at depth d >= 1
+    with probability r, and only if position p-1 is kept at depth d-1, so
+    depth d keeps about r^d of the positions and every kept position's
+    dependency is kept. At n = 8192, K = 8, r = 0.8 that is about
+    8192 * (1 - 0.8^8) / 0.2 = 34,080 positions, the pages' ~34K.
+    lengths: optional [B] sequence lengths <= n (positions past them are
+    padding, never kept); default n.
+    """
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 31]))
+    u = rng.random((B, K, n), dtype=np.float32)
+    L = np.full(B, n) if lengths is None else np.asarray(lengths)
+    keep = np.zeros((B, K, n), dtype=bool)
+    keep[:, 0, :] = np.arange(n)[None, :] < L[:, None]
+    for d in range(1, K):
+        keep[:, d, 1:] = keep[:, d - 1, :-1] & (u[:, d, 1:] < r)
+    return keep.astype(np.uint8)

@@ -30,8 +30,18 @@ MUTATIONS = [
     ("expand.py", "new_idx[r * K] = out_start + v - 1", "new_idx[r * K] = out_start + v"),     # NTP index
     ("forward.py", 'kvf["k"][l][sl] = kk', "pass"),                                           # AR: no KV carry-over
     ("expand.py", "pos_prev[new_idx[i]] + 1 for i in last", "pos_prev[new_idx[i]] + 2 for i in last"),  # AR position
-    ("forward.py", 'nxt["hidden_d"] = res["hidden_out"]', 'nxt["hidden_d"] = 0 * res["hidden_out"]'),  # AR feedback
+    ("forward.py", 'nxt["hidden_d"] = res["hidden_out"] if', 'nxt["hidden_d"] = 0 * res["hidden_out"] if'),  # AR feedback
+    ("partition.py", "seg[d][p] = dep", "seg[d][p] = _segment_of_index(b, p)"),             # deeper depths by index
+    ("partition.py", "dep = seg[d - 1][p - 1] if", "dep = seg[d - 1][p] if"),                  # wrong dependency
+    ("partition.py", "for p in range(b[s]) if keep[0][p]", "for p in range(b[s] - 1) if keep[0][p]"),  # context short
+    ("partition.py", "seg[1][p] = _segment_of_index(b, p)", "seg[1][p] = _segment_of_index(b, p - 1)"),  # depth 1 index
+    ("partition.py", "            else:\n                bad = True\n    owned", "            else:\n                pass\n    owned"),  # broken chain unreported
 ]
+
+PIN_FILES = {
+    "partition.py": ["tests/test_oracle_partition.py"],
+}
+DEFAULT_PINS = ["tests/test_oracle_expand.py", "tests/test_oracle_forward.py", "tests/test_oracle_ar.py"]
 
 
 @pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[m[2][:24] for m in MUTATIONS])
@@ -44,7 +54,6 @@ def test_planted_mistake_is_caught(tmp_path, fname, old, new):
     (dst / fname).write_text(src.replace(old, new))
     env = dict(os.environ, PD_ORACLE_MUTANT_DIR=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_expand.py", "tests/test_oracle_forward.py",
-                        "tests/test_oracle_ar.py"],
+                        *PIN_FILES.get(fname, DEFAULT_PINS)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, "the oracle pins did not catch: " + new + "\n" + r.stdout[-2000:]
