@@ -207,6 +207,45 @@ def ar_baseline(pdx, mdev, b, w, inp, cache, par_draft, stream, steps: int) -> d
             "passes": K, "steps_timed": n, "pass1_equals_parallel_ntp_frac": agree}
 
 
+def partition_leg(pdx, stream, reps: int = 20) -> dict:
+    """Sequence partitioning ([Paper] sec. 3.2) on a training batch: 256
+    sequences of 8192 tokens, K = 8 depths kept with COD decay r = 0.8 (the
+    pages' 8192 / K = 8 / r = 0.8 example, ~34K positions each), 4 segments.
+    HBM-bound: algorithmic bytes = keep bytes read + segment ids written +
+    row lists written + boundaries and offsets."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    B, n, K, S = 256, 8192, 8, 4
+    keep_np = synth.make_cod_keep(B, n, K, 0.8, 7)
+    placed = int(keep_np.sum())
+    keep = torch.from_numpy(keep_np).to(dev)
+    bnd = torch.tensor([[(s * n) // S for s in range(S + 1)]] * B, dtype=torch.int32, device=dev)
+    seg = torch.empty((B, K, n), dtype=torch.int32, device=dev)
+    off = torch.empty((B, S + 1), dtype=torch.int32, device=dev)
+    rows = torch.empty((B, K * n), dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pdx.pd_seq_partition(keep, bnd, seg, off, rows, st, stream)
+    torch.cuda.synchronize()
+    if int(st.item()) != 0 or int(off[:, S].sum().item()) != placed:
+        raise SystemExit("sequence partitioning: unexpected status or row count")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        pdx.pd_seq_partition(keep, bnd, seg, off, rows, st, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    alg = B * K * n + 4 * B * K * n + 4 * placed + 2 * 4 * B * (S + 1)
+    gbs = alg / (us * 1e-6) / 1e9
+    log(f"[bench] sequence partitioning: {us:.1f} us per call, {gbs:.0f} GB/s algorithmic")
+    return {"workload": f"{B} sequences x {n} tokens, K={K}, COD r=0.8, S={S} ({placed} positions)",
+            "us_per_call": us, "positions_per_s": placed / (us * 1e-6),
+            "roofline": {"bound": "hbm", "kernel": "seq_partition_kernel", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "bytes_per_call": alg}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +385,7 @@ def main():
 
     ar = ar_baseline(pdx, mdev, b, w, inp, cache, draft, stream, args.steps)
     ar["parallel_speedup"] = ar["ms_per_step"] / ms_step
+    part = partition_leg(pdx, stream)
 
     R = b["C"] * w.K
     if dom == "lm_head":
@@ -400,6 +440,7 @@ def main():
         "kernel_classes_us_per_step": {k: round(v["us_per_step"], 1) for k, v in cls_us.items()},
         "hipgraph": graph,
         "ar_baseline": ar,
+        "seq_partition": part,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

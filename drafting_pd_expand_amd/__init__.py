@@ -31,6 +31,8 @@ PD_OK, PD_EINVAL, PD_ENOMEM, PD_EHIP = 0, -1, -2, -3
 PD_PAGE = 16
 PD_MAX_LAYERS = 16
 KERNEL_LMHEAD, KERNEL_GEMM, KERNEL_ATTN, KERNEL_OTHER = 0, 1, 2, 3
+STATUS_BAD_CHAIN, STATUS_BAD_BOUNDS = 32, 64
+PART_MAX_K, PART_MAX_S, PART_MAX_POS = 16, 256, 1 << 19
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -72,6 +74,10 @@ class ForwardOpts(ctypes.Structure):
     _fields_ = [("hidden_d", c_void_p), ("hidden_out", c_void_p)]
 
 
+class PartitionDims(ctypes.Structure):
+    _fields_ = [("B", c_int32), ("K", c_int32), ("n", c_int32), ("S", c_int32)]
+
+
 class Model(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in ("d", "Hq", "Hkv", "dh", "F", "N", "V", "hidden3")] + [
         ("rms_eps", c_float), ("rope_theta", c_float),
@@ -104,6 +110,9 @@ def load():
     lib.pd_ar_advance.argtypes = [POINTER(BatchDims), POINTER(Batch), c_void_p, c_void_p, POINTER(Batch),
                                   c_void_p]
     lib.pd_ar_advance.restype = c_int
+    lib.pd_seq_partition.argtypes = [POINTER(PartitionDims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p]
+    lib.pd_seq_partition.restype = c_int
     lib.pd_free.argtypes = [c_void_p]
     lib.pd_free.restype = None
     lib.pd_strerror.argtypes = [c_int]
@@ -345,6 +354,33 @@ def pd_ar_advance(dims_prev: dict, prev: dict, draft_ids, block_table, nxt: dict
     bt = _dev(block_table, "block_table", (torch.int32,), C * dims_prev["max_blocks"], dev)
     _check(lib.pd_ar_advance(ctypes.byref(d), ctypes.byref(pb), c_void_p(di), c_void_p(bt), ctypes.byref(nb),
                              c_void_p(_stream_ptr(stream))), "pd_ar_advance")
+
+
+def pd_seq_partition(keep, boundaries, seg, seg_offsets, rows, status=None, stream=None) -> None:
+    """Enqueue the sequence partitioning (include/pd.h: pd_seq_partition).
+    keep: uint8 [B][K][n]; boundaries: int32 [B][S+1]; seg: int32 [B][K][n] out;
+    seg_offsets: int32 [B][S+1] out; rows: int32 [B][K*n] out; status: int32 [1] or None."""
+    lib = load()
+    if keep.dim() != 3 or boundaries.dim() != 2:
+        raise ValueError("keep must be [B][K][n] and boundaries [B][S+1]")
+    B, K, n = (int(x) for x in keep.shape)
+    S = int(boundaries.shape[1]) - 1
+    if boundaries.shape[0] != B:
+        raise ValueError("boundaries must have one row per sequence")
+    dims = PartitionDims(B, K, n, S)
+    if B == 0:
+        _check(lib.pd_seq_partition(ctypes.byref(dims), None, None, None, None, None, None,
+                                    c_void_p(_stream_ptr(stream))), "pd_seq_partition")
+        return
+    dev = keep.device
+    args = (_dev(keep, "keep", (torch.uint8,), B * K * n, dev, 8),
+            _dev(boundaries, "boundaries", (torch.int32,), B * (S + 1), dev),
+            _dev(seg, "seg", (torch.int32,), B * K * n, dev, 16),
+            _dev(seg_offsets, "seg_offsets", (torch.int32,), B * (S + 1), dev),
+            _dev(rows, "rows", (torch.int32,), B * K * n, dev),
+            _dev(status, "status", (torch.int32,), 1, dev) if status is not None else None)
+    _check(lib.pd_seq_partition(ctypes.byref(dims), *[c_void_p(a) for a in args],
+                                c_void_p(_stream_ptr(stream))), "pd_seq_partition")
 
 
 def pd_free(handle: Handle) -> None:

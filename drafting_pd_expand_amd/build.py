@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpdexpand.so")
-SOURCES = ["expand.hip", "gemm.hip", "rows.hip", "attn.hip", "api.hip"]
+SOURCES = ["expand.hip", "gemm.hip", "rows.hip", "attn.hip", "partition.hip", "api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -379,6 +379,22 @@ int pd_ar_advance(const pd_batch_dims* dims_prev, const pd_batch* prev, const in
     return launch_ar_advance(*dims_prev, *prev, draft_ids, block_table, *next, (hipStream_t)stream);
 }
 
+int pd_seq_partition(const pd_partition_dims* dims, const uint8_t* keep, const int32_t* boundaries,
+                     int32_t* seg, int32_t* seg_offsets, int32_t* rows, int32_t* status,
+                     void* stream) {
+    if (!dims) return PD_EINVAL;
+    const pd_partition_dims& d = *dims;
+    if (d.B < 0 || d.K < 1 || d.K > PD_PART_MAX_K || d.S < 1 || d.S > PD_PART_MAX_S || d.n < 8 ||
+        d.n % 8 != 0 || (int64_t)d.K * ((d.n + 63) / 64) * 64 > PD_PART_MAX_POS)
+        return PD_EINVAL;
+    if (d.B == 0) return PD_OK;
+    if (!keep || !boundaries || !seg || !seg_offsets || !rows) return PD_EINVAL;
+    if (((uintptr_t)keep & 7) || ((uintptr_t)seg & 15) || ((uintptr_t)seg_offsets & 3) ||
+        ((uintptr_t)rows & 3) || ((uintptr_t)boundaries & 3) || ((uintptr_t)status & 3))
+        return PD_EINVAL;
+    return launch_seq_partition(d, keep, boundaries, seg, seg_offsets, rows, status, (hipStream_t)stream);
+}
+
 void pd_free(pd_handle* h) {
     if (!h) return;
     (void)hipDeviceSynchronize();

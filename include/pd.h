@@ -52,6 +52,8 @@ extern "C" {
 #define PD_STATUS_BAD_PAGE     4  /* a block-table entry outside [0, num_blocks)            */
 #define PD_STATUS_BAD_TOKEN    8  /* a token id outside [0, V)                              */
 #define PD_STATUS_BAD_ROW     16  /* row bookkeeping (cu_out / new-token index) inconsistent */
+#define PD_STATUS_BAD_CHAIN   32  /* pd_seq_partition: a kept position whose dependency is not placeable */
+#define PD_STATUS_BAD_BOUNDS  64  /* pd_seq_partition: segment boundaries not 0 = b_0 <= ... <= b_S = n */
 
 /* Sizes of one draft step. [host]
  *   C             requests, 0..PD_MAX_C (0 = nothing to do)
@@ -273,6 +275,54 @@ int pd_profile(pd_handle* h, int class_mask);
 /* Wait for the recorded events and return the summed duration (ms) and the
  * launch count of one kernel class since profiling was enabled. */
 int pd_profile_read(pd_handle* h, int kernel_class, double* total_ms, int64_t* launches);
+
+/* ---- sequence partitioning (training side) ----------------------------------
+ *
+ * [Paper] sec. 3.2 "Sequence Partitioning"; [arXiv] Figure 4 caption. A
+ * training sequence of n tokens with K prediction depths holds position p
+ * at depth d if COD sampling kept it; position p at depth d >= 1 depends on
+ * position p-1 at depth d-1. The sequence is cut into S segments trained one
+ * after another: depths 0 and 1 go to the segment their index falls in,
+ * deeper positions go where their dependency went (so every dependency stays
+ * inside one segment), and each segment also carries, as attention context,
+ * the depth-0 positions before its first boundary (causal completion).
+ */
+
+#define PD_PART_MAX_K   16         /* prediction depths                      */
+#define PD_PART_MAX_S   256        /* segments per sequence                  */
+#define PD_PART_MAX_POS (1 << 19)  /* K * (n rounded up to 64) per sequence   */
+
+/* Sizes of one pd_seq_partition call. [host]
+ *   B  sequences (0 = nothing to do); K depths, 1..PD_PART_MAX_K;
+ *   n  positions per sequence (padded length), a multiple of 8,
+ *      K * (n rounded up to a multiple of 64) <= PD_PART_MAX_POS;
+ *   S  segments, 1..PD_PART_MAX_S. */
+typedef struct {
+    int32_t B, K, n, S;
+} pd_partition_dims;
+
+/* Assign every kept position of B sequences to a segment.
+ *   keep        [dev] uint8 [B][K][n], 8-byte aligned: nonzero = position p kept at depth d
+ *               (depth 0 holds the real tokens; padding is 0 at every depth).
+ *   boundaries  [dev] int32 [B][S+1]: 0 = b_0 <= b_1 <= ... <= b_S = n; segment s covers the
+ *               depth-0 indices [b_s, b_{s+1}); empty segments are allowed.
+ *   seg         [dev] int32 [B][K][n] out, 16-byte aligned: the segment of position (d, p), or -1
+ *               if it is not kept or not placeable (a link of its chain down to depth 0 is
+ *               missing).
+ *   seg_offsets [dev] int32 [B][S+1] out: segment s's rows are rows[b][seg_offsets[b][s] ..
+ *               seg_offsets[b][s+1]); seg_offsets[b][S] = placeable positions of sequence b.
+ *   rows        [dev] int32 [B][K*n] out: per sequence, the placeable positions as d * n + p,
+ *               segment by segment, then depth by depth, p ascending. Entries past
+ *               seg_offsets[b][S] are not written. Segment s's context is the depth-0
+ *               positions [0, b_s) (kept ones only), implied and not listed.
+ *   status      [dev] int32 [1] or NULL: PD_STATUS_BAD_CHAIN if a kept position is not
+ *               placeable, PD_STATUS_BAD_BOUNDS for a sequence with bad boundaries (its seg
+ *               is all -1 and its offsets 0).
+ * Errors: PD_EINVAL for bad dims, NULL or misaligned pointers (nothing enqueued); PD_EHIP.
+ * Deterministic; no scratch memory; one workgroup per sequence. */
+int pd_seq_partition(const pd_partition_dims* dims, const uint8_t* keep, const int32_t* boundaries,
+                     int32_t* seg, int32_t* seg_offsets, int32_t* rows, int32_t* status,
+                     void* stream);
 
 #ifdef __cplusplus
 }

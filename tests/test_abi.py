@@ -179,3 +179,21 @@ def test_forward_ex_and_ar_advance_reject_bad_calls(lib):
     assert lib.pd_ar_advance(ctypes.byref(d), ctypes.byref(b), FAKE, FAKE, ctypes.byref(b3), None) == pdx.PD_EINVAL
     assert lib.pd_ar_advance(ctypes.byref(_dims(C=0, T_in=0)), ctypes.byref(b), FAKE, FAKE,
                              ctypes.byref(b), None) == 0
+
+
+def test_seq_partition_rejects_bad_calls(lib):
+    P = pdx.PartitionDims
+
+    def call(d, keep=FAKE, bnd=FAKE, seg=FAKE, off=FAKE, rows=FAKE, st=None):
+        return lib.pd_seq_partition(ctypes.byref(d) if d is not None else None, keep, bnd, seg, off, rows, st, None)
+
+    assert call(None) == pdx.PD_EINVAL
+    for bad in (P(1, 0, 64, 2), P(1, 17, 64, 2), P(1, 4, 60, 2), P(1, 4, 0, 2), P(1, 4, 64, 0),
+                P(1, 4, 64, 257), P(1, 16, 1 << 16, 2), P(-1, 4, 64, 2)):
+        assert call(bad) == pdx.PD_EINVAL, (bad.B, bad.K, bad.n, bad.S)
+    ok = P(1, 4, 64, 2)
+    assert call(ok, keep=None) == pdx.PD_EINVAL
+    assert call(ok, rows=None) == pdx.PD_EINVAL
+    assert call(ok, keep=FAKE + 4) == pdx.PD_EINVAL     # keep must be 8-byte aligned
+    assert call(ok, seg=FAKE + 8) == pdx.PD_EINVAL      # seg must be 16-byte aligned
+    assert call(P(0, 4, 64, 2), keep=None, bnd=None, seg=None, off=None, rows=None) == pdx.PD_OK
