@@ -12,6 +12,9 @@ Plain, slow, float64 NumPy definitions of what the drafting step computes:
                          (one row per request, fed back token and hidden), and
   * ``ar_draft``      -- K such serial passes: the baseline that parallel
                          drafting replaces.
+  * ``verify_stub``, ``draft_rounds`` -- several draft/verify rounds in a
+                         row with a stand-in verifier (accepted counts and
+                         target outputs are inputs), KV carried over.
   * ``seq_partition`` -- the training-side sequence partitioning: every kept
                          (depth, position) of a long sequence assigned to a
                          segment with its dependencies, plus each segment's
@@ -40,6 +43,7 @@ from .expand import expand, ar_advance
 from .forward import draft_forward, ar_draft, rope_rotate, rms_norm, silu
 from .bf16 import bf16_to_f64
 from .partition import seq_partition, equal_boundaries
+from .rounds import verify_stub, draft_rounds
 
 __all__ = ["expand", "ar_advance", "draft_forward", "ar_draft", "rope_rotate", "rms_norm", "silu", "bf16_to_f64",
-           "seq_partition", "equal_boundaries"]
+           "seq_partition", "equal_boundaries", "verify_stub", "draft_rounds"]

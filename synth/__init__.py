@@ -35,7 +35,7 @@ import numpy as np
 
 __all__ = [
     "ModelDims", "Workload", "WORKLOADS", "MODELS", "get_workload",
-    "make_model", "make_batch", "make_kv_pool", "make_cod_keep", "f32_to_bf16_bits",
+    "make_model", "make_batch", "make_kv_pool", "make_cod_keep", "make_rounds", "f32_to_bf16_bits",
 ]
 
 _CHUNK = 1 << 22
@@ -198,11 +198,13 @@ def _context_lengths(w: Workload, rng) -> np.ndarray:
     raise ValueError(w.context)
 
 
-def make_batch(w: Workload, seed: int | None = None, block_size: int = 16) -> dict:
+def make_batch(w: Workload, seed: int | None = None, block_size: int = 16, extra_positions: int = 0) -> dict:
     """The verify-batch side of one draft step (all integer data + target rows).
 
     Returns int32 numpy arrays in the layout the expansion consumes, the
     target hidden rows as bf16 bits, and the page pool description.
+    extra_positions: block-table room for that many more positions per
+    request (later rounds of a multi-round run).
     """
     seed = w.seed if seed is None else seed
     m = w.model
@@ -222,7 +224,7 @@ def make_batch(w: Workload, seed: int | None = None, block_size: int = 16) -> di
     next_ids = rng.integers(0, m.V - 1, size=w.C)
     target_pos = np.concatenate([np.arange(L[r], L[r] + n[r]) for r in range(w.C)]) if w.C else np.zeros(0, np.int64)
     # pages: enough for every position this step can touch
-    pages = [int(-(-(L[r] + n[r] + w.K) // block_size)) for r in range(w.C)]
+    pages = [int(-(-(L[r] + n[r] + w.K + extra_positions) // block_size)) for r in range(w.C)]
     num_blocks = int(sum(pages)) + w.spare_pages
     max_blocks = max(pages) if pages else 1
     perm = rng.permutation(num_blocks)
@@ -276,3 +278,21 @@ def make_cod_keep(B: int, n: int, K: int, r: float, seed: int, lengths=None) -> 
     for d in range(1, K):
         keep[:, d, 1:] = keep[:, d - 1, :-1] & (u[:, d, 1:] < r)
     return keep.astype(np.uint8)
+
+
+def make_rounds(w: Workload, R: int, seed: int | None = None) -> list:
+    """Inputs of rounds 2..R of a multi-round run (the verifier stand-in's
+    draws): per round, accepted-draft counts a_r ~ U{0..K}, the token the
+    target samples after verification (uniform in [0, V-1)) and the target
+    hidden rows of the K+1-token verify windows (~ N(0, 1), bf16 bits)."""
+    seed = w.seed if seed is None else seed
+    m = w.model
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(41,)))
+    out = []
+    for t in range(R - 1):
+        out.append({
+            "accepted": np.ascontiguousarray(rng.integers(0, w.K + 1, size=w.C), dtype=np.int32),
+            "next_token_ids": np.ascontiguousarray(rng.integers(0, m.V - 1, size=w.C), dtype=np.int32),
+            "target_hidden": _fill((w.C * (w.K + 1), m.hidden3), seed * 1000 + t, 43, "normal", 1.0),
+        })
+    return out

@@ -36,10 +36,15 @@ MUTATIONS = [
     ("partition.py", "for p in range(b[s]) if keep[0][p]", "for p in range(b[s] - 1) if keep[0][p]"),  # context short
     ("partition.py", "seg[1][p] = _segment_of_index(b, p)", "seg[1][p] = _segment_of_index(b, p - 1)"),  # depth 1 index
     ("partition.py", "            else:\n                bad = True\n    owned", "            else:\n                pass\n    owned"),  # broken chain unreported
+    ("rounds.py", "p_ntp = int(pos[nti[r * K]])", "p_ntp = int(pos[nti[r * K]]) + 1"),          # window one position late
+    ("rounds.py", "ids.append(int(nxt[r]))", "ids.append(int(d[r, 0]))"),                     # sampled token dropped
+    ("rounds.py", '"num_rejected": (K - a).astype(np.int32)', '"num_rejected": a.astype(np.int32)'),  # rejected count
+    ("rounds.py", 'kvf["k"][l][sl] = kk', "pass"),                                            # no KV carry-over
 ]
 
 PIN_FILES = {
     "partition.py": ["tests/test_oracle_partition.py"],
+    "rounds.py": ["tests/test_oracle_rounds.py"],
 }
 DEFAULT_PINS = ["tests/test_oracle_expand.py", "tests/test_oracle_forward.py", "tests/test_oracle_ar.py"]
 
