@@ -207,6 +207,103 @@ def ar_baseline(pdx, mdev, b, w, inp, cache, par_draft, stream, steps: int) -> d
             "passes": K, "steps_timed": n, "pass1_equals_parallel_ntp_frac": agree}
 
 
+def rounds_leg(pdx, mdev, w, stream, R: int = 8, reps: int = 5) -> dict:
+    """R draft/verify rounds back to back on the device (NEXT-3): per round
+    the stand-in verifier (pd_verify_stub) builds the verify window from the
+    previous round's drafts, then pd_expand_batch + pd_draft_forward; the KV
+    cache carries over and each round's verify rows rewrite the previous
+    round's MASK-row entries. Timed eagerly and as one captured graph; every
+    graph replay must reproduce the eager drafts of every round."""
+    import torch
+    import synth
+    dev = torch.device("cuda:0")
+    dm, K = w.model, w.K
+    b = synth.make_batch(w, extra_positions=(R - 1) * (K + 1))
+    rounds = synth.make_rounds(w, R)
+    pool = synth.make_kv_pool(dm, b["num_blocks"], w.seed)
+    C = b["C"]
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    cache = pdx.pack_kv_cache(bf16(pool["k"]), bf16(pool["v"]))
+    d1 = pdx.batch_dims(C, K, b["T_in"], b["mask_id"], dm.hidden3, b["max_blocks"], b["num_blocks"])
+    dims = [d1] + [dict(d1, T_in=C * (K + 1)) for _ in range(R - 1)]
+    bt = i32(b["block_table"])
+    inp = [{"num_tokens": i32(b["num_tokens"]), "num_rejected": i32(b["num_rejected"]),
+            "target_ids": i32(b["target_ids"]), "target_pos": i32(b["target_pos"]),
+            "target_hidden": bf16(b["target_hidden"]), "next_token_ids": i32(b["next_token_ids"]),
+            "block_table": bt, "h_shared": mdev["h_shared"]}]
+    acc = []
+    for rd in rounds:
+        inp.append({"num_tokens": torch.empty(C, dtype=torch.int32, device=dev),
+                    "num_rejected": torch.empty(C, dtype=torch.int32, device=dev),
+                    "target_ids": torch.empty(C * (K + 1), dtype=torch.int32, device=dev),
+                    "target_pos": torch.empty(C * (K + 1), dtype=torch.int32, device=dev),
+                    "target_hidden": bf16(rd["target_hidden"]), "next_token_ids": i32(rd["next_token_ids"]),
+                    "block_table": bt, "h_shared": mdev["h_shared"]})
+        acc.append(i32(rd["accepted"]))
+    out = [pdx.alloc_batch(d, dev) for d in dims]
+    draft = [torch.empty(C * K, dtype=torch.int32, device=dev) for _ in range(R)]
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    h = pdx.Handle()
+
+    def run(s):
+        for t in range(R):
+            if t:
+                pdx.pd_verify_stub(dims[t - 1], out[t - 1], draft[t - 1], inp[t - 1]["next_token_ids"], acc[t - 1],
+                                   inp[t], st, s)
+            pdx.pd_expand_batch(dims[t], inp[t], out[t], s)
+            pdx.pd_draft_forward(h, mdev, dims[t], out[t], bt, cache, draft[t], None, s)
+
+    run(stream)
+    torch.cuda.synchronize()
+    status = h.status() | int(st.item()) | int(sum(int(o["status"].item()) for o in out))
+    if status:
+        raise SystemExit(f"multi-round run: device status {status}")
+    eager = [d.clone() for d in draft]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1000.0 / (reps * R)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        run(cap)
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            run(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    ok = True
+    for _ in range(3):
+        for d in draft:
+            d.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        ok = ok and all(bool(torch.equal(a, x)) for a, x in zip(draft, eager))
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1000.0 / (reps * R)
+    del g
+    h.free()
+    log(f"[bench] {R} rounds: {eager_us:.1f} us per round eager, {graph_us:.1f} us per round as one graph, "
+        f"replays match eager: {ok}")
+    return {"rounds": R, "us_per_round_eager": eager_us, "us_per_round_graph": graph_us,
+            "graph_replays_match_eager": ok,
+            "accepted_mean": float(np.mean([rd["accepted"].mean() for rd in rounds]))}
+
+
 def partition_leg(pdx, stream, reps: int = 20) -> dict:
     """Sequence partitioning ([Paper] sec. 3.2) on a training batch: 256
     sequences of 8192 tokens, K = 8 depths kept with COD decay r = 0.8 (the
@@ -386,6 +483,7 @@ def main():
     ar = ar_baseline(pdx, mdev, b, w, inp, cache, draft, stream, args.steps)
     ar["parallel_speedup"] = ar["ms_per_step"] / ms_step
     part = partition_leg(pdx, stream)
+    multi = rounds_leg(pdx, mdev, w, stream)
 
     R = b["C"] * w.K
     if dom == "lm_head":
@@ -441,6 +539,7 @@ def main():
         "hipgraph": graph,
         "ar_baseline": ar,
         "seq_partition": part,
+        "multi_round": multi,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

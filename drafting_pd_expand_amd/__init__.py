@@ -110,6 +110,8 @@ def load():
     lib.pd_ar_advance.argtypes = [POINTER(BatchDims), POINTER(Batch), c_void_p, c_void_p, POINTER(Batch),
                                   c_void_p]
     lib.pd_ar_advance.restype = c_int
+    lib.pd_verify_stub.argtypes = [POINTER(BatchDims), POINTER(Batch)] + [c_void_p] * 9
+    lib.pd_verify_stub.restype = c_int
     lib.pd_seq_partition.argtypes = [POINTER(PartitionDims), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p]
     lib.pd_seq_partition.restype = c_int
@@ -354,6 +356,31 @@ def pd_ar_advance(dims_prev: dict, prev: dict, draft_ids, block_table, nxt: dict
     bt = _dev(block_table, "block_table", (torch.int32,), C * dims_prev["max_blocks"], dev)
     _check(lib.pd_ar_advance(ctypes.byref(d), ctypes.byref(pb), c_void_p(di), c_void_p(bt), ctypes.byref(nb),
                              c_void_p(_stream_ptr(stream))), "pd_ar_advance")
+
+
+def pd_verify_stub(dims_prev: dict, prev: dict, prev_draft_ids, prev_next_token_ids, accepted, nxt: dict,
+                   status=None, stream=None) -> None:
+    """Enqueue the stand-in verifier (include/pd.h: pd_verify_stub). `nxt`
+    holds the next round's num_tokens, num_rejected [C] and target_ids,
+    target_pos [C*(K+1)] (int32, written)."""
+    lib = load()
+    C, K = dims_prev["C"], dims_prev["K"]
+    if C == 0:
+        return
+    dev = prev["positions"].device
+    pb = _batch_struct(prev, dims_prev, dev, hidden_optional=True)
+    d = _dims_struct(dims_prev)
+    I = (torch.int32,)
+    args = (_dev(prev_draft_ids, "prev_draft_ids", I, C * K, dev),
+            _dev(prev_next_token_ids, "prev_next_token_ids", I, C, dev),
+            _dev(accepted, "accepted", I, C, dev),
+            _dev(nxt["num_tokens"], "num_tokens", I, C, dev),
+            _dev(nxt["num_rejected"], "num_rejected", I, C, dev),
+            _dev(nxt["target_ids"], "target_ids", I, C * (K + 1), dev),
+            _dev(nxt["target_pos"], "target_pos", I, C * (K + 1), dev),
+            _dev(status, "status", I, 1, dev) if status is not None else None)
+    _check(lib.pd_verify_stub(ctypes.byref(d), ctypes.byref(pb), *[c_void_p(x) for x in args],
+                              c_void_p(_stream_ptr(stream))), "pd_verify_stub")
 
 
 def pd_seq_partition(keep, boundaries, seg, seg_offsets, rows, status=None, stream=None) -> None:

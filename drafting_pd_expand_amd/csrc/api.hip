@@ -379,6 +379,20 @@ int pd_ar_advance(const pd_batch_dims* dims_prev, const pd_batch* prev, const in
     return launch_ar_advance(*dims_prev, *prev, draft_ids, block_table, *next, (hipStream_t)stream);
 }
 
+int pd_verify_stub(const pd_batch_dims* dims_prev, const pd_batch* prev, const int32_t* prev_draft_ids,
+                   const int32_t* prev_next_token_ids, const int32_t* accepted, int32_t* num_tokens,
+                   int32_t* num_rejected, int32_t* target_ids, int32_t* target_pos, int32_t* status,
+                   void* stream) {
+    if (!dims_ok(dims_prev) || !prev) return PD_EINVAL;
+    if (dims_prev->C == 0) return PD_OK;
+    if (!prev->positions || !prev->new_token_indices || !prev_draft_ids || !prev_next_token_ids ||
+        !accepted || !num_tokens || !num_rejected || !target_ids || !target_pos)
+        return PD_EINVAL;
+    return launch_verify_stub(*dims_prev, *prev, prev_draft_ids, prev_next_token_ids, accepted,
+                              num_tokens, num_rejected, target_ids, target_pos, status,
+                              (hipStream_t)stream);
+}
+
 int pd_seq_partition(const pd_partition_dims* dims, const uint8_t* keep, const int32_t* boundaries,
                      int32_t* seg, int32_t* seg_offsets, int32_t* rows, int32_t* status,
                      void* stream) {

@@ -230,6 +230,52 @@ __global__ __launch_bounds__(256) void ar_advance_kernel(AdvanceArgs a) {
     a.next.seq_lens[r] = pos < 0 ? 1 : pos + 1;
 }
 
+// Stand-in verifier of a multi-round run ([Blog] "vLLM engineering
+// details": the drafter's window is the window the verifier checks next --
+// the K drafts plus the token the target sampled). Request r's next verify
+// window: that sampled token at p_ntp + 1 (p_ntp = the previous round's NTP
+// slot position: the slot pairs the sampled token with the hidden state at
+// p_ntp), then its K drafts at p_ntp + 2 ...; a_r of the drafts accepted.
+// One thread per window row.
+struct StubArgs {
+    pd_batch_dims d;   // the previous round's sizes
+    pd_batch prev;
+    const int32_t* draft;
+    const int32_t* next_prev;
+    const int32_t* accepted;
+    int32_t* num_tokens;
+    int32_t* num_rejected;
+    int32_t* target_ids;
+    int32_t* target_pos;
+    int32_t* status;
+};
+
+__global__ __launch_bounds__(256) void verify_stub_kernel(StubArgs a) {
+    const int C = a.d.C, K = a.d.K;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= C * (K + 1)) return;
+    const int r = i / (K + 1), j = i - r * (K + 1);
+    const int T_prev = a.d.T_in + C * (K - 1);
+    const int row = a.prev.new_token_indices[r * K];
+    int p_ntp = 0;
+    if (row < 0 || row >= T_prev) {
+        if (j == 0) flag(a.status, PD_STATUS_BAD_ROW);
+    } else {
+        p_ntp = a.prev.positions[row];
+    }
+    a.target_ids[i] = j == 0 ? a.next_prev[r] : a.draft[r * K + j - 1];
+    a.target_pos[i] = p_ntp + 1 + j;
+    if (j == 0) {
+        int acc = a.accepted[r];
+        if (acc < 0 || acc > K) {
+            flag(a.status, PD_STATUS_BAD_COUNTS);
+            acc = acc < 0 ? 0 : K;
+        }
+        a.num_tokens[r] = K + 1;
+        a.num_rejected[r] = K - acc;
+    }
+}
+
 }  // namespace
 
 int launch_ar_advance(const pd_batch_dims& d, const pd_batch& prev, const int32_t* draft_ids,
@@ -241,6 +287,26 @@ int launch_ar_advance(const pd_batch_dims& d, const pd_batch& prev, const int32_
     a.bt = block_table;
     a.next = next;
     hipLaunchKernelGGL(ar_advance_kernel, dim3((d.C + 1 + 255) / 256), dim3(256), 0, s, a);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+int launch_verify_stub(const pd_batch_dims& d, const pd_batch& prev, const int32_t* draft_ids,
+                       const int32_t* next_prev, const int32_t* accepted, int32_t* num_tokens,
+                       int32_t* num_rejected, int32_t* target_ids, int32_t* target_pos,
+                       int32_t* status, hipStream_t s) {
+    StubArgs a;
+    a.d = d;
+    a.prev = prev;
+    a.draft = draft_ids;
+    a.next_prev = next_prev;
+    a.accepted = accepted;
+    a.num_tokens = num_tokens;
+    a.num_rejected = num_rejected;
+    a.target_ids = target_ids;
+    a.target_pos = target_pos;
+    a.status = status;
+    const int n = d.C * (d.K + 1);
+    hipLaunchKernelGGL(verify_stub_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 

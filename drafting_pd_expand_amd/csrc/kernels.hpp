@@ -14,6 +14,10 @@ int launch_expand(const pd_batch_dims& d, const pd_expand_in& in, const pd_batch
 int launch_seq_partition(const pd_partition_dims& d, const uint8_t* keep, const int32_t* boundaries,
                          int32_t* seg, int32_t* seg_offsets, int32_t* rows, int32_t* status,
                          hipStream_t s);
+int launch_verify_stub(const pd_batch_dims& d, const pd_batch& prev, const int32_t* draft_ids,
+                       const int32_t* next_prev, const int32_t* accepted, int32_t* num_tokens,
+                       int32_t* num_rejected, int32_t* target_ids, int32_t* target_pos,
+                       int32_t* status, hipStream_t s);
 int launch_ar_advance(const pd_batch_dims& d, const pd_batch& prev, const int32_t* draft_ids,
                       const int32_t* block_table, const pd_batch& next, hipStream_t s);
 

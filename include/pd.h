@@ -276,6 +276,35 @@ int pd_profile(pd_handle* h, int class_mask);
  * launch count of one kernel class since profiling was enabled. */
 int pd_profile_read(pd_handle* h, int kernel_class, double* total_ms, int64_t* launches);
 
+/* ---- multi-round runs --------------------------------------------------------
+ *
+ * [Blog] "vLLM engineering details": for EAGLE the window the drafter
+ * consumes is the window the verifier checks next (the K drafts plus one
+ * token the target sampled), and the draft step runs under graph capture.
+ * pd_verify_stub stands in for the verifier so that rounds of
+ * verify -> pd_expand_batch -> pd_draft_forward can run back to back on the
+ * device (and be captured as one graph): how many drafts the target accepts,
+ * the token it samples and its hidden rows are the caller's inputs.
+ */
+
+/* Build round t+1's verify batch from round t. dims_prev: round t's sizes;
+ * prev: round t's expanded batch (positions and new_token_indices are read);
+ * prev_draft_ids [dev] [C*K]: round t's drafts; prev_next_token_ids [dev] [C]:
+ * the token the target sampled in round t (round t's next_token_ids);
+ * accepted [dev] [C]: drafts of round t the target accepts, 0..K.
+ * Out [dev]: num_tokens [C] (= K+1), num_rejected [C] (= K - accepted),
+ * target_ids and target_pos [C*(K+1)]: per request the sampled token at
+ * p_ntp + 1 (p_ntp = round t's NTP slot position), then the K drafts at
+ * p_ntp + 2 ... p_ntp + K + 1. Round t+1's dims are {C, K, T_in = C*(K+1)};
+ * its target_hidden and next_token_ids come from the caller.
+ * status [dev] [1] or NULL: PD_STATUS_BAD_ROW for a bad NTP index of prev,
+ * PD_STATUS_BAD_COUNTS for accepted outside [0, K] (clamped).
+ * Errors: PD_EINVAL for bad dims or NULL pointers; PD_EHIP. */
+int pd_verify_stub(const pd_batch_dims* dims_prev, const pd_batch* prev, const int32_t* prev_draft_ids,
+                   const int32_t* prev_next_token_ids, const int32_t* accepted, int32_t* num_tokens,
+                   int32_t* num_rejected, int32_t* target_ids, int32_t* target_pos, int32_t* status,
+                   void* stream);
+
 /* ---- sequence partitioning (training side) ----------------------------------
  *
  * [Paper] sec. 3.2 "Sequence Partitioning"; [arXiv] Figure 4 caption. A

@@ -197,3 +197,17 @@ def test_seq_partition_rejects_bad_calls(lib):
     assert call(ok, keep=FAKE + 4) == pdx.PD_EINVAL     # keep must be 8-byte aligned
     assert call(ok, seg=FAKE + 8) == pdx.PD_EINVAL      # seg must be 16-byte aligned
     assert call(P(0, 4, 64, 2), keep=None, bnd=None, seg=None, off=None, rows=None) == pdx.PD_OK
+
+
+def test_verify_stub_rejects_bad_calls(lib):
+    d = _dims()
+    b = pdx.Batch(*([FAKE] * len(pdx.Batch._fields_)))
+    args = [FAKE] * 9
+    assert lib.pd_verify_stub(None, ctypes.byref(b), *args, None) == pdx.PD_EINVAL
+    assert lib.pd_verify_stub(ctypes.byref(d), None, *args, None) == pdx.PD_EINVAL
+    for i in range(7):       # every pointer but status (the 8th) is required
+        a = list(args)
+        a[i] = None
+        assert lib.pd_verify_stub(ctypes.byref(d), ctypes.byref(b), *a, None) == pdx.PD_EINVAL, i
+    assert lib.pd_verify_stub(ctypes.byref(_dims(K=0)), ctypes.byref(b), *args, None) == pdx.PD_EINVAL
+    assert lib.pd_verify_stub(ctypes.byref(_dims(C=0)), ctypes.byref(b), *args, None) == pdx.PD_OK
