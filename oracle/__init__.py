@@ -15,6 +15,8 @@ Plain, slow, float64 NumPy definitions of what the drafting step computes:
   * ``verify_stub``, ``draft_rounds`` -- several draft/verify rounds in a
                          row with a stand-in verifier (accepted counts and
                          target outputs are inputs), KV carried over.
+  * ``fp8``           -- the E4M3 codec of the fp8 KV cache (``draft_forward``
+                         and the drivers take ``kv_fp8`` scales).
   * ``seq_partition`` -- the training-side sequence partitioning: every kept
                          (depth, position) of a long sequence assigned to a
                          segment with its dependencies, plus each segment's
@@ -42,6 +44,7 @@ printed values on the pages: beyond those pins they are "parity unpinned".
 from .expand import expand, ar_advance
 from .forward import draft_forward, ar_draft, rope_rotate, rms_norm, silu
 from .bf16 import bf16_to_f64
+from . import fp8
 from .partition import seq_partition, equal_boundaries
 from .rounds import verify_stub, draft_rounds
 

@@ -35,6 +35,7 @@ from __future__ import annotations
 import numpy as np
 
 from .bf16 import bf16_to_f64
+from .fp8 import e4m3_decode, fp8_roundtrip
 from .expand import ar_advance as _ar_advance
 
 
@@ -68,13 +69,24 @@ def _as_f64(a) -> np.ndarray:
     return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
+def _cache_values(a, kv_fp8, l: int, which: str) -> np.ndarray:
+    """Cache contents of layer l as values: bf16 bits (uint16), E4M3 codes
+    (uint8: the code's value times the layer's scale) or floats as they are."""
+    a = np.asarray(a)
+    if a.dtype == np.uint8:
+        if kv_fp8 is None:
+            raise ValueError("an fp8 cache needs kv_fp8 scales")
+        return e4m3_decode(a) * float(kv_fp8[which + "_scale"][l])
+    return _as_f64(a)
+
+
 def _softmax(s: np.ndarray) -> np.ndarray:
     e = np.exp(s - s.max(axis=-1, keepdims=True))
     return e / e.sum(axis=-1, keepdims=True)
 
 
 def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
-                  requests=None, block_size: int = 16, return_layers: bool = False) -> dict:
+                  requests=None, block_size: int = 16, return_layers: bool = False, kv_fp8=None) -> dict:
     """Run the drafter over the expanded batch `exp` (the oracle's own expansion).
 
     model: bf16-bit weights as made by synth.make_model (row-major [out][in]).
@@ -87,6 +99,12 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
     bool): those rows take hidden_d as their projected hidden input directly
     (no fc) -- the drafter's own hidden state fed back in autoregressive
     passes (see expand.ar_advance).
+    kv_fp8: None for a bf16 cache, or {"k_scale": [N], "v_scale": [N]} for an
+    fp8 E4M3 cache ([Blog] "vLLM engineering details": the serving
+    configuration keeps the KV cache in fp8): every K/V value this pass writes
+    is stored as the code of value / scale (oracle.fp8) and read back as
+    code value * scale; kv then holds uint8 codes (or values already read
+    back).
     Returns logits [R][V] and draft_ids [R] for the K sampled rows of each
     requested request (request-major, NTP row first), hidden_out [R][d] (their
     final residual, before the final norm), the K/V each layer wrote (slots,
@@ -150,8 +168,11 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
         k = rope_rotate(k, pos, theta)
 
         # cache: prior contents of the readable slots, then this layer's writes
-        kc = _as_f64(kv["k"][l][all_slots])
-        vc = _as_f64(kv["v"][l][all_slots])
+        kc = _cache_values(kv["k"][l][all_slots], kv_fp8, l, "k")
+        vc = _cache_values(kv["v"][l][all_slots], kv_fp8, l, "v")
+        if kv_fp8 is not None:   # what an fp8 cache holds for the new rows
+            k = fp8_roundtrip(k, float(kv_fp8["k_scale"][l]))
+            v = fp8_roundtrip(v, float(kv_fp8["v_scale"][l]))
         kc[local(slots)] = k
         vc[local(slots)] = v
         written.append((slots.copy(), k.copy(), v.copy()))
@@ -193,7 +214,7 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
 
 
 def ar_draft(model: dict, exp1: dict, block_table, kv: dict, K: int, block_size: int = 16,
-             tokens=None, hidden=None) -> list:
+             tokens=None, hidden=None, kv_fp8=None) -> list:
     """Autoregressive EAGLE-style drafting of K tokens per request: K serial
     drafter passes ([Blog] "background and motivation"), the baseline that
     parallel drafting replaces.
@@ -215,11 +236,11 @@ def ar_draft(model: dict, exp1: dict, block_table, kv: dict, K: int, block_size:
     hidden_out, ...) and the batches they ran on ("batch").
     """
     m = model["dims"]
-    kvf = {"k": [_as_f64(kv["k"][l]).copy() for l in range(m.N)],
-           "v": [_as_f64(kv["v"][l]).copy() for l in range(m.N)]}
+    kvf = {"k": [_cache_values(kv["k"][l], kv_fp8, l, "k").copy() for l in range(m.N)],
+           "v": [_cache_values(kv["v"][l], kv_fp8, l, "v").copy() for l in range(m.N)]}
     out, batch = [], exp1
     for k in range(K):
-        res = draft_forward(model, batch, block_table, kvf, 1, block_size=block_size)
+        res = draft_forward(model, batch, block_table, kvf, 1, block_size=block_size, kv_fp8=kv_fp8)
         res["batch"] = batch
         out.append(res)
         for l, (sl, kk, vv) in enumerate(res["kv_written"]):

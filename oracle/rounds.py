@@ -26,7 +26,7 @@ from __future__ import annotations
 import numpy as np
 
 from .expand import expand
-from .forward import draft_forward, _as_f64
+from .forward import draft_forward, _cache_values
 
 
 def verify_stub(prev_exp: dict, K: int, prev_draft_ids, prev_next_token_ids, accepted) -> dict:
@@ -56,7 +56,7 @@ def verify_stub(prev_exp: dict, K: int, prev_draft_ids, prev_next_token_ids, acc
 
 
 def draft_rounds(model: dict, args1: dict, rounds: list, block_table, kv: dict, K: int, mask_id: int,
-                 block_size: int = 16, tokens=None) -> list:
+                 block_size: int = 16, tokens=None, kv_fp8=None) -> list:
     """R = len(rounds) + 1 rounds of verify stand-in -> expansion -> drafter pass.
 
     args1: round 1's verify batch (num_tokens, num_rejected, target_ids,
@@ -69,15 +69,15 @@ def draft_rounds(model: dict, args1: dict, rounds: list, block_table, kv: dict, 
     (logits, draft_ids, kv_written, ...). The KV cache is carried in float64.
     """
     m = model["dims"]
-    kvf = {"k": [_as_f64(kv["k"][l]).copy() for l in range(m.N)],
-           "v": [_as_f64(kv["v"][l]).copy() for l in range(m.N)]}
+    kvf = {"k": [_cache_values(kv["k"][l], kv_fp8, l, "k").copy() for l in range(m.N)],
+           "v": [_cache_values(kv["v"][l], kv_fp8, l, "v").copy() for l in range(m.N)]}
     out = []
     args = args1
     for t in range(len(rounds) + 1):
         exp = expand(args["num_tokens"], args["num_rejected"], args["target_ids"], args["target_pos"],
                      args["target_hidden"], args["next_token_ids"], block_table, model["h_shared"], K,
                      mask_id, block_size)
-        res = draft_forward(model, exp, block_table, kvf, K, block_size=block_size)
+        res = draft_forward(model, exp, block_table, kvf, K, block_size=block_size, kv_fp8=kv_fp8)
         res["exp"] = exp
         out.append(res)
         for l, (sl, kk, vv) in enumerate(res["kv_written"]):

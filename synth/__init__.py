@@ -35,7 +35,8 @@ import numpy as np
 
 __all__ = [
     "ModelDims", "Workload", "WORKLOADS", "MODELS", "get_workload",
-    "make_model", "make_batch", "make_kv_pool", "make_cod_keep", "make_rounds", "f32_to_bf16_bits",
+    "make_model", "make_batch", "make_kv_pool", "kv_fp8_scales", "make_cod_keep", "make_rounds",
+    "f32_to_bf16_bits",
 ]
 
 _CHUNK = 1 << 22
@@ -247,14 +248,33 @@ def make_batch(w: Workload, seed: int | None = None, block_size: int = 16, extra
     }
 
 
-def make_kv_pool(m: ModelDims, num_blocks: int, seed: int, block_size: int = 16) -> dict:
+def make_kv_pool(m: ModelDims, num_blocks: int, seed: int, block_size: int = 16, fp8: bool = False) -> dict:
     """Prior KV-cache contents, slot-addressed: k, v bf16 bits of shape
     [N layers][num_blocks * block_size slots][Hkv][dh], all ~ N(0, 1).
     (Slots past a request's context hold stale values that the step must
-    overwrite before it reads them.)"""
+    overwrite before it reads them.)
+    fp8: the same draws stored as E4M3 codes (uint8), rounded to nearest by
+    the library's float8_e4m3fn type; with the scales of kv_fp8_scales they
+    read back as code value * scale."""
     shape = (m.N, num_blocks * block_size, m.Hkv, m.dh)
-    return {"k": _fill(shape, seed, 21, "normal", 1.0),
-            "v": _fill(shape, seed, 22, "normal", 1.0)}
+    if not fp8:
+        return {"k": _fill(shape, seed, 21, "normal", 1.0),
+                "v": _fill(shape, seed, 22, "normal", 1.0)}
+    import torch
+    out = {}
+    for name, tag in (("k", 23), ("v", 24)):
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(tag,)))
+        x = np.clip(rng.standard_normal(shape, dtype=np.float32), -448.0, 448.0)
+        out[name] = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out
+
+
+def kv_fp8_scales(m: ModelDims, seed: int) -> dict:
+    """Per-layer scales of an fp8 KV cache (stored code = value / scale):
+    k_scale and v_scale uniform in [0.5, 2), float32."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(25,)))
+    return {"k_scale": rng.uniform(0.5, 2.0, m.N).astype(np.float32),
+            "v_scale": rng.uniform(0.5, 2.0, m.N).astype(np.float32)}
 
 
 def make_cod_keep(B: int, n: int, K: int, r: float, seed: int, lengths=None) -> np.ndarray:

@@ -32,9 +32,19 @@ def _rope_complex(x, positions, theta):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def dense_prefill_logits(model, prompt_ids, prompt_hidden, next_token, K, mask_id):
+def _fp8_cache(t, scale):
+    """What an fp8 (E4M3) cache returns for t: the library's float8_e4m3fn
+    rounding of t / scale (saturated to +-448 first: the type itself does not
+    saturate), times scale."""
+    c = torch.clamp(t / scale, -448.0, 448.0).to(torch.float32).to(torch.float8_e4m3fn)
+    return c.to(torch.float64) * scale
+
+
+def dense_prefill_logits(model, prompt_ids, prompt_hidden, next_token, K, mask_id, kv_fp8=None):
     """Logits [K][V] of the K sampled rows (NTP, then MASK rows) for a prompt
-    of n tokens at positions 0..n-1 with target hidden rows prompt_hidden."""
+    of n tokens at positions 0..n-1 with target hidden rows prompt_hidden.
+    kv_fp8: {"k_scale": [N], "v_scale": [N]} to read K and V as an fp8
+    cache holds them."""
     m = model["dims"]
     n = len(prompt_ids)
     toks = list(prompt_ids[1:]) + [int(next_token)] + [mask_id] * (K - 1)
@@ -56,6 +66,9 @@ def dense_prefill_logits(model, prompt_ids, prompt_hidden, next_token, K, mask_i
         q = _rope_complex(q.reshape(T, m.Hq, m.dh), positions, m.rope_theta)
         k = _rope_complex(k.reshape(T, m.Hkv, m.dh), positions, m.rope_theta)
         v = v.reshape(T, m.Hkv, m.dh)
+        if kv_fp8 is not None:
+            k = _fp8_cache(k, float(kv_fp8["k_scale"][l]))
+            v = _fp8_cache(v, float(kv_fp8["v_scale"][l]))
         G = m.Hq // m.Hkv
         k = k.repeat_interleave(G, dim=1)
         v = v.repeat_interleave(G, dim=1)

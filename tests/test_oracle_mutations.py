@@ -40,13 +40,19 @@ MUTATIONS = [
     ("rounds.py", "ids.append(int(nxt[r]))", "ids.append(int(d[r, 0]))"),                     # sampled token dropped
     ("rounds.py", '"num_rejected": (K - a).astype(np.int32)', '"num_rejected": a.astype(np.int32)'),  # rejected count
     ("rounds.py", 'kvf["k"][l][sl] = kk', "pass"),                                            # no KV carry-over
+    ("fp8.py", "(frac == 0.5) & (lo % 2 == 1)", "(frac == 0.5) & (lo % 2 == 0)"),             # ties to odd
+    ("fp8.py", "E4M3_MAX = 448.0", "E4M3_MAX = 480.0"),                                        # wrong saturation bound
+    ("fp8.py", "(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)"),    # exponent bias
+    ("forward.py", 'k = fp8_roundtrip(k, float(kv_fp8["k_scale"][l]))', "k = fp8_roundtrip(k, 1.0)"),  # K scale ignored
 ]
 
 PIN_FILES = {
     "partition.py": ["tests/test_oracle_partition.py"],
     "rounds.py": ["tests/test_oracle_rounds.py"],
+    "fp8.py": ["tests/test_oracle_fp8.py"],
 }
-DEFAULT_PINS = ["tests/test_oracle_expand.py", "tests/test_oracle_forward.py", "tests/test_oracle_ar.py"]
+DEFAULT_PINS = ["tests/test_oracle_expand.py", "tests/test_oracle_forward.py", "tests/test_oracle_ar.py",
+                "tests/test_oracle_fp8.py"]
 
 
 @pytest.mark.parametrize("fname,old,new", MUTATIONS, ids=[m[2][:24] for m in MUTATIONS])
