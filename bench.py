@@ -304,6 +304,66 @@ def rounds_leg(pdx, mdev, w, stream, R: int = 8, reps: int = 5) -> dict:
             "accepted_mean": float(np.mean([rd["accepted"].mean() for rd in rounds]))}
 
 
+def fp8_leg(pdx, mdev, w, b, dims, inp, cache, stream, steps: int, bf16_ids, bf16_attn_us: float) -> dict:
+    """The same step over an fp8 (E4M3) KV cache (NEXT-2): the prior cache is
+    the bf16 one rounded to E4M3 codes (per-layer scales from synth), new
+    K/V are written as codes. Timed like the main leg, with HIP events
+    around the attention kernel; its roofline counts one byte per cached K/V
+    element."""
+    import torch
+    import synth
+    dm, K = w.model, w.K
+    sc = synth.kv_fp8_scales(dm, w.seed)
+    pairs = np.stack([sc["k_scale"], sc["v_scale"]], axis=1)
+    # codes of the prior cache: value / scale rounded by the library's E4M3 type (saturated first)
+    N = dm.N
+    src = cache.view(torch.bfloat16).view(N, 2, -1)
+    cache8 = torch.empty(src.shape, dtype=torch.uint8, device=cache.device)
+    for l in range(N):
+        for t, s in ((0, float(sc["k_scale"][l])), (1, float(sc["v_scale"][l]))):
+            cache8[l, t] = (src[l, t].float() / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    cache8 = cache8.view(cache.shape)
+    out = pdx.alloc_batch(dims, cache.device)
+    draft = torch.empty(b["C"] * K, dtype=torch.int32, device=cache.device)
+    h = pdx.Handle()
+
+    def step():
+        pdx.pd_expand_batch(dims, inp, out, stream)
+        pdx.pd_draft_forward(h, mdev, dims, out, inp["block_table"], cache8, draft, None, stream, kv_scales=pairs)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    st = h.status() | int(out["status"].item())
+    if st:
+        raise SystemExit(f"fp8 leg: device status {st}")
+    h.profile(1 << pdx.KERNEL_ATTN)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    a_ms, a_n = h.profile_read(pdx.KERNEL_ATTN)
+    h.profile(0)
+    a_us = a_ms * 1000.0 / max(a_n, 1)
+    v = b["num_tokens"] - b["num_rejected"]
+    seq = b["context_lens"] + v + K - 1
+    T_out = b["T_in"] + b["C"] * (K - 1)
+    abytes = int(seq.sum()) * dm.Hkv * dm.dh * 2 + 2 * T_out * dm.Hq * dm.dh * 2
+    agree = float((draft == bf16_ids).float().mean().item())
+    h.free()
+    log(f"[bench] fp8 KV cache: {ms * 1000:.1f} us/step, attention {a_us:.1f} us/launch "
+        f"({abytes / (a_us * 1e-6) / 1e9:.0f} GB/s; bf16 cache {bf16_attn_us:.1f} us)")
+    return {"ms_per_step": ms, "steps_per_s": 1000.0 / ms, "attention_us_per_launch": a_us,
+            "attention_us_per_launch_bf16_cache": bf16_attn_us,
+            "attention_roofline": {"bound": "hbm", "kernel": f"attn_split_kernel<{dm.dh}, fp8>",
+                                   "achieved": abytes / (a_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": abytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes_per_launch": abytes},
+            "draft_ids_equal_bf16_cache_frac": agree}
+
+
 def partition_leg(pdx, stream, reps: int = 20) -> dict:
     """Sequence partitioning ([Paper] sec. 3.2) on a training batch: 256
     sequences of 8192 tokens, K = 8 depths kept with COD decay r = 0.8 (the
@@ -483,6 +543,8 @@ def main():
     ar = ar_baseline(pdx, mdev, b, w, inp, cache, draft, stream, args.steps)
     ar["parallel_speedup"] = ar["ms_per_step"] / ms_step
     part = partition_leg(pdx, stream)
+    kv8 = fp8_leg(pdx, mdev, w, b, dims, inp, cache, stream, max(5, args.steps // 2), eager_ids,
+                  cls_us["attention"]["us_per_launch"])
     multi = rounds_leg(pdx, mdev, w, stream)
 
     R = b["C"] * w.K
@@ -539,6 +601,7 @@ def main():
         "hipgraph": graph,
         "ar_baseline": ar,
         "seq_partition": part,
+        "kv_fp8": kv8,
         "multi_round": multi,
         "roofline": roof,
         "cpu_baseline": cpu,

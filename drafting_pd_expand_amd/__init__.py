@@ -71,7 +71,8 @@ _L = c_void_p * PD_MAX_LAYERS
 
 
 class ForwardOpts(ctypes.Structure):
-    _fields_ = [("hidden_d", c_void_p), ("hidden_out", c_void_p)]
+    _fields_ = [("hidden_d", c_void_p), ("hidden_out", c_void_p), ("kv_fp8", c_int32),
+                ("kv_scales", POINTER(ctypes.c_float))]
 
 
 class PartitionDims(ctypes.Structure):
@@ -302,10 +303,14 @@ def _model_struct(m: dict) -> Model:
 
 
 def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block_table, kv_cache,
-                     draft_ids, logits=None, stream=None, hidden_d=None, hidden_out=None) -> None:
+                     draft_ids, logits=None, stream=None, hidden_d=None, hidden_out=None,
+                     kv_scales=None) -> None:
     """Enqueue the drafter pass (include/pd.h: pd_draft_forward, or
-    pd_draft_forward_ex when hidden_d / hidden_out are given). `model` is a
-    dict made by device_model(); `batch` holds the expanded-batch tensors.
+    pd_draft_forward_ex when hidden_d / hidden_out are given or the cache is
+    fp8). `model` is a dict made by device_model(); `batch` holds the
+    expanded-batch tensors. kv_cache: bf16 (see pack_kv_cache) or uint8 E4M3
+    codes (an fp8 cache; kv_scales then gives the [N][2] per-layer K and V
+    scales, default 1.0).
     hidden_d: bf16 [T_out][d] projected hidden rows (fc skipped);
     hidden_out: bf16 [C*K][d] receives the sampled rows' final residual."""
     lib = load()
@@ -324,17 +329,23 @@ def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block
     bs = _batch_struct(batch, dims, dev, hidden_optional=hidden_d is not None)
     d = _dims_struct(dims)
     bt = _dev(block_table, "block_table", (torch.int32,), C * dims["max_blocks"], dev)
-    kv = _dev(kv_cache, "kv_cache", _BF16, kv_cache_elems(dm, dims["num_blocks"]), dev)
+    fp8 = kv_cache.dtype == torch.uint8
+    kv = _dev(kv_cache, "kv_cache", (torch.uint8,) if fp8 else _BF16, kv_cache_elems(dm, dims["num_blocks"]), dev)
     di = _dev(draft_ids, "draft_ids", (torch.int32,), C * K, dev)
     lg = _dev(logits, "logits", (torch.float32,), C * K * dm.V, dev) if logits is not None else None
     args = (ctypes.byref(handle.ptr), ctypes.byref(ms), ctypes.byref(d), ctypes.byref(bs), c_void_p(bt),
             c_void_p(kv), c_void_p(di), c_void_p(lg))
-    if hidden_d is None and hidden_out is None:
+    if hidden_d is None and hidden_out is None and not fp8:
         _check(lib.pd_draft_forward(*args, c_void_p(_stream_ptr(stream))), "pd_draft_forward")
         return
+    scales = None
+    if fp8 and kv_scales is not None:
+        sc = np.ascontiguousarray(np.asarray(kv_scales, dtype=np.float32).reshape(dm.N, 2))
+        scales = (ctypes.c_float * (2 * dm.N))(*sc.reshape(-1).tolist())
     opts = ForwardOpts(
         _dev(hidden_d, "hidden_d", _BF16, T_out * dm.d, dev) if hidden_d is not None else None,
-        _dev(hidden_out, "hidden_out", _BF16, C * K * dm.d, dev) if hidden_out is not None else None)
+        _dev(hidden_out, "hidden_out", _BF16, C * K * dm.d, dev) if hidden_out is not None else None,
+        1 if fp8 else 0, scales)
     _check(lib.pd_draft_forward_ex(*args, ctypes.byref(opts), c_void_p(_stream_ptr(stream))),
            "pd_draft_forward_ex")
 
@@ -445,6 +456,11 @@ def pack_kv_cache(k_slots: torch.Tensor, v_slots: torch.Tensor) -> torch.Tensor:
     kp = k_slots.reshape(N, nb, PD_PAGE, Hkv, dh).permute(0, 1, 3, 2, 4).reshape(N, nb, Hkv, PD_PAGE * dh)
     vp = v_slots.reshape(N, nb, PD_PAGE, Hkv, dh).permute(0, 1, 3, 4, 2).reshape(N, nb, Hkv, PD_PAGE * dh)
     return torch.stack([kp, vp], dim=1).contiguous()
+
+
+def pack_kv_cache_fp8(k_codes: torch.Tensor, v_codes: torch.Tensor) -> torch.Tensor:
+    """Like pack_kv_cache for uint8 E4M3 codes (an fp8 cache)."""
+    return pack_kv_cache(k_codes, v_codes)
 
 
 def unpack_kv_cache(cache: torch.Tensor, Hkv: int, dh: int):

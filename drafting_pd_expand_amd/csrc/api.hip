@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <new>
 #include <utility>
@@ -222,7 +223,12 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
                         void* stream) {
     const uint16_t* hidden_d = opts ? opts->hidden_d : nullptr;
     uint16_t* hidden_out = opts ? opts->hidden_out : nullptr;
+    const bool fp8 = opts && opts->kv_fp8;
+    const float* kv_scales = fp8 ? opts->kv_scales : nullptr;
     if (!hp || !model_ok(m) || !dims_ok(dims) || !batch_ok(b, hidden_d != nullptr)) return PD_EINVAL;
+    if (kv_scales)
+        for (int i = 0; i < 2 * m->N; ++i)
+            if (!(kv_scales[i] > 0.f) || !std::isfinite(kv_scales[i])) return PD_EINVAL;
     if (((uintptr_t)hidden_d | (uintptr_t)hidden_out) & 15) return PD_EINVAL;
     if (dims->C == 0) return PD_OK;
     if (dims->block_size != PD_PAGE || dims->hidden3 != m->hidden3) return PD_EINVAL;
@@ -249,7 +255,8 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
     const int T = L.T, R = L.R, d = m->d;
     const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
     const int hd = m->Hq * m->dh;
-    const size_t plane = (size_t)dims->num_blocks * m->Hkv * PD_PAGE * m->dh;
+    // bytes of one K or V plane: bf16 elements or E4M3 codes
+    const size_t plane = (size_t)dims->num_blocks * m->Hkv * PD_PAGE * m->dh * (fp8 ? 1 : 2);
     int32_t* st = h->status;
 
     // one projection; returns its split count through *splits (EPI_PARTIAL)
@@ -307,14 +314,17 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
         const int in_l = (l == 0) ? 2 * d : d;
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, u, in_l, nullptr, 0, m->w_qkv[l], nullptr, T, qkvw,
                     in_l, nullptr, 0, &sp));
-        uint16_t* kpl = kv_cache + (size_t)(2 * l) * plane;
-        uint16_t* vpl = kv_cache + (size_t)(2 * l + 1) * plane;
+        char* kpl = reinterpret_cast<char*>(kv_cache) + (size_t)(2 * l) * plane;
+        char* vpl = reinterpret_cast<char*>(kv_cache) + (size_t)(2 * l + 1) * plane;
+        const float ks = kv_scales ? kv_scales[2 * l] : 1.0f, vs = kv_scales ? kv_scales[2 * l + 1] : 1.0f;
         {
             Timed t(h, PD_KERNEL_OTHER, s);
             PD_TRY(launch_rope_cache(ws, sp, b->positions, b->slot_mapping, T, m->Hq, m->Hkv, m->dh,
-                                     m->rope_theta, q, kpl, vpl, dims->num_blocks, st, s));
+                                     m->rope_theta, q, kpl, vpl, dims->num_blocks, st, s, fp8 ? 1 : 0, ks,
+                                     vs));
         }
         aa.q = q; aa.kplane = kpl; aa.vplane = vpl;
+        aa.fp8 = fp8; aa.k_scale = ks; aa.v_scale = vs;
         {
             hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr, e3 = nullptr;
             if (h->prof & (1 << PD_KERNEL_ATTN)) { e0 = take_event(h); e1 = take_event(h); }

@@ -41,6 +41,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -62,21 +63,22 @@ constexpr int kMaxSplits = 128;           // splits of one request the merge com
 // (zero-initialised at load; nothing writes it).
 __device__ __align__(16) uint16_t g_zero_page[PD_PAGE * 128];
 
-// Per head size: waves per workgroup, query tiles per wave (one pass covers
-// 128 queries), pages per LDS stage, stages in the ring, 1 KB loads per
-// page (K then V^T) and per wave per stage.
-template <int DH>
+// Per head size and cache type: waves per workgroup, query tiles per wave
+// (one pass covers 128 queries), pages per LDS stage, stages in the ring,
+// 1 KB loads per page (K then V^T) and per wave per stage. An fp8 stage holds
+// twice the pages of a bf16 one (the same bytes).
+template <int DH, bool F8 = false>
 struct AttnCfg {
     static constexpr int NW = 4;
     static constexpr int TPW = 2;
-    static constexpr int CH = DH == 64 ? 4 : 2;
+    static constexpr int EB = F8 ? 1 : 2;          // bytes per cached element
+    static constexpr int CH = (DH == 64 ? 4 : 2) * (F8 ? 2 : 1);
     static constexpr int NST = 4;
-    static constexpr int LPP = DH / 16;            // 1 KB blocks per page: K DH/32, V DH/32
-    static constexpr int L = CH * LPP / NW;        // loads per wave per stage
     static constexpr int PE = 16 * DH;             // elements of one page of K (or V)
+    static constexpr int LPP = 2 * PE * EB / 1024; // 1 KB blocks per page: K half, V half
+    static constexpr int L = CH * LPP / NW;        // loads per wave per stage
     static_assert(CH * LPP % NW == 0, "stage loads split evenly over the waves");
     static_assert(CH % 2 == 0, "pages are consumed in pairs");
-    static_assert(LPP % NW == 0, "a wave's loads of one page are whole parts");
 };
 
 // LDS swizzles (element offsets inside one staged page). A K row keeps its
@@ -87,6 +89,30 @@ struct AttnCfg {
 // of rows 0..7 at one half cover 8 distinct 16-byte positions.
 __device__ __forceinline__ int key_sw(int key) { return (key & 3) | ((key >> 1) & 4); }
 __device__ __forceinline__ int v_half(int row, int half) { return half ^ ((row >> 2) & 1); }
+
+// fp8 pages: a K row (one key, DH bytes) keeps its 16-byte chunks
+// XOR-permuted by key_sw8; the 16 lanes of one fragment read are keys
+// {0-3, 8-11} of both pages of a pair at one chunk, and the permutation puts
+// them on 16 distinct 16-byte slots of a 256-byte bank line. V^T rows are
+// 16 bytes (16 keys) and are read 8 bytes at a time: no permutation needed.
+template <int DH>
+__device__ __forceinline__ int key_sw8(int key, int page) {
+    if constexpr (DH == 64) return ((key >> 3) & 1) | ((page & 1) << 1);
+    else return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | ((page & 1) << 2);
+}
+
+// 8 E4M3 codes -> 8 bf16 (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
 
 // The ring's global -> LDS copies are ordered by hand: wait_vmcnt<N> (own
 // copies), then barrier_lds (every wave's copies visible, every wave done
@@ -204,13 +230,14 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
     }
 }
 
-template <int DH>
-__global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnArgs a) {
-    using Cf = AttnCfg<DH>;
+template <int DH, bool F8>
+__global__ __launch_bounds__((64 * AttnCfg<DH, F8>::NW)) void attn_split_kernel(AttnArgs a) {
+    using Cf = AttnCfg<DH, F8>;
+    using ET = typename std::conditional<F8, uint8_t, uint16_t>::type;   // cached element
     constexpr int KB = DH / 32;  // 16x16x32 steps over dh for the scores
     constexpr int OT = DH / 16;  // 16-dim output tiles
     constexpr int TPW = Cf::TPW, NW = Cf::NW, NT = 64 * NW, CH = Cf::CH, NST = Cf::NST;
-    __shared__ __align__(16) uint16_t kv[NST][CH][2][Cf::PE];   // [stage][page][K, V^T]
+    __shared__ __align__(16) ET kv[NST][CH][2][Cf::PE];   // [stage][page][K, V^T]
     __shared__ int btc[kBtMax + Cf::CH];
     __shared__ int pv[NST][CH];
 
@@ -229,7 +256,10 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
     const int nchunks = (npages + CH - 1) / CH;
     const int G = a.Hq / a.Hkv;
     const int nq = (row1 - row0) * G;
-    const float scale = a.scale_log2, inv_scale = 1.0f / a.scale_log2;
+    // an fp8 cache holds K / k_scale and V / v_scale: the scores take k_scale
+    // with the softmax scale, the outputs v_scale
+    const float scale = a.scale_log2 * (F8 ? a.k_scale : 1.0f), inv_scale = 1.0f / scale;
+    const float osc = F8 ? a.v_scale : 1.0f;
 
     bf16x8 qv[TPW][KB];
     int qrow[TPW], qh[TPW], lim[TPW];
@@ -249,8 +279,12 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
             lim[tt] = qrej[tt] ? 0x7fffffff : min(ke - 1, pos);
             const uint16_t* qp = a.q + ((size_t)qrow[tt] * a.Hq + qh[tt]) * DH;
 #pragma unroll
-            for (int kk = 0; kk < KB; ++kk)
-                qv[tt][kk] = qok[tt] ? ld_bf16x8(qp + 32 * kk + 8 * g4) : zero_bf16x8();
+            for (int kk = 0; kk < KB; ++kk) {
+                // fp8: the dims of a score step are regrouped so that one 16-byte
+                // read of a key row feeds two steps (the q side follows suit)
+                const int dim = F8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
+                qv[tt][kk] = qok[tt] ? ld_bf16x8(qp + dim) : zero_bf16x8();
+            }
         }
     };
     load_q(0);
@@ -265,15 +299,33 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const uint16_t* zp = g_zero_page;
     int loff[Cf::L];   // per-lane source offset (elements) inside the page
+    // the wave's qd-th block of a stage: page and part (wave-uniform)
+    auto blk_page = [&](int qd) {
+        if constexpr (Cf::LPP % NW == 0) return qd * NW / Cf::LPP;
+        else return (qd * NW + wv) / Cf::LPP;
+    };
+    auto blk_part = [&](int qd) {
+        if constexpr (Cf::LPP % NW == 0) return (qd * NW) % Cf::LPP + wv;
+        else return (qd * NW + wv) % Cf::LPP;
+    };
 #pragma unroll
     for (int qd = 0; qd < Cf::L; ++qd) {
-        const int part = (qd * NW) % Cf::LPP + wv;
-        if (part < Cf::LPP / 2) {               // K: 512 / DH keys per 1 KB block
-            const int key = (512 / DH) * part + lane / (DH / 8);
-            loff[qd] = key * DH + (((lane % (DH / 8)) ^ key_sw(key)) << 3);
-        } else {                                // V^T: 32 dim rows of 16 keys per 1 KB block
-            const int row = 32 * (part - Cf::LPP / 2) + lane / 2;
-            loff[qd] = row * PD_PAGE + (v_half(row, lane & 1) << 3);
+        const int part = blk_part(qd);
+        if constexpr (!F8) {
+            if (part < Cf::LPP / 2) {               // K: 512 / DH keys per 1 KB block
+                const int key = (512 / DH) * part + lane / (DH / 8);
+                loff[qd] = key * DH + (((lane % (DH / 8)) ^ key_sw(key)) << 3);
+            } else {                                // V^T: 32 dim rows of 16 keys per 1 KB block
+                const int row = 32 * (part - Cf::LPP / 2) + lane / 2;
+                loff[qd] = row * PD_PAGE + (v_half(row, lane & 1) << 3);
+            }
+        } else {
+            if (part < Cf::LPP / 2) {               // K: 1024 / DH keys per 1 KB block
+                const int key = (1024 / DH) * part + lane / (DH / 16);
+                loff[qd] = key * DH + (((lane % (DH / 16)) ^ key_sw8<DH>(key, blk_page(qd))) << 4);
+            } else {                                // V^T: 64 dim rows of 16 keys per 1 KB block
+                loff[qd] = (64 * (part - Cf::LPP / 2) + lane) * PD_PAGE;
+            }
         }
     }
     // global -> LDS for chunk c into ring slot `slot`: every wave issues exactly
@@ -282,14 +334,14 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
     auto issue = [&](int c, int slot) {
 #pragma unroll
         for (int qd = 0; qd < Cf::L; ++qd) {
-            const int p = qd * NW / Cf::LPP;
-            const int part = (qd * NW) % Cf::LPP + wv;
+            const int p = blk_page(qd);
+            const int part = blk_part(qd);
             const int blk = __builtin_amdgcn_readfirstlane(btc[c * CH + p]);
             const bool ok = (unsigned)blk < (unsigned)a.num_blocks;
             const bool isk = part < Cf::LPP / 2;
-            const uint16_t* base =
-                ok ? (isk ? a.kplane : a.vplane) + ((size_t)blk * a.Hkv + g) * Cf::PE : zp;
-            uint16_t* dst = &kv[slot][p][isk ? 0 : 1][(isk ? part : part - Cf::LPP / 2) * 512];
+            const ET* base = ok ? static_cast<const ET*>(isk ? a.kplane : a.vplane) + ((size_t)blk * a.Hkv + g) * Cf::PE
+                                : reinterpret_cast<const ET*>(zp);
+            ET* dst = &kv[slot][p][isk ? 0 : 1][(isk ? part : part - Cf::LPP / 2) * (1024 / Cf::EB)];
             __builtin_amdgcn_global_load_lds((void*)(base + loff[qd]),
                                              (__attribute__((address_space(3))) void*)(uintptr_t)lds_addr(dst),
                                              16, 0, 0);
@@ -345,18 +397,39 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
                 const int p0 = kb + (c * CH + pi) * PD_PAGE;
                 if (p0 >= ke) break;
                 const bool pgok = pv[b][pi + vpage] != 0;   // this lane group's page
-                const uint16_t* Kp = kv[b][pi + kpage][0];
-                const uint16_t* Vp = kv[b][pi + vpage][1];
+                const ET* Kp = kv[b][pi + kpage][0];
+                const ET* Vp = kv[b][pi + vpage][1];
                 bf16x8 k0[KB], k1[KB], vf[OT];
+                if constexpr (!F8) {
 #pragma unroll
-                for (int kk = 0; kk < KB; ++kk) {
-                    const int ch = ((4 * kk + g4) ^ ksw) << 3;
-                    k0[kk] = *reinterpret_cast<const bf16x8*>(Kp + key0 * DH + ch);
-                    k1[kk] = *reinterpret_cast<const bf16x8*>(Kp + (key0 + 4) * DH + ch);
+                    for (int kk = 0; kk < KB; ++kk) {
+                        const int ch = ((4 * kk + g4) ^ ksw) << 3;
+                        k0[kk] = *reinterpret_cast<const bf16x8*>(Kp + key0 * DH + ch);
+                        k1[kk] = *reinterpret_cast<const bf16x8*>(Kp + (key0 + 4) * DH + ch);
+                    }
+#pragma unroll
+                    for (int j = 0; j < OT; ++j)
+                        vf[j] = *reinterpret_cast<const bf16x8*>(Vp + 16 * PD_PAGE * j + voff);
+                } else {
+                    // K: one 16-byte read per key row feeds score steps 2m and 2m + 1
+                    const int sw = key_sw8<DH>(key0, kpage);   // the same for key0 + 4
+#pragma unroll
+                    for (int m2 = 0; m2 < KB / 2; ++m2) {
+                        const int ch = ((4 * m2 + g4) ^ sw) << 4;
+                        const uint4 a0 = *reinterpret_cast<const uint4*>(Kp + key0 * DH + ch);
+                        const uint4 a1 = *reinterpret_cast<const uint4*>(Kp + (key0 + 4) * DH + ch);
+                        k0[2 * m2] = fp8x8_to_bf16(a0.x, a0.y);
+                        k0[2 * m2 + 1] = fp8x8_to_bf16(a0.z, a0.w);
+                        k1[2 * m2] = fp8x8_to_bf16(a1.x, a1.y);
+                        k1[2 * m2 + 1] = fp8x8_to_bf16(a1.z, a1.w);
+                    }
+                    // V^T: keys 8 (g4 & 1) .. + 7 of one dim row
+#pragma unroll
+                    for (int j = 0; j < OT; ++j) {
+                        const uint2 w = *reinterpret_cast<const uint2*>(Vp + (16 * j + r16) * PD_PAGE + 8 * (g4 & 1));
+                        vf[j] = fp8x8_to_bf16(w.x, w.y);
+                    }
                 }
-#pragma unroll
-                for (int j = 0; j < OT; ++j)
-                    vf[j] = *reinterpret_cast<const bf16x8*>(Vp + 16 * PD_PAGE * j + voff);
                 const int t0 = p0 + 8 * g4;   // keys t0 .. t0+7 in this lane's scores
 #pragma unroll
                 for (int tt = 0; tt < TPW; ++tt) {
@@ -408,7 +481,7 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
             if (!qok[tt]) continue;
             if (ns == 1) {
                 // the only split: normalized bf16 output (rejected rows: zeros)
-                const float inv = (!qrej[tt] && l > 0.f) ? 1.0f / l : 0.f;
+                const float inv = (!qrej[tt] && l > 0.f) ? osc / l : 0.f;
                 uint16_t* op = a.out + ((size_t)qrow[tt] * a.Hq + qh[tt]) * DH + 4 * g4;
 #pragma unroll
                 for (int j = 0; j < OT; ++j) {
@@ -420,7 +493,7 @@ __global__ __launch_bounds__(64 * AttnCfg<DH>::NW) void attn_split_kernel(AttnAr
                 const size_t base = ((size_t)s * a.T + qrow[tt]) * a.Hq + qh[tt];
 #pragma unroll
                 for (int j = 0; j < OT; ++j)
-                    *reinterpret_cast<f32x4*>(a.part_o + base * DH + 16 * j + 4 * g4) = o[tt][j];
+                    *reinterpret_cast<f32x4*>(a.part_o + base * DH + 16 * j + 4 * g4) = o[tt][j] * osc;
                 if (g4 == 0) *reinterpret_cast<float2*>(a.part_ml + base * 2) = make_float2(mrun[tt], l);
             }
         }
@@ -498,8 +571,12 @@ int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1, hi
               hipEvent_t e3) {
     constexpr int NW = AttnCfg<DH>::NW;
     if (e0) (void)hipEventRecord(e0, s);
-    hipLaunchKernelGGL(attn_split_kernel<DH>, dim3((unsigned)a.sp.max_units * a.Hkv), dim3(64 * NW), 0,
-                       s, a);
+    if (a.fp8)
+        hipLaunchKernelGGL((attn_split_kernel<DH, true>), dim3((unsigned)a.sp.max_units * a.Hkv), dim3(64 * NW),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((attn_split_kernel<DH, false>), dim3((unsigned)a.sp.max_units * a.Hkv), dim3(64 * NW),
+                           0, s, a);
     if (e1) (void)hipEventRecord(e1, s);
     if (hipGetLastError() != hipSuccess) return PD_EHIP;
     if (e2) (void)hipEventRecord(e2, s);

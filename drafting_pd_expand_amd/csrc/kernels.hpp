@@ -77,9 +77,11 @@ int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
                       int d, float eps, hipStream_t s, const int32_t* rows = nullptr, int nrows = 0,
                       int32_t* status = nullptr, uint16_t* xout = nullptr);
+// fp8: the planes hold E4M3 codes of value / k_scale (K) and value / v_scale (V)
 int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
-                      int Hq, int Hkv, int dh, float theta, uint16_t* q_out, uint16_t* kplane,
-                      uint16_t* vplane, int num_blocks, int32_t* status, hipStream_t s);
+                      int Hq, int Hkv, int dh, float theta, uint16_t* q_out, void* kplane,
+                      void* vplane, int num_blocks, int32_t* status, hipStream_t s, int fp8 = 0,
+                      float k_scale = 1.0f, float v_scale = 1.0f);
 int launch_argmax_reduce(const float* amax_v, const int* amax_i, int M, int ntiles, int32_t* out,
                          int32_t* status, hipStream_t s);
 
@@ -107,8 +109,8 @@ inline size_t attn_plan_ints(const AttnSplit& p) {
 
 struct AttnArgs {
     const uint16_t* q;            // bf16 [T][Hq][dh] (rotated)
-    const uint16_t* kplane;       // this layer's K plane [num_blocks][Hkv][16][dh]
-    const uint16_t* vplane;       // this layer's V plane [num_blocks][Hkv][dh][16]
+    const void* kplane;           // this layer's K plane [num_blocks][Hkv][16][dh] (bf16 or fp8 codes)
+    const void* vplane;           // this layer's V plane [num_blocks][Hkv][dh][16]
     const int32_t* positions;
     const uint8_t* is_rejected;
     const int32_t* cu_out;        // [C+1]
@@ -118,6 +120,8 @@ struct AttnArgs {
     AttnSplit sp;
     int32_t* plan;                // attn_plan_ints(sp) words, written by launch_attn_plan
     float scale_log2;             // log2(e) / sqrt(dh)
+    bool fp8;                     // planes hold E4M3 codes: value = code * k_scale (K), * v_scale (V)
+    float k_scale, v_scale;
     float* part_o;                // [scap][T][Hq][dh]
     float* part_ml;               // [scap][T][Hq][2]  (running max in log2 units, sum)
     uint16_t* out;                // bf16 [T][Hq][dh]

@@ -192,11 +192,19 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int 
 // V pages dim-major [dh][16]. The angle pos * theta^(-2i/dh) is formed and
 // reduced in double precision, so positions up to 20k keep full fp32
 // accuracy in cos/sin.
+// fp8 cache: the E4M3 code of x / scale, nearest with ties to even (the
+// hardware conversion), saturated to +-448
+__device__ __forceinline__ uint8_t to_e4m3(float x, float scale) {
+    const float y = fminf(fmaxf(x / scale, -448.0f), 448.0f);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.0f, 0, false) & 0xff);
+}
+
 __global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S, const int32_t* positions,
                                                          const int32_t* slots, int T, int Hq, int Hkv,
                                                          int dh, float theta, uint16_t* q_out,
-                                                         uint16_t* kplane, uint16_t* vplane,
-                                                         int num_blocks, int32_t* status) {
+                                                         void* kplane, void* vplane,
+                                                         int num_blocks, int32_t* status, int fp8,
+                                                         float k_scale, float v_scale) {
     const int o = blockIdx.y;
     const int half = dh / 2;
     const int npairs = (Hq + Hkv) * half;          // rotated pairs (q heads, then k heads)
@@ -227,14 +235,21 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S,
         double sd, cd;
         sincos((double)pos * inv, &sd, &cd);
         const float c = (float)cd, s = (float)sd;
-        const uint16_t r0 = f2bf(a * c - b * s), r1 = f2bf(b * c + a * s);
+        const float x0 = a * c - b * s, x1 = b * c + a * s;
         if (h < Hq) {
-            q_out[(size_t)o * Hq * dh + c0] = r0;
-            q_out[(size_t)o * Hq * dh + c0 + half] = r1;
+            q_out[(size_t)o * Hq * dh + c0] = f2bf(x0);
+            q_out[(size_t)o * Hq * dh + c0 + half] = f2bf(x1);
         } else if (write) {
-            uint16_t* kp = kplane + ((size_t)blk * Hkv + (h - Hq)) * PD_PAGE * dh + off * dh;
-            kp[i] = r0;
-            kp[i + half] = r1;
+            const size_t e = ((size_t)blk * Hkv + (h - Hq)) * PD_PAGE * dh + off * dh;
+            if (fp8) {
+                uint8_t* kp = static_cast<uint8_t*>(kplane) + e;
+                kp[i] = to_e4m3(x0, k_scale);
+                kp[i + half] = to_e4m3(x1, k_scale);
+            } else {
+                uint16_t* kp = static_cast<uint16_t*>(kplane) + e;
+                kp[i] = f2bf(x0);
+                kp[i + half] = f2bf(x1);
+            }
         }
     } else if (write) {
         const int idx = item - npairs;                 // V element: head idx / dh, dim idx % dh
@@ -246,7 +261,9 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S,
         for (int sp = 0; sp < kMaxSplits; ++sp)
             if (sp < S) v += pv[sp];
         const int g = idx / dh, cc = idx % dh;
-        vplane[((size_t)blk * Hkv + g) * PD_PAGE * dh + cc * PD_PAGE + off] = f2bf(v);
+        const size_t e = ((size_t)blk * Hkv + g) * PD_PAGE * dh + cc * PD_PAGE + off;
+        if (fp8) static_cast<uint8_t*>(vplane)[e] = to_e4m3(v, v_scale);
+        else static_cast<uint16_t*>(vplane)[e] = f2bf(v);
     }
 }
 
@@ -328,14 +345,15 @@ int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32
 }
 
 int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
-                      int Hq, int Hkv, int dh, float theta, uint16_t* q_out, uint16_t* kplane,
-                      uint16_t* vplane, int num_blocks, int32_t* status, hipStream_t s) {
+                      int Hq, int Hkv, int dh, float theta, uint16_t* q_out, void* kplane,
+                      void* vplane, int num_blocks, int32_t* status, hipStream_t s, int fp8,
+                      float k_scale, float v_scale) {
     if (T <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
     const int items = (Hq + Hkv) * (dh / 2) + Hkv * dh;
     hipLaunchKernelGGL(rope_cache_kernel, dim3((items + 255) / 256, T), dim3(256), 0, s, ws, S,
                        positions, slots, T, Hq, Hkv, dh, theta, q_out, kplane, vplane, num_blocks,
-                       status);
+                       status, fp8, k_scale, v_scale);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 

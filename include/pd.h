@@ -222,11 +222,19 @@ typedef struct {
                                    NULL), or NULL for fc(batch->hidden)                        */
     uint16_t*       hidden_out; /* bf16 [C*K][d] out: the final residual (before the final norm)
                                    of every sampled row, request-major, or NULL                */
+    int32_t         kv_fp8;     /* nonzero: kv_cache holds fp8 E4M3 codes ([Blog] "vLLM engineering
+                                   details": the serving setup keeps the KV cache in fp8), one byte
+                                   per element, same layout and index formula as the bf16 cache;
+                                   a stored code is value / scale, nearest with ties to even,
+                                   saturated to +-448, and reads back as code value * scale    */
+    const float*    kv_scales;  /* [host] [N][2] (K scale, V scale) per layer, each > 0 and finite;
+                                   NULL = 1.0. Read only when kv_fp8                            */
 } pd_forward_opts;
 
 /* pd_draft_forward with options (opts NULL = pd_draft_forward). Same
  * arguments, ownership and errors; hidden_d / hidden_out must be 16-byte
- * aligned. */
+ * aligned. With opts->kv_fp8 the kv_cache pointer addresses uint8 codes (pass
+ * it cast to uint16_t*); PD_EINVAL for a scale that is not > 0 and finite. */
 int pd_draft_forward_ex(pd_handle** h, const pd_model* m, const pd_batch_dims* dims,
                         const pd_batch* batch, const int32_t* block_table,
                         uint16_t* kv_cache, int32_t* draft_ids, float* logits,
