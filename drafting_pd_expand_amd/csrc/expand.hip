@@ -130,10 +130,20 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
         const int i = o - (in0 + r * (K - 1));
         const int n = s_n[r], v = s_v[r];
         const int32_t* bt_row = a.in.block_table + (size_t)r * maxb;
-        const uint16_t* src;
+        // the row copy's loads go out first (the first 2048 16-byte chunks: a
+        // 16384-wide row), so they overlap the metadata loads below
+        const uint16_t* src = i < n ? a.in.target_hidden + (size_t)(in0 + i) * H3 : a.in.h_shared;
+        const uint4* s4 = reinterpret_cast<const uint4*>(src);
+        uint4* d4 = reinterpret_cast<uint4*>(a.out.hidden + (size_t)o * H3);
+        const int n16 = H3 / 8;
+        uint4 buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = j * 256 + tid;
+            if (c < n16) buf[j] = s4[c];
+        }
         if (i < n) {
             const int j = in0 + i;
-            src = a.in.target_hidden + (size_t)j * H3;
             if (tid == 0) {
                 const int next = a.in.next_token_ids[r];
                 const int id = (i == v - 1 || i + 1 >= n) ? next : a.in.target_ids[j + 1];
@@ -149,7 +159,6 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
             }
         } else {
             const int m = i - n + 1;  // 1 .. K-1
-            src = a.in.h_shared;
             if (tid == 0) {
                 const int pos = a.in.target_pos[in0 + v - 1] + m;
                 a.out.input_ids[o] = a.d.mask_token_id;
@@ -160,12 +169,13 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
                 a.out.new_token_indices[r * K + m] = o;
             }
         }
-        // the row copy: every thread's 16-byte loads are issued before its stores
-        const uint4* s4 = reinterpret_cast<const uint4*>(src);
-        uint4* d4 = reinterpret_cast<uint4*>(a.out.hidden + (size_t)o * H3);
-        const int n16 = H3 / 8;
-        for (int c0 = 0; c0 < n16; c0 += 256 * 8) {
-            uint4 buf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = j * 256 + tid;
+            if (c < n16) d4[c] = buf[j];
+        }
+        // wider rows: the rest, loads before stores
+        for (int c0 = 256 * 8; c0 < n16; c0 += 256 * 8) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = c0 + j * 256 + tid;
