@@ -777,7 +777,7 @@ GemmPlan plan_gemm(int M, int N, int K, int epi) {
             const long tiles = (long)p.ntiles * p.mblocks;
             const int ksteps = (K + kTK - 1) / kTK;
             int s = (int)((512 + tiles - 1) / tiles);
-            if (s > 4) s = 4;
+            if (s > 8) s = 8;
             while (s > 1 && s * 4 > ksteps) --s;
             p.splits = s < 1 ? 1 : s;
         }
