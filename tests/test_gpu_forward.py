@@ -63,6 +63,21 @@ def _sample(b, K, k=3):
     return out[:k]
 
 
+@pytest.mark.parametrize("C,K,L", [(300, 3, 200), (1024, 2, 40)], ids=["c300", "c1024-max"])
+def test_many_requests_sampled(C, K, L):
+    """Large batches up to the 1024-request limit (plan, expansion and merge
+    over many requests): the whole expansion bit-exact, logits and argmax on
+    a spread of sampled requests (requests are independent)."""
+    w = synth.Workload(f"gqa64-c{C}", GQA64, C=C, K=K, context="fixed", L=L, seed=C + K)
+    _say(f"[forward] {w.name} K={K}")
+    c = Case(w).run()
+    assert c.status() == 0
+    reqs = sorted(set([0, C - 1, C // 2] + list(np.random.default_rng(C).choice(C, 5, replace=False))))
+    res = check_case(c, requests=reqs, check_cache=False)
+    _say(f"  worst logit err/RMS {res['worst_logit_ratio']:.4g} over {len(reqs)} requests")
+    c.close()
+
+
 @pytest.mark.parametrize("name", ["g_c1", "g_c4", "g_c64", "g_c64_k3", "g_c64_k5", "q_c16"])
 def test_full_size_workloads(name):
     w = synth.get_workload(name)
