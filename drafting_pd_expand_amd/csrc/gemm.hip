@@ -4,7 +4,7 @@
 // [Paper] = "P-EAGLE: Parallel-Drafting EAGLE with Scalable Training" summary
 // page, sec. 2 architecture; [arXiv] = its ScienceStack page, Figure 2) see
 // few rows per step: the draft batch has v_r + K - 1 computed rows per
-// request and the LM head C*K rows. Two kernels:
+// request and the LM head C*K rows. Three kernels:
 //
 //  * M <= 64 rows (low concurrency): every projection is a stream of its
 //    weight matrix. A persistent ring kernel (one workgroup per CU) copies W
@@ -12,7 +12,9 @@
 //    and runs v_mfma_f32_16x16x32_bf16 on them (W rows are the A operand, X
 //    rows the B operand, so a lane ends with 4 consecutive output columns of
 //    one row);
-//  * M > 64 rows: 128 x 128 output tiles staged through LDS.
+//  * 64 < M < 384 rows: 128 x 128 output tiles staged through LDS, two
+//    workgroups per CU;
+//  * M >= 384 rows: persistent 256 x 256 tiles fed by a global -> LDS ring.
 //
 // Projections with few output columns are split over workgroups along K.
 // Those splits never meet inside the GEMM: each writes an fp32 partial plane,
@@ -45,8 +47,12 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
 // straight from HBM into LDS (global_load_lds, 16 B per lane) through a ring
 // of NST stages of 128 reduction elements, so each CU keeps ~100 KB of
 // weights in flight with a single workgroup and no staging registers. A
-// stage holds the workgroup's W rows (16 output columns per wave, one row
-// group per matrix) and the matching X columns of all M rows; the waves read
+// stage holds the workgroup's W rows (NM groups of 16 output columns per
+// wave: for SwiGLU one group per matrix, otherwise NM adjacent column
+// groups of the one matrix) and the matching X columns of all M rows. Two
+// column groups per wave halve the X bytes staged per W byte (the X rows are
+// shared by every column of the tile), at the cost of fewer ring stages; the
+// waves read
 // their MFMA fragments from it (W is the A operand, X the B operand, in every
 // kernel of this file, so the epilogues agree). Rows are stored with
 // their 16-byte chunks XOR-permuted by (row & 15): the 16 lanes that one LDS
@@ -63,13 +69,13 @@ __device__ __align__(16) uint16_t g_gemm_zero[8];
 template <int WN, int NM, int MT>
 struct RingCfg {
     static constexpr int NT = 64 * WN;
-    static constexpr int WR = 16 * WN * NM;   // W rows per stage
+    static constexpr int WR = 16 * WN * NM;   // W rows per stage (64 or 128)
     static constexpr int XR = 16 * MT;        // X rows per stage
     static constexpr int WL = WR * 16 / NT;   // 16-byte W loads per thread per stage
     static constexpr int XL = XR * 16 / NT;   // 16-byte X loads per thread per stage
     static constexpr int L = WL + XL;
     static constexpr int SE = (WR + XR) * kRS;   // elements per stage
-    static constexpr int NST = MT == 1 ? 6 : (MT == 2 ? 5 : 4);
+    static constexpr int NST = WR == 64 ? (MT == 1 ? 6 : (MT == 2 ? 5 : 4)) : (MT == 1 ? 4 : 3);
     static_assert(WL * NT == WR * 16 && XL * NT == XR * 16, "whole loads per thread");
 };
 
@@ -102,6 +108,8 @@ template <int WN, int NM, int MT, int EPI>
 __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
     using Cf = RingCfg<WN, NM, MT>;
     constexpr int NT = Cf::NT, NST = Cf::NST, L = Cf::L, WL = Cf::WL, XL = Cf::XL;
+    constexpr bool PAIR = (EPI == EPI_SWIGLU);          // row groups = gate, up of the same columns
+    constexpr int TW = 16 * WN * (PAIR ? 1 : NM);       // output columns per tile
     __shared__ __align__(16) uint16_t ring[NST * Cf::SE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 
     const int ksteps = (a.K + kRS - 1) / kRS;
     const int per = (ksteps + a.splits - 1) / a.splits;
-    const int ntn = (a.N + 16 * WN - 1) / (16 * WN);   // column tiles
+    const int ntn = (a.N + TW - 1) / TW;   // column tiles
     const int nitems = ntn * a.splits;
     const int G = gridDim.x;
 
@@ -167,20 +175,21 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
                 ike = min(ksteps, (sp + 1) * per);
             }
         }
-        const int n0 = (iitem % ntn) * 16 * WN;
+        const int n0 = (iitem % ntn) * TW;
         const int k0 = iks * kRS;
         const unsigned sbase = lds0 + (unsigned)(slot * Cf::SE) * 2u;
         // whole tile inside N and whole stage inside K: no per-lane bounds
-        const bool inner = n0 + 16 * WN <= a.N && k0 + kRS <= a.K;
+        const bool inner = n0 + TW <= a.N && k0 + kRS <= a.K;
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
-            const int q = j * NT / (16 * 16 * WN);   // matrix of this load (compile-time)
-            const uint16_t* tile = (q == 0 ? a.W : a.W2) + (size_t)n0 * a.K + k0;
+            const int q = j * NT / (16 * 16 * WN);   // row group of this load (compile-time)
+            const int nq = n0 + (PAIR ? 0 : q * 16 * WN);
+            const uint16_t* tile = (PAIR && q == 1 ? a.W2 : a.W) + (size_t)nq * a.K + k0;
             const uint16_t* src;
             if (inner) {
                 src = tile + wofs[j];
             } else {
-                const int n = n0 + wrr[j], k = k0 + wch[j];
+                const int n = nq + wrr[j], k = k0 + wch[j];
                 src = (n < a.N && k < a.K) ? tile + wofs[j] : zp;
             }
             __builtin_amdgcn_global_load_lds((void*)src,
@@ -235,47 +244,56 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             }
         }
 
-        // lane holds rows m = 16t + r16 and columns n .. n+3
-        const int n = (it % ntn) * 16 * WN + 16 * wave + 4 * g4;
+        // lane holds rows m = 16t + r16 and columns n .. n+3 of each column group q
+        const int n0 = (it % ntn) * TW + 16 * wave + 4 * g4;
         if constexpr (EPI == EPI_ARGMAX) {
-            const int tile = (it % ntn) * WN + wave;   // 16-column group
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int m = 16 * t + r16;
-                float bv = -FLT_MAX;
-                int bi = INT_MAX;
-                if (n < a.N) {
+            for (int q = 0; q < NM; ++q) {
+                const int n = n0 + q * 16 * WN;
+                const int tile = n >> 4;   // 16-column group
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) better(bv, bi, acc[t][0][e], n + e);
-                    if (a.logits && m < a.M)
-                        *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[t][0];
-                }
+                for (int t = 0; t < MT; ++t) {
+                    const int m = 16 * t + r16;
+                    float bv = -FLT_MAX;
+                    int bi = INT_MAX;
+                    if (n < a.N) {
 #pragma unroll
-                for (int off = 16; off <= 32; off <<= 1) {
-                    const float ov = __shfl_xor(bv, off, kWave);
-                    const int oi = __shfl_xor(bi, off, kWave);
-                    better(bv, bi, ov, oi);
-                }
-                if (g4 == 0 && m < a.M && 16 * tile < a.N) {
-                    a.amax_v[(size_t)m * a.ntiles + tile] = bv;
-                    a.amax_i[(size_t)m * a.ntiles + tile] = bi;
+                        for (int e = 0; e < 4; ++e) better(bv, bi, acc[t][q][e], n + e);
+                        if (a.logits && m < a.M)
+                            *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[t][q];
+                    }
+#pragma unroll
+                    for (int off = 16; off <= 32; off <<= 1) {
+                        const float ov = __shfl_xor(bv, off, kWave);
+                        const int oi = __shfl_xor(bi, off, kWave);
+                        better(bv, bi, ov, oi);
+                    }
+                    if (g4 == 0 && m < a.M && 16 * tile < a.N) {
+                        a.amax_v[(size_t)m * a.ntiles + tile] = bv;
+                        a.amax_i[(size_t)m * a.ntiles + tile] = bi;
+                    }
                 }
             }
         } else {
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
                 const int m = 16 * t + r16;
-                if (m >= a.M || n >= a.N) continue;
+                if (m >= a.M) continue;
                 if constexpr (EPI == EPI_PARTIAL) {
-                    *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[t][0];
+#pragma unroll
+                    for (int q = 0; q < NM; ++q) {
+                        const int n = n0 + q * 16 * WN;
+                        if (n < a.N) *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[t][q];
+                    }
                 } else {
+                    if (n0 >= a.N) continue;
                     float h[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) h[e] = silu(acc[t][0][e]) * acc[t][NM - 1][e];
                     uint2 pk;
                     pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
                     pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
-                    *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
+                    *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n0) = pk;
                 }
             }
         }
@@ -708,10 +726,9 @@ int launch_tiled(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
-template <int EPI>
-int launch_ring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+template <int EPI, int NM>
+int launch_ring_nm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     constexpr int WN = EPI == EPI_SWIGLU ? 2 : 4;
-    constexpr int NM = EPI == EPI_SWIGLU ? 2 : 1;
     if (p.wn != WN) return PD_EINVAL;
     switch (p.mt) {
         case 1: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 1, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
@@ -720,6 +737,17 @@ int launch_ring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
         default: return PD_EINVAL;
     }
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+template <int EPI>
+int launch_ring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    if constexpr (EPI == EPI_SWIGLU) {
+        return p.nm == 2 ? launch_ring_nm<EPI, 2>(p, a, s) : PD_EINVAL;
+    } else {
+        if (p.nm == 1) return launch_ring_nm<EPI, 1>(p, a, s);
+        if (p.nm == 2) return launch_ring_nm<EPI, 2>(p, a, s);
+        return PD_EINVAL;
+    }
 }
 
 template <int EPI>
@@ -733,8 +761,9 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-GemmPlan plan_gemm(int M, int N, int K, int epi) {
+GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
     GemmPlan p;
+    p.nm = 1;
     p.kind = M <= 64 ? GEMM_RING : (M < 384 ? GEMM_TILED : GEMM_BIG);
     p.splits = 1;
     p.grid = 0;
@@ -783,13 +812,16 @@ GemmPlan plan_gemm(int M, int N, int K, int epi) {
         }
         return p;
     }
-    // persistent LDS ring: 16 output columns per wave, 4 waves (2 for the
-    // gate/up pair); K splits (partial planes) chosen to minimise the stages
-    // the busiest of the <= 256 workgroups streams
+    // persistent LDS ring: nm groups of 16 output columns per wave, 4 waves
+    // (2 for the gate/up pair, whose two groups are the two matrices); K
+    // splits (partial planes) chosen to minimise the stages the busiest of
+    // the <= 256 workgroups streams
     p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     p.mblocks = 1;
     p.wn = (epi == EPI_SWIGLU) ? 2 : 4;
-    const int ntn = (N + 16 * p.wn - 1) / (16 * p.wn);
+    p.nm = (epi == EPI_SWIGLU) ? 2 : ring_nm;
+    const int tw = 16 * p.wn * (epi == EPI_SWIGLU ? 1 : p.nm);
+    const int ntn = (N + tw - 1) / tw;
     const int ksteps = (K + kRS - 1) / kRS;
     if (epi == EPI_PARTIAL) {
         long best = -1;
@@ -804,6 +836,23 @@ GemmPlan plan_gemm(int M, int N, int K, int epi) {
     p.ntiles = (epi == EPI_ARGMAX) ? (N + 15) / 16 : ntn;
     const long items = (long)ntn * p.splits;
     p.grid = (int)(items < 256 ? items : 256);
+    return p;
+}
+
+// Projections of 17..64 rows take two column groups per wave whenever that
+// plan still spreads over >= 240 of the 256 CUs: with two or four 16-row X
+// tiles the X bytes staged per stage are a large share, and the wider tile
+// halves them per weight byte (LM head at 28 rows in the drafting step: 231
+// -> 228 us). With one X tile the deeper ring of the narrow tile is faster
+// (LM head at 7 rows: 207 vs 210 us), and so is the narrow tile where the
+// wide one leaves CUs idle (the d-wide outputs, whose K splits are capped
+// at 8).
+GemmPlan plan_gemm(int M, int N, int K, int epi) {
+    const GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
+    if (p.kind == GEMM_RING && p.mt >= 2 && epi != EPI_SWIGLU) {
+        const GemmPlan w = plan_gemm_nm(M, N, K, epi, 2);
+        if (w.grid >= 240) return w;
+    }
     return p;
 }
 

@@ -54,13 +54,15 @@ struct GemmPlan {
     int kind;      // GemmKind
     int mt;        // ring: 16-row X tiles (1, 2 or 4)
     int mblocks;   // tiled / big: workgroups along M
-    int wn;        // waves per workgroup (ring: 16 output columns each)
+    int wn;        // waves per workgroup
+    int nm;        // ring: groups of 16 output columns per wave
     int ntiles;    // column tiles (ARGMAX: groups of the max/argmax partial results per row)
     int splits;    // K splits (EPI_PARTIAL: one fp32 plane each)
     int grid;      // ring / big: persistent workgroups
 };
 
 GemmPlan plan_gemm(int M, int N, int K, int epi);
+GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm);
 size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi);
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 
