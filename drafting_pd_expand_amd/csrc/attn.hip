@@ -58,6 +58,9 @@ constexpr float kRescale = 8.0f;
 constexpr int kBtMax = 512;               // block-table entries of one split cached in LDS
 constexpr int kMaxSplitKeys = kBtMax * PD_PAGE;
 constexpr int kMaxSplits = 128;           // splits of one request the merge combines
+// split-kernel workgroups resident at once (two per CU: ~66 KB of LDS each)
+constexpr int kRoundSlots = 512;
+constexpr int kOneRoundMaxKeys = 512;
 
 // K and V of pages that are past the split end or invalid come from here
 // (zero-initialised at load; nothing writes it).
@@ -184,6 +187,17 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
     }
     const long long tw = a.sp.target_wg;
     long long sl = (total * a.Hkv + tw - 1) / tw;
+    // Few keys in all: the shortest split whose (unit, kv head) workgroups
+    // all fit in one round of kRoundSlots (units <= total / sl + C per head),
+    // as long as that split stays short. A second round costs more than the
+    // longer splits: C = 4 with 17.7k keys, 22 us at 304 keys / 472
+    // workgroups vs 27 us at 128 keys / 1120 and at 256 keys / 568 (26 us
+    // at 512 keys / 288); with 13k keys, 19 us at 224 keys vs 22 at 128.
+    const long long free_slots = kRoundSlots - (long long)a.Hkv * a.C;
+    if (free_slots > 0) {
+        const long long one = (total * a.Hkv + free_slots - 1) / free_slots;
+        if (one <= kOneRoundMaxKeys) sl = max(sl, one);
+    }
     sl = max(sl, (long long)a.sp.min_split);
     sl = max(sl, (long long)((mx + a.sp.scap - 1) / a.sp.scap));
     sl = (sl + PD_PAGE - 1) / PD_PAGE * PD_PAGE;
