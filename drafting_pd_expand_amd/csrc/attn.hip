@@ -155,6 +155,8 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
     __shared__ long long s_sum[16];
     __shared__ int s_max[16];
     __shared__ int s_cnt[16];
+    __shared__ int s_incl[PD_MAX_C];   // inclusive prefix of the split counts
+    __shared__ int4 s_req[PD_MAX_C];   // validated {row0, row1, seq} of every request
     const int r = threadIdx.x, lane = r & 63, w = r >> 6;
     int seq = 0, row0 = 0, row1 = 0;
     if (r < a.C) {
@@ -225,22 +227,33 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
     const int first = before + incl - ns;
     if (r < a.C) {
         a.plan[kPlanNs + r] = ns;
-        for (int s = 0; s < ns; ++s) {
-            const int u = first + s;
-            if (u >= a.sp.max_units) {   // excluded by the host's bound on units
-                flag(a.status, PD_STATUS_BAD_ROW);
-                break;
-            }
-            const int kb = s * split_len;
-            const int ke = min(seq, kb + split_len);
-            int4* rec = reinterpret_cast<int4*>(a.plan + kPlanUnits + (size_t)u * kPlanRec);
-            rec[0] = make_int4(r, s, ns, row0);
-            rec[1] = make_int4(row1, kb, ke, 0);
-        }
+        s_incl[r] = first + ns;
+        s_req[r] = make_int4(row0, row1, seq, 0);
     }
     if (r == 0) {
+        if (units > a.sp.max_units) flag(a.status, PD_STATUS_BAD_ROW);   // excluded by the host's bound
         a.plan[0] = min(units, a.sp.max_units);
         a.plan[1] = split_len;
+    }
+    __syncthreads();
+    // unit records, spread over the block: unit u belongs to the first
+    // request whose inclusive split count exceeds u (never one without splits)
+    const int nu = min(units, a.sp.max_units);
+    for (int u = r; u < nu; u += blockDim.x) {
+        int lo = 0, hi = a.C - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_incl[mid] > u) hi = mid; else lo = mid + 1;
+        }
+        const int q = lo;
+        const int nsq = s_incl[q] - (q > 0 ? s_incl[q - 1] : 0);
+        const int sq = u - (s_incl[q] - nsq);
+        const int4 rq = s_req[q];
+        const int kb = sq * split_len;
+        const int ke = min(rq.z, kb + split_len);
+        int4* rec = reinterpret_cast<int4*>(a.plan + kPlanUnits + (size_t)u * kPlanRec);
+        rec[0] = make_int4(q, sq, nsq, rq.x);
+        rec[1] = make_int4(rq.y, kb, ke, 0);
     }
 }
 

@@ -23,8 +23,9 @@
 // waits on another, so no device-wide fence is needed, and the result is
 // deterministic. Epilogues: fp32 partial plane, SwiGLU on a pair of matrices
 // (gate and up rows streamed side by side, one bf16 rounding), and LM-head
-// max/argmax per column group (lowest index on ties) with optional fp32
-// logits.
+// max/argmax (lowest index on ties) with optional fp32 logits: one partial
+// per column tile, or in the few-row kernel one per wave, which keeps its
+// best over every column it computes.
 #include <float.h>
 #include <limits.h>
 
@@ -211,6 +212,15 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
     ring_wait<0>();   // row gathers done before the ring starts counting
     for (int st = 0; st < NST - 1 && st < total; ++st) issue(st);
 
+    // LM head: a lane's best (value, lowest index) of row 16t + r16 over every
+    // column it sees, across all of the workgroup's items
+    float runv[MT];
+    int runi[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        runv[t] = -FLT_MAX;
+        runi[t] = INT_MAX;
+    }
     int qc = 0;   // stages consumed
     for (int it = blockIdx.x; it < nitems; it += G) {
         const int sp = it / ntn;
@@ -250,28 +260,14 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 #pragma unroll
             for (int q = 0; q < NM; ++q) {
                 const int n = n0 + q * 16 * WN;
-                const int tile = n >> 4;   // 16-column group
+                if (n >= a.N) continue;
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
                     const int m = 16 * t + r16;
-                    float bv = -FLT_MAX;
-                    int bi = INT_MAX;
-                    if (n < a.N) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) better(bv, bi, acc[t][q][e], n + e);
-                        if (a.logits && m < a.M)
-                            *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[t][q];
-                    }
-#pragma unroll
-                    for (int off = 16; off <= 32; off <<= 1) {
-                        const float ov = __shfl_xor(bv, off, kWave);
-                        const int oi = __shfl_xor(bi, off, kWave);
-                        better(bv, bi, ov, oi);
-                    }
-                    if (g4 == 0 && m < a.M && 16 * tile < a.N) {
-                        a.amax_v[(size_t)m * a.ntiles + tile] = bv;
-                        a.amax_i[(size_t)m * a.ntiles + tile] = bi;
-                    }
+                    for (int e = 0; e < 4; ++e) better(runv[t], runi[t], acc[t][q][e], n + e);
+                    if (a.logits && m < a.M)
+                        *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[t][q];
                 }
             }
         } else {
@@ -295,6 +291,25 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
                     pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
                     *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n0) = pk;
                 }
+            }
+        }
+    }
+    if constexpr (EPI == EPI_ARGMAX) {
+        // one (value, index) per row per wave: entry blockIdx.x * WN + wave
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            float bv = runv[t];
+            int bi = runi[t];
+#pragma unroll
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ov = __shfl_xor(bv, off, kWave);
+                const int oi = __shfl_xor(bi, off, kWave);
+                better(bv, bi, ov, oi);
+            }
+            const int m = 16 * t + r16;
+            if (g4 == 0 && m < a.M) {
+                a.amax_v[(size_t)m * a.ntiles + blockIdx.x * WN + wave] = bv;
+                a.amax_i[(size_t)m * a.ntiles + blockIdx.x * WN + wave] = bi;
             }
         }
     }
@@ -833,9 +848,10 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
             if (best < 0 || span < best) { best = span; p.splits = sp; }
         }
     }
-    p.ntiles = (epi == EPI_ARGMAX) ? (N + 15) / 16 : ntn;
     const long items = (long)ntn * p.splits;
     p.grid = (int)(items < 256 ? items : 256);
+    // LM head: one max/argmax partial per row per wave
+    p.ntiles = (epi == EPI_ARGMAX) ? p.grid * p.wn : ntn;
     return p;
 }
 

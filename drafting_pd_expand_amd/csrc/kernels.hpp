@@ -25,7 +25,8 @@ int launch_ar_advance(const pd_batch_dims& d, const pd_batch& prev, const int32_
 enum Epi : int {
     EPI_PARTIAL = 0,  // fp32 partial plane per K split: ws[split][M][N] (the consumer sums)
     EPI_SWIGLU = 1,   // y_bf16 = silu(X W^T) * (X W2^T)
-    EPI_ARGMAX = 2,   // per (row, column tile) max / argmax (+ optional fp32 logits)
+    EPI_ARGMAX = 2,   // max / argmax partials per row (+ optional fp32 logits): one per
+                      // (row, column tile), or per (row, wave) in the few-row kernel
 };
 
 struct GemmArgs {
@@ -90,7 +91,9 @@ int launch_argmax_reduce(const float* amax_v, const int* amax_i, int M, int ntil
 // ---------------------------------------------------------------- attention
 // Split-KV plan, computed on the device once per forward from seq_lens:
 // split_len = max(min_split, ceil(sum_r seq_r * Hkv / target_wg),
-// ceil(max_r seq_r / scap)) rounded up to a page; request r gets
+// ceil(max_r seq_r / scap)) rounded up to a page -- or, where a split of at
+// most 512 keys puts every workgroup into one round of 512 resident ones, the
+// shortest such split (if longer); request r gets
 // ns_r = ceil(seq_r / split_len) units of work (one workgroup per unit and kv
 // head). The host sizes everything from bounds it knows without a sync.
 struct AttnSplit {

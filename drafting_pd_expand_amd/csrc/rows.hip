@@ -281,7 +281,7 @@ __global__ __launch_bounds__(1024) void argmax_reduce_kernel(const float* amax_v
     const int m = blockIdx.x;
     float bv = -FLT_MAX;
     int bi = INT_MAX;
-    // a row's partials (up to ~12.6k) in one round of independent loads per thread
+    // a row's partials (a few thousand at most) in one round of independent loads per thread
 #pragma unroll 16
     for (int t = threadIdx.x; t < ntiles; t += 1024)
         better(bv, bi, amax_v[(size_t)m * ntiles + t], amax_i[(size_t)m * ntiles + t]);
