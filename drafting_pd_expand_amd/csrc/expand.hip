@@ -13,8 +13,8 @@
 //
 // Design for gfx950: every workgroup recomputes the per-request start
 // indices with a block-wide prefix sum over <= 1024 counts (4 KB, L2
-// resident), so no second launch or global scratch is needed; it then owns a
-// few output rows, writes their metadata and copies each 3d-wide bf16 row with
+// resident), so no second launch or global scratch is needed; it then owns
+// one (or two) output rows, writes their metadata and copies each 3d-wide bf16 row with
 // 16-byte vector loads/stores (a full row is contiguous, so every wave issues
 // fully coalesced 1 KB transactions).
 #include "common.hpp"
@@ -24,13 +24,12 @@ namespace pd {
 
 namespace {
 
-constexpr int kRowsPerBlock = 2;
-
 struct ExpandArgs {
     pd_batch_dims d;
     pd_expand_in in;
     pd_batch out;
     int T_out;
+    int rows_per_block;   // 1, or 2 for very long batches (fewer redundant prefix sums)
 };
 
 __device__ __forceinline__ int slot_of(const int32_t* bt_row, int pos, int bs, int max_blocks,
@@ -47,7 +46,7 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
     __shared__ int s_in[PD_MAX_C + 1];  // first input row of each request
     __shared__ int s_n[PD_MAX_C];
     __shared__ int s_v[PD_MAX_C];
-    __shared__ int s_scan[256];
+    __shared__ int s_wsum[4];
     __shared__ int s_bad;
 
     const int C = a.d.C, K = a.d.K, tid = threadIdx.x;
@@ -77,23 +76,28 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
         sum += n;
     }
     if (bad) atomicOr(&s_bad, 1);
-    // inclusive scan of the per-thread sums (Hillis-Steele over 256 entries)
-    s_scan[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int t = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += t;
-        __syncthreads();
+    // inclusive scan of the per-thread sums: within each wave by lane
+    // shifts, then across the 4 waves through LDS
+    const int lane = tid & 63, wv = tid >> 6;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
     }
-    int run = s_scan[tid] - sum;
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) before += w < wv ? s_wsum[w] : 0;
+    int run = before + incl - sum;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = tid * 4 + i;
         if (r < C) s_in[r] = run;
         run += cnt[i];
     }
-    if (tid == 0) s_in[C] = s_scan[255];
+    if (tid == 0) s_in[C] = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
     __syncthreads();
     if (s_in[C] != T_in) s_bad = 1;  // benign race: every writer stores 1
     __syncthreads();
@@ -116,8 +120,8 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
         if (tid == 0) a.out.cu_out[C] = a.T_out;
     }
 
-    for (int rr = 0; rr < kRowsPerBlock; ++rr) {
-        const int o = blockIdx.x * kRowsPerBlock + rr;
+    for (int rr = 0; rr < a.rows_per_block; ++rr) {
+        const int o = blockIdx.x * a.rows_per_block + rr;
         if (o >= a.T_out) break;
         // request of row o: the last r whose first output row is <= o
         int lo = 0, hi = C - 1;
@@ -327,7 +331,11 @@ int launch_expand(const pd_batch_dims& d, const pd_expand_in& in, const pd_batch
     a.in = in;
     a.out = out;
     a.T_out = d.T_in + d.C * (d.K - 1);
-    const int grid = (a.T_out + kRowsPerBlock - 1) / kRowsPerBlock;
+    // one output row per workgroup (their dependent load chains run side by
+    // side); two for very long batches, where each workgroup's prefix sum
+    // over the counts is the larger cost
+    a.rows_per_block = a.T_out <= 8192 ? 1 : 2;
+    const int grid = (a.T_out + a.rows_per_block - 1) / a.rows_per_block;
     hipLaunchKernelGGL(expand_kernel, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
