@@ -36,7 +36,7 @@
 // fragment read touches 8 different bank groups. Pages past the split or
 // with a bad block-table entry are read from a zero page and masked.
 // Each split writes an unnormalized partial (O, running max, running sum);
-// a merge kernel combines the splits in order (deterministic). A request
+// a merge kernel combines the splits in a fixed order (deterministic). A request
 // with a single split writes its normalized bf16 output directly.
 #include <math.h>
 
@@ -527,12 +527,18 @@ __global__ __launch_bounds__((64 * AttnCfg<DH, F8>::NW)) void attn_split_kernel(
     }
 }
 
-// out[row][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in
-// order. One wave per (row, q head): the split weights are formed across
-// lanes, then each lane accumulates its dims over the splits. Requests with
-// one split were written by the split kernel.
+// out[row][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. One wave per
+// (row, q head): the split weights are formed across lanes (lane s holds
+// split s); the partial outputs are read as float4s, DH/4 lanes per split and
+// 64/(DH/4) splits per load instruction, all of a chunk's loads issued before
+// any is used; each lane sums its splits in order and the lane groups are
+// then added in a fixed tree (deterministic). Requests with one split were
+// written by the split kernel.
 template <int DH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+    constexpr int LPS = DH / 4;        // lanes per split
+    constexpr int SPI = 64 / LPS;      // splits per load instruction
+    constexpr int CHUNK = 16;          // load instructions in flight per lane
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int pair = blockIdx.x * 4 + wave;
     if (pair >= a.T * a.Hq) return;
@@ -547,12 +553,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int nsr = a.plan[kPlanNs + r];
     if (inr && nsr == 1) return;
     const int ns = (inr && !a.is_rejected[row]) ? min(nsr, kMaxSplits) : 0;
-    constexpr int PER = DH / 64;
     const size_t stride = (size_t)a.T * a.Hq;   // between splits, in (row, head) units
     const size_t base = (size_t)row * a.Hq + h;
+    const int sub = lane / LPS, dq = lane % LPS;   // split within an instruction, dim quad
     float2 ml0 = make_float2(kNegInf, 0.f), ml1 = make_float2(kNegInf, 0.f);
     if (lane < ns) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + base) * 2);
     if (lane + 64 < ns) ml1 = *reinterpret_cast<const float2*>(a.part_ml + ((lane + 64) * stride + base) * 2);
+    // the first chunk of partial outputs goes out with the (m, l) loads
+    const int ninst = (ns + SPI - 1) / SPI;
+    float4 v[CHUNK];
+#pragma unroll
+    for (int k = 0; k < CHUNK; ++k) {
+        const int sp = k * SPI + sub;
+        v[k] = sp < ns ? *reinterpret_cast<const float4*>(a.part_o + (sp * stride + base) * DH + 4 * dq)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     const float M = wave_max(fmaxf(ml0.x, ml1.x));
     float w0 = 0.f, w1 = 0.f, L = 0.f;
     if (M != kNegInf) {
@@ -561,36 +576,43 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
         L = w0 * ml0.y + w1 * ml1.y;
     }
     L = wave_sum(L);
-    float acc[PER];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i0 = 0; i0 < ninst; i0 += CHUNK) {
+        if (i0 > 0) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-    // all split loads of a lane are independent: issue them in groups
-    int sp = 0;
-    for (; sp + 8 <= ns; sp += 8) {
-        float v[8][PER];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float* po = a.part_o + ((sp + k) * stride + base) * DH;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) v[k][i] = po[lane + 64 * i];
+            for (int k = 0; k < CHUNK; ++k) {
+                const int sp = (i0 + k) * SPI + sub;
+                v[k] = sp < ns ? *reinterpret_cast<const float4*>(a.part_o + (sp * stride + base) * DH + 4 * dq)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float w = __shfl(sp + k < 64 ? w0 : w1, (sp + k) & 63, kWave);
-#pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] += w * v[k][i];
+        for (int k = 0; k < CHUNK; ++k) {
+            const int s0 = (i0 + k) * SPI;   // first split of this instruction (uniform; 64 | s0 + SPI)
+            const int sp = s0 + sub;
+            const float w = __shfl(s0 < 64 ? w0 : w1, sp & 63, kWave);
+            if (sp < ns) {
+                acc.x += w * v[k].x;
+                acc.y += w * v[k].y;
+                acc.z += w * v[k].z;
+                acc.w += w * v[k].w;
+            }
         }
     }
-    for (; sp < ns; ++sp) {
-        const float w = __shfl(sp < 64 ? w0 : w1, sp & 63, kWave);
-        const float* po = a.part_o + (sp * stride + base) * DH;
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += w * po[lane + 64 * i];
+    for (int off = LPS; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off, kWave);
+        acc.y += __shfl_xor(acc.y, off, kWave);
+        acc.z += __shfl_xor(acc.z, off, kWave);
+        acc.w += __shfl_xor(acc.w, off, kWave);
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    uint16_t* op = a.out + base * DH;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) op[lane + 64 * i] = f2bf(acc[i] * inv);
+    if (sub == 0) {
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+        uint2 pk;
+        pk.x = uint32_t(f2bf(acc.x * inv)) | (uint32_t(f2bf(acc.y * inv)) << 16);
+        pk.y = uint32_t(f2bf(acc.z * inv)) | (uint32_t(f2bf(acc.w * inv)) << 16);
+        *reinterpret_cast<uint2*>(a.out + base * DH + 4 * dq) = pk;
+    }
 }
 
 template <int DH>
@@ -633,6 +655,10 @@ AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks)
     scap = std::max(scap, (reach + kMaxSplitKeys - 1) / kMaxSplitKeys);
     p.scap = (int)std::max(1LL, std::min(scap, (long long)kMaxSplits));
     p.max_units = (p.target_wg + Hkv - 1) / Hkv + C;
+    // every split holds >= min_split keys of a request of <= reach keys:
+    // short batches launch only the workgroups they can use
+    const long long most = (long long)C * ((reach + p.min_split - 1) / p.min_split);
+    if (most < p.max_units) p.max_units = (int)std::max(1LL, most);
     return p;
 }
 
