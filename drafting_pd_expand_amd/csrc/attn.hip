@@ -543,13 +543,25 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     const int pair = blockIdx.x * 4 + wave;
     if (pair >= a.T * a.Hq) return;
     const int row = pair / a.Hq, h = pair % a.Hq;
-    int lo = 0, hi = a.C - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (a.cu_out[mid] <= row) lo = mid; else hi = mid - 1;
+    // request of the row = the last r with cu_out[r] <= row, found by the
+    // whole wave: lane l tests start l * step, then the 64 starts after the
+    // last hit (two dependent loads for up to 4096 requests, not log2 C)
+    int r = 0;
+    bool found = true;
+    {
+        const int step = (a.C + 63) / 64;
+        const int i1 = lane * step;
+        const uint64_t m1 = __ballot(i1 < a.C && a.cu_out[i1] <= row);
+        if (m1 == 0) {
+            found = false;
+        } else {
+            const int b = (63 - __clzll((long long)m1)) * step;
+            const int i2 = b + lane;
+            const uint64_t m2 = __ballot(lane < step && i2 < a.C && a.cu_out[i2] <= row);
+            r = b + (63 - __clzll((long long)m2));   // m2 holds lane 0: cu_out[b] <= row
+        }
     }
-    const int r = lo;
-    const bool inr = a.cu_out[r] <= row && row < a.cu_out[r + 1];
+    const bool inr = found && row < a.cu_out[r + 1];
     const int nsr = a.plan[kPlanNs + r];
     if (inr && nsr == 1) return;
     const int ns = (inr && !a.is_rejected[row]) ? min(nsr, kMaxSplits) : 0;
