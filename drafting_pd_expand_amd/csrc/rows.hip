@@ -190,8 +190,11 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int 
 // bf16 once, after the rotation. One thread per rotation pair (or V element),
 // so every thread's loads go out together. K pages are token-major [16][dh],
 // V pages dim-major [dh][16]. The angle pos * theta^(-2i/dh) is formed and
-// reduced in double precision, so positions up to 20k keep full fp32
-// accuracy in cos/sin.
+// reduced to [-pi, pi] in double precision (theta^(-2/dh) comes from the
+// host, its i-th power by repeated squaring: <= 12 double products, ~1e-15
+// relative; the reduction subtracts k * 2pi in two parts, Cody and Waite's
+// method), so positions up to 20k keep full fp32 accuracy in cos/sin, which
+// are then taken in fp32 on the reduced angle.
 // fp8 cache: the E4M3 code of x / scale, nearest with ties to even (the
 // hardware conversion), saturated to +-448
 __device__ __forceinline__ uint8_t to_e4m3(float x, float scale) {
@@ -201,7 +204,7 @@ __device__ __forceinline__ uint8_t to_e4m3(float x, float scale) {
 
 __global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S, const int32_t* positions,
                                                          const int32_t* slots, int T, int Hq, int Hkv,
-                                                         int dh, float theta, uint16_t* q_out,
+                                                         int dh, double inv_step, uint16_t* q_out,
                                                          void* kplane, void* vplane,
                                                          int num_blocks, int32_t* status, int fp8,
                                                          float k_scale, float v_scale) {
@@ -231,10 +234,17 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S,
 #pragma unroll
         for (int sp = 0; sp < kMaxSplits; ++sp)
             if (sp < S) { a += pa[sp]; b += pb[sp]; }
-        const double inv = exp(-(2.0 * i / dh) * log((double)theta));
-        double sd, cd;
-        sincos((double)pos * inv, &sd, &cd);
-        const float c = (float)cd, s = (float)sd;
+        double inv = 1.0, pw = inv_step;   // inv_step^i = theta^(-2i/dh)
+        for (int e = i; e != 0; e >>= 1) {
+            if (e & 1) inv *= pw;
+            pw *= pw;
+        }
+        const double ang = (double)pos * inv;
+        const double kq = rint(ang * 0.15915494309189535);             // 1 / (2 pi)
+        double red = fma(-kq, 6.283185307179586, ang);                  // 2 pi, leading part
+        red = fma(-kq, 2.4492935982947064e-16, red);                     // 2 pi, remainder
+        float s, c;
+        sincosf((float)red, &s, &c);
         const float x0 = a * c - b * s, x1 = b * c + a * s;
         if (h < Hq) {
             q_out[(size_t)o * Hq * dh + c0] = f2bf(x0);
@@ -351,8 +361,9 @@ int launch_rope_cache(const float* ws, int S, const int32_t* positions, const in
     if (T <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
     const int items = (Hq + Hkv) * (dh / 2) + Hkv * dh;
+    const double inv_step = std::pow((double)theta, -2.0 / dh);
     hipLaunchKernelGGL(rope_cache_kernel, dim3((items + 255) / 256, T), dim3(256), 0, s, ws, S,
-                       positions, slots, T, Hq, Hkv, dh, theta, q_out, kplane, vplane, num_blocks,
+                       positions, slots, T, Hq, Hkv, dh, inv_step, q_out, kplane, vplane, num_blocks,
                        status, fp8, k_scale, v_scale);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
