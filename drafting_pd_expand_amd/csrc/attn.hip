@@ -60,6 +60,9 @@ constexpr int kMaxSplitKeys = kBtMax * PD_PAGE;
 constexpr int kMaxSplits = 128;           // splits of one request the merge combines
 // split-kernel workgroups resident at once (two per CU: ~66 KB of LDS each)
 constexpr int kRoundSlots = 512;
+// merge-kernel workgroups resident at once with one head per wave (four per
+// CU, register-bound)
+constexpr int kMergeRoundWgs = 1024;
 constexpr int kOneRoundMaxKeys = 512;
 
 // K and V of pages that are past the split end or invalid come from here
@@ -528,21 +531,22 @@ __global__ __launch_bounds__((64 * AttnCfg<DH, F8>::NW)) void attn_split_kernel(
 }
 
 // out[row][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s. One wave per
-// (row, q head): the split weights are formed across lanes (lane s holds
-// split s); the partial outputs are read as float4s, DH/4 lanes per split and
-// 64/(DH/4) splits per load instruction, all of a chunk's loads issued before
-// any is used; each lane sums its splits in order and the lane groups are
-// then added in a fixed tree (deterministic). Requests with one split were
-// written by the split kernel.
-template <int DH>
+// HPW q heads of one row: the row's request and split count are found once;
+// then the (m, l) pairs and the first chunk of partial outputs of all HPW
+// heads are loaded together (one round trip), the partial outputs as float4s,
+// DH/4 lanes per split and 64/(DH/4) splits per load instruction. The split
+// weights are formed across lanes (lane s holds split s); each lane sums its
+// splits in order and the lane groups are then added in a fixed tree
+// (deterministic). Requests with one split were written by the split kernel.
+template <int DH, int HPW>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     constexpr int LPS = DH / 4;        // lanes per split
     constexpr int SPI = 64 / LPS;      // splits per load instruction
-    constexpr int CHUNK = 16;          // load instructions in flight per lane
+    constexpr int CHUNK = 16 / HPW;    // load instructions in flight per head
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int pair = blockIdx.x * 4 + wave;
-    if (pair >= a.T * a.Hq) return;
-    const int row = pair / a.Hq, h = pair % a.Hq;
+    const int pair0 = (blockIdx.x * 4 + wave) * HPW;   // HPW | Hq: one row per wave
+    if (pair0 >= a.T * a.Hq) return;
+    const int row = pair0 / a.Hq, h0 = pair0 % a.Hq;
     // request of the row = the last r with cu_out[r] <= row, found by the
     // whole wave: lane l tests start l * step, then the 64 starts after the
     // last hit (two dependent loads for up to 4096 requests, not log2 C)
@@ -566,64 +570,84 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
     if (inr && nsr == 1) return;
     const int ns = (inr && !a.is_rejected[row]) ? min(nsr, kMaxSplits) : 0;
     const size_t stride = (size_t)a.T * a.Hq;   // between splits, in (row, head) units
-    const size_t base = (size_t)row * a.Hq + h;
+    const size_t base0 = (size_t)row * a.Hq + h0;
     const int sub = lane / LPS, dq = lane % LPS;   // split within an instruction, dim quad
-    float2 ml0 = make_float2(kNegInf, 0.f), ml1 = make_float2(kNegInf, 0.f);
-    if (lane < ns) ml0 = *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + base) * 2);
-    if (lane + 64 < ns) ml1 = *reinterpret_cast<const float2*>(a.part_ml + ((lane + 64) * stride + base) * 2);
-    // the first chunk of partial outputs goes out with the (m, l) loads
-    const int ninst = (ns + SPI - 1) / SPI;
-    float4 v[CHUNK];
+    float2 ml0[HPW], ml1[HPW];
+    float4 v[HPW][CHUNK];
 #pragma unroll
-    for (int k = 0; k < CHUNK; ++k) {
-        const int sp = k * SPI + sub;
-        v[k] = sp < ns ? *reinterpret_cast<const float4*>(a.part_o + (sp * stride + base) * DH + 4 * dq)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    const float M = wave_max(fmaxf(ml0.x, ml1.x));
-    float w0 = 0.f, w1 = 0.f, L = 0.f;
-    if (M != kNegInf) {
-        w0 = __builtin_amdgcn_exp2f(ml0.x - M);   // -inf -> 0 for missing splits
-        w1 = __builtin_amdgcn_exp2f(ml1.x - M);
-        L = w0 * ml0.y + w1 * ml1.y;
-    }
-    L = wave_sum(L);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int i0 = 0; i0 < ninst; i0 += CHUNK) {
-        if (i0 > 0) {
-#pragma unroll
-            for (int k = 0; k < CHUNK; ++k) {
-                const int sp = (i0 + k) * SPI + sub;
-                v[k] = sp < ns ? *reinterpret_cast<const float4*>(a.part_o + (sp * stride + base) * DH + 4 * dq)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
+    for (int j = 0; j < HPW; ++j) {
+        const size_t base = base0 + j;
+        ml0[j] = lane < ns ? *reinterpret_cast<const float2*>(a.part_ml + (lane * stride + base) * 2)
+                           : make_float2(kNegInf, 0.f);
+        ml1[j] = lane + 64 < ns ? *reinterpret_cast<const float2*>(a.part_ml + ((lane + 64) * stride + base) * 2)
+                                : make_float2(kNegInf, 0.f);
 #pragma unroll
         for (int k = 0; k < CHUNK; ++k) {
-            const int s0 = (i0 + k) * SPI;   // first split of this instruction (uniform; 64 | s0 + SPI)
-            const int sp = s0 + sub;
-            const float w = __shfl(s0 < 64 ? w0 : w1, sp & 63, kWave);
-            if (sp < ns) {
-                acc.x += w * v[k].x;
-                acc.y += w * v[k].y;
-                acc.z += w * v[k].z;
-                acc.w += w * v[k].w;
-            }
+            const int sp = k * SPI + sub;
+            v[j][k] = sp < ns ? *reinterpret_cast<const float4*>(a.part_o + (sp * stride + base) * DH + 4 * dq)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
+    const int ninst = (ns + SPI - 1) / SPI;
+    float w0[HPW], w1[HPW], L[HPW];
+    float4 acc[HPW];
 #pragma unroll
-    for (int off = LPS; off < 64; off <<= 1) {
-        acc.x += __shfl_xor(acc.x, off, kWave);
-        acc.y += __shfl_xor(acc.y, off, kWave);
-        acc.z += __shfl_xor(acc.z, off, kWave);
-        acc.w += __shfl_xor(acc.w, off, kWave);
+    for (int j = 0; j < HPW; ++j) {
+        const float M = wave_max(fmaxf(ml0[j].x, ml1[j].x));
+        w0[j] = 0.f;
+        w1[j] = 0.f;
+        L[j] = 0.f;
+        if (M != kNegInf) {
+            w0[j] = __builtin_amdgcn_exp2f(ml0[j].x - M);   // -inf -> 0 for missing splits
+            w1[j] = __builtin_amdgcn_exp2f(ml1[j].x - M);
+            L[j] = w0[j] * ml0[j].y + w1[j] * ml1[j].y;
+        }
+        L[j] = wave_sum(L[j]);
+        acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    if (sub == 0) {
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        uint2 pk;
-        pk.x = uint32_t(f2bf(acc.x * inv)) | (uint32_t(f2bf(acc.y * inv)) << 16);
-        pk.y = uint32_t(f2bf(acc.z * inv)) | (uint32_t(f2bf(acc.w * inv)) << 16);
-        *reinterpret_cast<uint2*>(a.out + base * DH + 4 * dq) = pk;
+    for (int i0 = 0; i0 < ninst; i0 += CHUNK) {
+        if (i0 > 0) {   // more splits than a chunk holds: the next chunk of every head at once
+#pragma unroll
+            for (int j = 0; j < HPW; ++j)
+#pragma unroll
+                for (int k = 0; k < CHUNK; ++k) {
+                    const int sp = (i0 + k) * SPI + sub;
+                    v[j][k] = sp < ns ? *reinterpret_cast<const float4*>(a.part_o + (sp * stride + base0 + j) * DH +
+                                                                         4 * dq)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < HPW; ++j)
+#pragma unroll
+            for (int k = 0; k < CHUNK; ++k) {
+                const int s0 = (i0 + k) * SPI;   // first split of this instruction (uniform; 64 | s0 + SPI)
+                const int sp = s0 + sub;
+                const float w = __shfl(s0 < 64 ? w0[j] : w1[j], sp & 63, kWave);
+                if (sp < ns) {
+                    acc[j].x += w * v[j][k].x;
+                    acc[j].y += w * v[j][k].y;
+                    acc[j].z += w * v[j][k].z;
+                    acc[j].w += w * v[j][k].w;
+                }
+            }
+    }
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+#pragma unroll
+        for (int off = LPS; off < 64; off <<= 1) {
+            acc[j].x += __shfl_xor(acc[j].x, off, kWave);
+            acc[j].y += __shfl_xor(acc[j].y, off, kWave);
+            acc[j].z += __shfl_xor(acc[j].z, off, kWave);
+            acc[j].w += __shfl_xor(acc[j].w, off, kWave);
+        }
+        if (sub == 0) {
+            const float inv = L[j] > 0.f ? 1.0f / L[j] : 0.f;
+            uint2 pk;
+            pk.x = uint32_t(f2bf(acc[j].x * inv)) | (uint32_t(f2bf(acc[j].y * inv)) << 16);
+            pk.y = uint32_t(f2bf(acc[j].z * inv)) | (uint32_t(f2bf(acc[j].w * inv)) << 16);
+            *reinterpret_cast<uint2*>(a.out + (base0 + j) * DH + 4 * dq) = pk;
+        }
     }
 }
 
@@ -641,7 +665,15 @@ int launch_dh(const AttnArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1, hi
     if (e1) (void)hipEventRecord(e1, s);
     if (hipGetLastError() != hipSuccess) return PD_EHIP;
     if (e2) (void)hipEventRecord(e2, s);
-    hipLaunchKernelGGL(attn_merge_kernel<DH>, dim3((a.T * a.Hq + 3) / 4), dim3(256), 0, s, a);
+    // heads per wave: one while a wave per (row, head) fits one round of
+    // resident workgroups (every wave's load chain then runs side by side);
+    // four (or two) for more rows, which cuts the rounds (C = 64: 34.5 ->
+    // 24.9 us; at C = 1 four heads per wave would take 10.9 instead of 4.7)
+    const int hpw = (a.T * a.Hq + 3) / 4 <= kMergeRoundWgs ? 1 : (a.Hq % 4 == 0 ? 4 : (a.Hq % 2 == 0 ? 2 : 1));
+    const unsigned mgrid = (unsigned)((a.T * a.Hq / hpw + 3) / 4);
+    if (hpw == 4) hipLaunchKernelGGL((attn_merge_kernel<DH, 4>), dim3(mgrid), dim3(256), 0, s, a);
+    else if (hpw == 2) hipLaunchKernelGGL((attn_merge_kernel<DH, 2>), dim3(mgrid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_merge_kernel<DH, 1>), dim3(mgrid), dim3(256), 0, s, a);
     if (e3) (void)hipEventRecord(e3, s);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
