@@ -78,6 +78,23 @@ def test_many_requests_sampled(C, K, L):
     c.close()
 
 
+@pytest.mark.parametrize("dims", [GQA64, GQA128], ids=["dh64", "dh128"])
+def test_merge_many_rows_many_splits(dims):
+    """64 requests x 16 draft positions (over 1000 rows: the merge takes
+    several heads per wave) with lognormal contexts, so the longest requests
+    have 30-60 splits and the merge walks several chunks of partials per
+    head. The longest requests and request 0 are checked."""
+    w = synth.Workload(f"{dims.name}-c64k16", dims, C=64, K=16, context="lognormal", seed=47)
+    _say(f"[forward] {w.name}")
+    c = Case(w).run()
+    assert c.status() == 0
+    L = c.b["context_lens"]
+    reqs = sorted(set([0] + [int(i) for i in np.argsort(L)[-2:]]))
+    res = check_case(c, requests=reqs, check_cache=False)
+    _say(f"  contexts {[int(L[r]) for r in reqs]}: worst logit err/RMS {res['worst_logit_ratio']:.4g}")
+    c.close()
+
+
 @pytest.mark.parametrize("name", ["g_c1", "g_c4", "g_c64", "g_c64_k3", "g_c64_k5", "q_c16"])
 def test_full_size_workloads(name):
     w = synth.get_workload(name)
