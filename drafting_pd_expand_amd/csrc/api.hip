@@ -294,10 +294,6 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
     aa.scale_log2 = 1.4426950408889634f / sqrtf((float)m->dh);
     aa.part_o = (float*)(S + L.po); aa.part_ml = (float*)(S + L.pml);
     aa.out = ao; aa.status = st;
-    {
-        Timed t(h, PD_KERNEL_OTHER, s);
-        PD_TRY(launch_attn_plan(aa, s));
-    }
 
     // fc projection 3d -> d (starts the residual stream; skipped when the
     // projected rows are given), then the layer-0 input
@@ -306,8 +302,9 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
                     d, m->hidden3, nullptr, 0, &sp));
     {
         Timed t(h, PD_KERNEL_OTHER, s);
+        // the attention split plan runs as one more workgroup of this launch
         PD_TRY(launch_layer0_input(hidden_d, ws, sp, b->input_ids, m->embed, m->V, x, m->norm_emb,
-                                   m->norm_hid, u, T, d, m->rms_eps, st, s));
+                                   m->norm_hid, u, T, d, m->rms_eps, st, s, &aa));
     }
     PD_TRY(dbg(0));
     for (int l = 0; l < m->N; ++l) {

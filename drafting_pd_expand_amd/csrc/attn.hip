@@ -43,6 +43,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "attn_plan.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -55,15 +56,12 @@ constexpr float kNegInf = -INFINITY;
 // this (log2 units); exp2 arguments then stay <= kRescale, the final O / l is
 // unchanged, and the accumulator rescales are skipped on most pages.
 constexpr float kRescale = 8.0f;
-constexpr int kBtMax = 512;               // block-table entries of one split cached in LDS
-constexpr int kMaxSplitKeys = kBtMax * PD_PAGE;
+constexpr int kBtMax = kAttnBtMax;        // block-table entries of one split cached in LDS
+constexpr int kMaxSplitKeys = kAttnMaxSplitKeys;
 constexpr int kMaxSplits = 128;           // splits of one request the merge combines
-// split-kernel workgroups resident at once (two per CU: ~66 KB of LDS each)
-constexpr int kRoundSlots = 512;
 // merge-kernel workgroups resident at once with one head per wave (four per
 // CU, register-bound)
 constexpr int kMergeRoundWgs = 1024;
-constexpr int kOneRoundMaxKeys = 512;
 
 // K and V of pages that are past the split end or invalid come from here
 // (zero-initialised at load; nothing writes it).
@@ -151,114 +149,9 @@ __device__ __forceinline__ unsigned lds_addr(void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)p);
 }
 
-// One workgroup: reads cu_out / seq_lens of every request, validates them,
-// picks the split length and writes the per-request split counts and the
-// unit records {r, s, ns, row0, row1, kb, ke, 0}.
-__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
-    __shared__ long long s_sum[16];
-    __shared__ int s_max[16];
-    __shared__ int s_cnt[16];
-    __shared__ int s_incl[PD_MAX_C];   // inclusive prefix of the split counts
-    __shared__ int4 s_req[PD_MAX_C];   // validated {row0, row1, seq} of every request
-    const int r = threadIdx.x, lane = r & 63, w = r >> 6;
-    int seq = 0, row0 = 0, row1 = 0;
-    if (r < a.C) {
-        row0 = a.cu_out[r];
-        row1 = a.cu_out[r + 1];
-        seq = a.seq_lens[r];
-        const bool ok = row0 >= 0 && row1 <= a.T && row1 >= row0 && seq >= 1 &&
-                        seq <= a.max_blocks * PD_PAGE;
-        if (!ok) flag(a.status, PD_STATUS_BAD_ROW);
-        if (!ok || row1 == row0) seq = 0;   // no work
-    }
-    long long sv = seq;
-    int mv = seq;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        sv += __shfl_xor(sv, o, kWave);
-        mv = max(mv, __shfl_xor(mv, o, kWave));
-    }
-    if (lane == 0) {
-        s_sum[w] = sv;
-        s_max[w] = mv;
-    }
-    __syncthreads();
-    long long total = 0;
-    int mx = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        total += s_sum[i];
-        mx = max(mx, s_max[i]);
-    }
-    const long long tw = a.sp.target_wg;
-    long long sl = (total * a.Hkv + tw - 1) / tw;
-    // Few keys in all: the shortest split whose (unit, kv head) workgroups
-    // all fit in one round of kRoundSlots (units <= total / sl + C per head),
-    // as long as that split stays short. A second round costs more than the
-    // longer splits: C = 4 with 17.7k keys, 22 us at 304 keys / 472
-    // workgroups vs 27 us at 128 keys / 1120 and at 256 keys / 568 (26 us
-    // at 512 keys / 288); with 13k keys, 19 us at 224 keys vs 22 at 128.
-    const long long free_slots = kRoundSlots - (long long)a.Hkv * a.C;
-    if (free_slots > 0) {
-        const long long one = (total * a.Hkv + free_slots - 1) / free_slots;
-        if (one <= kOneRoundMaxKeys) sl = max(sl, one);
-    }
-    sl = max(sl, (long long)a.sp.min_split);
-    sl = max(sl, (long long)((mx + a.sp.scap - 1) / a.sp.scap));
-    sl = (sl + PD_PAGE - 1) / PD_PAGE * PD_PAGE;
-    const int split_len = (int)min(sl, (long long)kMaxSplitKeys);
-    int ns = seq > 0 ? (seq + split_len - 1) / split_len : 0;
-    if (ns > a.sp.scap) {   // excluded by the host's choice of scap; never write past it
-        flag(a.status, PD_STATUS_BAD_ROW);
-        ns = 0;
-    }
-    // exclusive prefix of ns over the block
-    int incl = ns;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
-    if (lane == 63) s_cnt[w] = incl;
-    __syncthreads();
-    int before = 0, units = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        before += i < w ? s_cnt[i] : 0;
-        units += s_cnt[i];
-    }
-    const int first = before + incl - ns;
-    if (r < a.C) {
-        a.plan[kPlanNs + r] = ns;
-        s_incl[r] = first + ns;
-        s_req[r] = make_int4(row0, row1, seq, 0);
-    }
-    if (r == 0) {
-        if (units > a.sp.max_units) flag(a.status, PD_STATUS_BAD_ROW);   // excluded by the host's bound
-        a.plan[0] = min(units, a.sp.max_units);
-        a.plan[1] = split_len;
-    }
-    __syncthreads();
-    // unit records, spread over the block: unit u belongs to the first
-    // request whose inclusive split count exceeds u (never one without splits)
-    const int nu = min(units, a.sp.max_units);
-    for (int u = r; u < nu; u += blockDim.x) {
-        int lo = 0, hi = a.C - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (s_incl[mid] > u) hi = mid; else lo = mid + 1;
-        }
-        const int q = lo;
-        const int nsq = s_incl[q] - (q > 0 ? s_incl[q - 1] : 0);
-        const int sq = u - (s_incl[q] - nsq);
-        const int4 rq = s_req[q];
-        const int kb = sq * split_len;
-        const int ke = min(rq.z, kb + split_len);
-        int4* rec = reinterpret_cast<int4*>(a.plan + kPlanUnits + (size_t)u * kPlanRec);
-        rec[0] = make_int4(q, sq, nsq, rq.x);
-        rec[1] = make_int4(rq.y, kb, ke, 0);
-    }
-}
+// The split plan on its own (the forward runs it inside the layer-0 input
+// kernel instead).
+__global__ __launch_bounds__(kAttnPlanThreads) void attn_plan_kernel(AttnArgs a) { attn_plan_block(a); }
 
 template <int DH, bool F8>
 __global__ __launch_bounds__((64 * AttnCfg<DH, F8>::NW)) void attn_split_kernel(AttnArgs a) {
@@ -708,7 +601,7 @@ AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks)
 
 int launch_attn_plan(const AttnArgs& a, hipStream_t s) {
     if (a.C <= 0) return PD_OK;
-    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAttnPlanThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 

@@ -71,10 +71,13 @@ int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 // Every consumer of a projection sums its fp32 partial planes
 // (ws[s][T][width], s < S) in split order.
 // xin != nullptr: the projected hidden rows given directly (bf16 [T][d]); ws / S unused.
+// plan != nullptr: the attention split plan (launch_attn_plan's work) runs as
+// one more workgroup of the same launch.
+struct AttnArgs;
 int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32_t* ids,
                         const uint16_t* embed, int V, float* x, const uint16_t* g_emb,
                         const uint16_t* g_hid, uint16_t* u, int T, int d, float eps,
-                        int32_t* status, hipStream_t s);
+                        int32_t* status, hipStream_t s, const AttnArgs* plan = nullptr);
 // rows != nullptr: output row o = norm of row rows[o] (o < nrows), x untouched;
 // xout (row-list mode) also gets the bf16 residual row itself.
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,

@@ -13,6 +13,9 @@
 #include <limits.h>
 #include <math.h>
 
+#include <cstring>
+
+#include "attn_plan.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -117,9 +120,13 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int 
                                                            const uint16_t* g_emb,
                                                            const uint16_t* g_hid, uint16_t* u, int T,
                                                            int d, float eps, int32_t* status,
-                                                           const uint16_t* xin) {
+                                                           const uint16_t* xin, AttnArgs plan, int with_plan) {
     __shared__ float red[4];
-    const int o = blockIdx.x;
+    if (with_plan && blockIdx.x == 0) {   // the attention split plan, beside the rows
+        attn_plan_block(plan);
+        return;
+    }
+    const int o = blockIdx.x - with_plan;
     int id = ids[o];
     if (id < 0 || id >= V) {
         if (threadIdx.x == 0) flag(status, PD_STATUS_BAD_TOKEN);
@@ -344,11 +351,15 @@ int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, u
 
 int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
                         float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
-                        int d, float eps, int32_t* status, hipStream_t s) {
+                        int d, float eps, int32_t* status, hipStream_t s, const AttnArgs* plan) {
     if (T <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
-#define L_(NC) hipLaunchKernelGGL(layer0_input_kernel<NC>, dim3(T), dim3(256), 0, s, ws, S, ids, embed, V, \
-                                  x, g_emb, g_hid, u, T, d, eps, status, xin)
+    AttnArgs pa;
+    if (plan) pa = *plan;
+    else std::memset(&pa, 0, sizeof(pa));
+    const int wp = (plan && plan->C > 0) ? 1 : 0;
+#define L_(NC) hipLaunchKernelGGL(layer0_input_kernel<NC>, dim3(T + wp), dim3(256), 0, s, ws, S, ids, embed, V, \
+                                  x, g_emb, g_hid, u, T, d, eps, status, xin, pa, wp)
     PD_ROW_NC(d, L_)
 #undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
