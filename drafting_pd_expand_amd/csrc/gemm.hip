@@ -619,46 +619,41 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
     for (int i = 0; i < 8; ++i)
         wrow[i] = DUAL ? (i < 4 ? 64 * wn + 16 * i : COLS + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
     const int rsw = (r16 >> 2) & 3;
+    const int pos = (g4 ^ rsw) * 8;
 
-    for (int st = 0; st < kBNST - 1 && st < total; ++st) issue(st);
+    // one stage's MFMA operands: W fragments a[8] are overwritten with the
+    // next stage's one by one, each right after its last MFMA has been issued;
+    // X fragments are double-buffered (read at the start of the previous stage)
+    auto read_a = [&](int q, int i) {
+        const uint16_t* Ws = ring + (q % kBNST) * kBSE;
+        return *reinterpret_cast<const bf16x8*>(Ws + (wrow[i] + r16) * kBS + pos);
+    };
+    auto read_b = [&](bf16x8 (&b)[4], int q) {
+        const uint16_t* Xs = ring + (q % kBNST) * kBSE + kBT * kBS;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b[j] = *reinterpret_cast<const bf16x8*>(Xs + (64 * wm + 16 * j + r16) * kBS + pos);
+    };
 
-    int qc = 0;
-    for (int it = rpos; it < nitems; it += G) {
-        const int sp = it / tiles;
-        const int kb = sp * per, ke = min(ksteps, (sp + 1) * per);
-        if (kb >= ke) continue;
-        const int tile = it % tiles;
-        const int m0 = (tile % mblocks) * kBT;
-        const int ntile = tile / mblocks;
-        const int n0 = ntile * COLS;
-        f32x4 acc[8][4];
+    f32x4 acc[8][4];
+    auto zero_acc = [&]() {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = kb; ks < ke; ++ks, ++qc) {
-            ring_wait_later<L, kBNST - 2>(min(kBNST - 2, total - 1 - qc));
-            ring_barrier();
-            if (qc + kBNST - 1 < total) issue((qc + kBNST - 1) % kBNST);
-            const uint16_t* Ws = ring + (qc % kBNST) * kBSE;
-            const uint16_t* Xs = Ws + kBT * kBS;
-            const int pos = (g4 ^ rsw) * 8;
-            bf16x8 af[8], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const bf16x8*>(Ws + (wrow[i] + r16) * kBS + pos);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(Xs + (64 * wm + 16 * j + r16) * kBS + pos);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bfr[j], acc[i][j]);
-        }
+    };
 
-        // lane holds rows m = m0 + 64*wm + 16*j + r16 and 4 consecutive columns per group i
+    // lane holds rows m = m0 + 64*wm + 16*j + r16 and 4 consecutive columns per group i
+    auto epilogue = [&](int it) {
+        const int sp = it / tiles;
+        const int tile = it % tiles;
+        const int m0 = (tile % mblocks) * kBT;
+        const int ntile = tile / mblocks;
+        const int n0 = ntile * COLS;
         if constexpr (EPI == EPI_ARGMAX) {
             __shared__ float s_v[2][kBT];
             __shared__ int s_i[2][kBT];
+            ring_barrier();   // the previous item's readers of s_v / s_i are done
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int ml = 64 * wm + 16 * j + r16;
@@ -724,6 +719,53 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
                 }
             }
         }
+    };
+
+    // all ring slots filled up front; stage q lives in slot q % kBNST
+    for (int st = 0; st < kBNST && st < total; ++st) issue(st);
+    bf16x8 af[8], bc[4], bn[4];
+    if (total > 0) {
+        ring_wait_later<L, kBNST - 1>(min(kBNST - 1, total - 1));
+        ring_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) af[i] = read_a(0, i);
+        read_b(bc, 0);
+    }
+    int qc = 0;
+    // one stage: wait for the next stage's copies, refill the slot everyone
+    // has read, then this stage's MFMAs interleaved with the reads of the
+    // next stage's operands. After the last stage the reads fetch a stale
+    // (in-bounds) slot whose values are never used; the waits and barriers
+    // are uniform over the workgroup.
+    auto stage = [&](bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
+        ring_wait_later<L, kBNST - 2>(max(0, min(kBNST - 2, total - 2 - qc)));
+        ring_barrier();
+        if (qc + kBNST < total) issue((qc + kBNST) % kBNST);
+        read_b(bn, qc + 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bc[j], acc[i][j]);
+            af[i] = read_a(qc + 1, i);
+            __builtin_amdgcn_sched_barrier(0);   // each read after its register's last MFMA
+        }
+        ++qc;
+    };
+    for (int it = rpos; it < nitems; it += G) {
+        const int sp = it / tiles;
+        const int kb = sp * per, ke = min(ksteps, (sp + 1) * per);
+        if (kb >= ke) continue;
+        zero_acc();
+        for (int ks = kb; ks < ke; ks += 2) {
+            stage(bc, bn);
+            if (ks + 1 < ke) {
+                stage(bn, bc);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bc[j] = bn[j];
+            }
+        }
+        epilogue(it);
     }
 }
 
