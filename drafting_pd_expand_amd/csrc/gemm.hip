@@ -529,7 +529,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
 // every round each XCD takes a contiguous run of tiles (M blocks innermost):
 // tiles sharing a W tile and K range meet in one L2. For SwiGLU a tile's W
 // rows are 128 gate rows then the same 128 up rows; a wave takes 64 of each.
-// X rows are read directly (no row gather).
+// X rows are read directly (no row gather). The MFMA operands of the next
+// stage are read from LDS while the current stage's MFMAs run (X fragments
+// double-buffered, each W fragment register refilled right after its last
+// MFMA), so a wave never stalls on LDS between MFMAs.
 constexpr int kBT = 256;                 // tile rows of W and of X
 constexpr int kBS = 32;                  // reduction elements per stage (64 B of each row)
 constexpr int kBNST = 4;                 // ring stages
