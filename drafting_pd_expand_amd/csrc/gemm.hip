@@ -556,7 +556,11 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
     const int per = (ksteps + a.splits - 1) / a.splits;
     const int nitems = tiles * a.splits;
     const int G = gridDim.x;
-    const int rpos = (G % 8 == 0) ? (blockIdx.x & 7) * (G / 8) + (blockIdx.x >> 3) : blockIdx.x;
+    // workgroups go round-robin to the 8 XCDs: XCD x holds blocks x, x+8, ...;
+    // give it a contiguous run of item positions (any G: the first G % 8
+    // XCDs hold one block more)
+    const int xcd = blockIdx.x & 7, q8 = G >> 3, r8 = G & 7;
+    const int rpos = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
 
     // this thread's fixed share of every stage: units u = tid + 512 j; j = 0, 1
     // are W rows u / 4, j = 2, 3 are X rows (u - 1024) / 4; chunk u % 4
@@ -848,10 +852,11 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
             }
         }
         p.ntiles = ntn;
+        // one workgroup per item when they fit in one round (rounding such a
+        // grid down to whole rounds of 8 XCDs would give a few workgroups a
+        // second item and double the launch); otherwise 256, a multiple of 8
         const long items = tiles * p.splits;
-        long g = items < 256 ? items : 256;
-        if (g >= 8) g -= g % 8;   // whole rounds of 8 XCDs
-        p.grid = (int)g;
+        p.grid = (int)(items < 256 ? items : 256);
         return p;
     }
     if (p.kind == GEMM_TILED) {
