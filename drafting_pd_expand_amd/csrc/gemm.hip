@@ -868,12 +868,18 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
         const int cols = (epi == EPI_SWIGLU) ? kTN / 2 : kTN;
         p.ntiles = (N + cols - 1) / cols;
         if (epi == EPI_PARTIAL) {
+            // the split count that minimises the K steps of the busiest of
+            // the 512 resident workgroups (two per CU): a grid just over 512
+            // would run a second round for a few workgroups
             const long tiles = (long)p.ntiles * p.mblocks;
             const int ksteps = (K + kTK - 1) / kTK;
-            int s = (int)((512 + tiles - 1) / tiles);
-            if (s > 8) s = 8;
-            while (s > 1 && s * 4 > ksteps) --s;
-            p.splits = s < 1 ? 1 : s;
+            long best = -1;
+            for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
+                const int per = (ksteps + sp - 1) / sp;
+                if ((sp - 1) * per >= ksteps) continue;   // no empty split
+                const long span = ((tiles * sp + 511) / 512) * per;
+                if (best < 0 || span < best) { best = span; p.splits = sp; }
+            }
         }
         return p;
     }
