@@ -12,9 +12,9 @@
 //    and runs v_mfma_f32_16x16x32_bf16 on them (W rows are the A operand, X
 //    rows the B operand, so a lane ends with 4 consecutive output columns of
 //    one row);
-//  * 64 < M < 384 rows: 128 x 128 output tiles staged through LDS, two
-//    workgroups per CU;
-//  * M >= 384 rows: persistent 256 x 256 tiles fed by a global -> LDS ring.
+//  * more rows: persistent tiles fed by a global -> LDS ring, 256 x 256 from
+//    384 rows on, 128 x 128 (two workgroups per CU) below; the LM head below
+//    384 rows uses 128 x 128 tiles staged through registers instead.
 //
 // Projections with few output columns are split over workgroups along K.
 // Those splits never meet inside the GEMM: each writes an fp32 partial plane,
@@ -316,12 +316,12 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel for many rows (M > 64): a 128 x 128 output tile per workgroup,
+// Tiled kernel (the LM head at 64 < M < 384): a 128 x 128 output tile per workgroup,
 // K in steps of 64 staged through LDS (double buffered: the next step's
 // global loads are in registers while the current step's MFMAs run), four
 // waves each owning a 64 x 64 quarter (4 x 4 MFMA tiles); two workgroups fit
-// a CU. Used for 64 < M < 384 rows, where the 256-row tiles below would
-// mostly be padding. For SwiGLU the tile's 128 W rows are 64 gate rows then
+// a CU. Used for the LM head at 64 < M < 384 rows, where the 256-row tiles
+// below would mostly be padding. For SwiGLU the tile's 128 W rows are 64 gate rows then
 // the same 64 up rows, and each wave takes 32 of each: a lane holds matching
 // gate and up columns.
 constexpr int kTM = 128, kTN = 128, kTK = 64;
@@ -515,14 +515,17 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     }
 }
 
-// Persistent big-tile kernel for many rows (M > 64). A workgroup of 8 waves
-// (two per SIMD: one wave per SIMD cannot keep the matrix core busy) owns a
-// 256 (W rows = output columns) x 256 (X rows = output rows) tile; each wave
-// computes 128 x 64 of it (8 x 4 MFMA tiles), which keeps the LDS fragment
-// reads at 3 bytes per flop-pair lower than 64 x 64 wave tiles. W and X tiles
-// of 32 reduction elements go straight from HBM/L2 into a 4-stage LDS ring
-// (global_load_lds, 32 KB per stage); each of <= 256 workgroups walks its work
-// items (tile, K split) without restarting the ring. Rows are 64 B in LDS
+// Persistent ring-fed tile kernel for many rows (M > 64). With BT = 256 a
+// workgroup of 8 waves (two per SIMD: one wave per SIMD cannot keep the
+// matrix core busy) owns a 256 (W rows = output columns) x 256 (X rows =
+// output rows) tile; each wave computes 128 x 64 of it (8 x 4 MFMA tiles),
+// which keeps the LDS fragment reads at 3 bytes per flop-pair lower than
+// 64 x 64 wave tiles. With BT = 128 (for 64 < M < 384) four waves of 64 x 64
+// share a 128 x 128 tile and two workgroups fit a CU. W and X tiles of 32
+// reduction elements go straight from HBM/L2 into a 4-stage LDS ring
+// (global_load_lds, 2 BT x 64 B per stage); each resident workgroup walks its
+// work items (tile, K split) without restarting the ring. The copy sources
+// are set once per item, so a stage only adds its K offset. Rows are 64 B in LDS
 // with their 16-byte chunks XOR-permuted by ((row >> 2) & 3): the 16 lanes
 // that one LDS cycle serves (rows r..r+15, one chunk) then read 16 different
 // 16-byte slots of the 256-byte bank line. Items are dealt so that in
@@ -536,20 +539,22 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
 constexpr int kBT = 256;                 // tile rows of W and of X
 constexpr int kBS = 32;                  // reduction elements per stage (64 B of each row)
 constexpr int kBNST = 4;                 // ring stages
-constexpr int kBSE = 2 * kBT * kBS;      // elements per stage: W tile rows, then X tile rows
 
-template <int EPI>
-__global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
+template <int EPI, int BT>
+__global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     constexpr int L = 4;                      // 16-byte loads per thread per stage: 2 of W, 2 of X
-    constexpr int COLS = DUAL ? kBT / 2 : kBT;   // output columns per tile
-    __shared__ __align__(16) uint16_t ring[kBNST * kBSE];
+    constexpr int NT = 2 * BT;                // threads: BT / 32 waves
+    constexpr int NA = BT / 32;               // W fragments (16 output columns each) per wave
+    constexpr int SE = 2 * BT * kBS;          // elements per stage: W tile rows, then X tile rows
+    constexpr int COLS = DUAL ? BT / 2 : BT;  // output columns per tile
+    __shared__ __align__(16) uint16_t ring[kBNST * SE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
-    const int wn = wave & 1, wm = wave >> 1;   // 2 column halves x 4 row quarters
+    const int wn = wave & 1, wm = wave >> 1;   // 2 column halves x (BT / 64) groups of 64 rows
 
-    const int mblocks = (a.M + kBT - 1) / kBT;
+    const int mblocks = (a.M + BT - 1) / BT;
     const int ntn = (a.N + COLS - 1) / COLS;
     const int tiles = ntn * mblocks;
     const int ksteps = (a.K + kBS - 1) / kBS;
@@ -562,13 +567,13 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
     const int xcd = blockIdx.x & 7, q8 = G >> 3, r8 = G & 7;
     const int rpos = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
 
-    // this thread's fixed share of every stage: units u = tid + 512 j; j = 0, 1
-    // are W rows u / 4, j = 2, 3 are X rows (u - 1024) / 4; chunk u % 4
+    // this thread's fixed share of every stage: units u = tid + NT j; j = 0, 1
+    // are W rows u / 4, j = 2, 3 are X rows (u - 2 NT) / 4; chunk u % 4
     int rowrel[4], ch[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int u = tid + 512 * j;
-        const int r = (j < 2 ? u : u - 1024) >> 2;
+        const int u = tid + NT * j;
+        const int r = (j < 2 ? u : u - 2 * NT) >> 2;
         rowrel[j] = r;
         ch[j] = ((u & 3) ^ ((r >> 2) & 3)) * 8;
     }
@@ -580,72 +585,81 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
         const int sp = it / tiles;
         total += max(0, min(ksteps, (sp + 1) * per) - sp * per);
     }
+    // The copy sources of the item being issued: row pointers (at the row's
+    // chunk) set once per item, so a stage only adds its K offset. Rows past
+    // N / M and chunks past K come from the zero buffer.
     int iitem = rpos, iks = 0, ike = 0;
-    if (iitem < nitems) {
+    const uint16_t* rsrc[4];
+    bool rok[4];
+    auto set_item = [&]() {
         const int sp = iitem / tiles;
         iks = sp * per;
         ike = min(ksteps, (sp + 1) * per);
-    }
-    auto issue = [&](int slot) {
-        while (iitem < nitems && iks >= ike) {
-            iitem += G;
-            if (iitem < nitems) {
-                const int sp = iitem / tiles;
-                iks = sp * per;
-                ike = min(ksteps, (sp + 1) * per);
-            }
-        }
         const int tile = iitem % tiles;
-        const int m0 = (tile % mblocks) * kBT;
+        const int m0 = (tile % mblocks) * BT;
         const int n0 = (tile / mblocks) * COLS;
-        const int k0 = iks * kBS;
-        const unsigned sbase = lds0 + (unsigned)(slot * kBSE) * 2u;
-        const bool kin = k0 + kBS <= a.K;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint16_t* src;
             if (j < 2) {
                 const int r = rowrel[j];
                 const int n = n0 + (DUAL ? (r & (COLS - 1)) : r);
                 const uint16_t* base = (DUAL && r >= COLS) ? a.W2 : a.W;
-                src = (n < a.N && (kin || k0 + ch[j] < a.K)) ? base + (size_t)n * a.K + k0 + ch[j] : zp;
+                rok[j] = n < a.N;
+                rsrc[j] = base + (size_t)(rok[j] ? n : 0) * a.K + ch[j];
             } else {
                 const int m = m0 + rowrel[j];
-                src = (m < a.M && (kin || k0 + ch[j] < a.K)) ? a.X + (size_t)m * a.ldx + k0 + ch[j] : zp;
+                rok[j] = m < a.M;
+                rsrc[j] = a.X + (size_t)(rok[j] ? m : 0) * a.ldx + ch[j];
             }
+        }
+    };
+    if (iitem < nitems) set_item();
+    auto issue = [&](int slot) {
+        while (iitem < nitems && iks >= ike) {
+            iitem += G;
+            if (iitem < nitems) set_item();
+        }
+        const int k0 = iks * kBS;
+        const bool kin = k0 + kBS <= a.K;
+        const unsigned sbase = lds0 + (unsigned)(slot * SE) * 2u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = rok[j] && (kin || k0 + ch[j] < a.K);
+            const uint16_t* src = ok ? rsrc[j] + k0 : zp;
             __builtin_amdgcn_global_load_lds((void*)src,
-                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + 512 * j) * 16u),
+                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
                 16, 0, 0);
         }
         ++iks;
     };
 
-    // LDS rows of this wave's fragments: W rows for the 8 column groups, X rows for 4
-    int wrow[8];
+    // LDS rows of this wave's fragments: W rows for the NA column groups, X rows for 4
+    int wrow[NA];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        wrow[i] = DUAL ? (i < 4 ? 64 * wn + 16 * i : COLS + 64 * wn + 16 * (i - 4)) : 128 * wn + 16 * i;
+    for (int i = 0; i < NA; ++i)
+        wrow[i] = DUAL ? (i < NA / 2 ? (BT / 4) * wn + 16 * i : COLS + (BT / 4) * wn + 16 * (i - NA / 2))
+                       : (BT / 2) * wn + 16 * i;
     const int rsw = (r16 >> 2) & 3;
     const int pos = (g4 ^ rsw) * 8;
 
-    // one stage's MFMA operands: W fragments a[8] are overwritten with the
+    // one stage's MFMA operands: W fragments a[NA] are overwritten with the
     // next stage's one by one, each right after its last MFMA has been issued;
     // X fragments are double-buffered (read at the start of the previous stage)
     auto read_a = [&](int q, int i) {
-        const uint16_t* Ws = ring + (q % kBNST) * kBSE;
+        const uint16_t* Ws = ring + (q % kBNST) * SE;
         return *reinterpret_cast<const bf16x8*>(Ws + (wrow[i] + r16) * kBS + pos);
     };
     auto read_b = [&](bf16x8 (&b)[4], int q) {
-        const uint16_t* Xs = ring + (q % kBNST) * kBSE + kBT * kBS;
+        const uint16_t* Xs = ring + (q % kBNST) * SE + BT * kBS;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             b[j] = *reinterpret_cast<const bf16x8*>(Xs + (64 * wm + 16 * j + r16) * kBS + pos);
     };
 
-    f32x4 acc[8][4];
+    f32x4 acc[NA][4];
     auto zero_acc = [&]() {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
@@ -654,12 +668,12 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
     auto epilogue = [&](int it) {
         const int sp = it / tiles;
         const int tile = it % tiles;
-        const int m0 = (tile % mblocks) * kBT;
+        const int m0 = (tile % mblocks) * BT;
         const int ntile = tile / mblocks;
         const int n0 = ntile * COLS;
         if constexpr (EPI == EPI_ARGMAX) {
-            __shared__ float s_v[2][kBT];
-            __shared__ int s_i[2][kBT];
+            __shared__ float s_v[2][BT];
+            __shared__ int s_i[2][BT];
             ring_barrier();   // the previous item's readers of s_v / s_i are done
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -668,8 +682,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
                 float bv = -FLT_MAX;
                 int bi = INT_MAX;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int n = n0 + 128 * wn + 16 * i + 4 * g4;
+                for (int i = 0; i < NA; ++i) {
+                    const int n = n0 + (BT / 2) * wn + 16 * i + 4 * g4;
                     if (n >= a.N) continue;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) better(bv, bi, acc[i][j][e], n + e);
@@ -688,7 +702,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
                 }
             }
             ring_barrier();   // (no wait on the ring's copies in flight)
-            if (tid < kBT) {
+            if (tid < BT) {
                 const int m = m0 + tid;
                 float bv = s_v[0][tid];
                 int bi = s_i[0][tid];
@@ -705,19 +719,19 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
                 if (m >= a.M) continue;
                 if constexpr (EPI == EPI_PARTIAL) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int n = n0 + 128 * wn + 16 * i + 4 * g4;
+                    for (int i = 0; i < NA; ++i) {
+                        const int n = n0 + (BT / 2) * wn + 16 * i + 4 * g4;
                         if (n < a.N)
                             *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[i][j];
                     }
-                } else {  // SwiGLU: groups 0..3 = gate, 4..7 = the matching up columns
+                } else {  // SwiGLU: groups 0..NA/2-1 = gate, the rest the matching up columns
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int n = n0 + 64 * wn + 16 * i + 4 * g4;
+                    for (int i = 0; i < NA / 2; ++i) {
+                        const int n = n0 + (BT / 4) * wn + 16 * i + 4 * g4;
                         if (n >= a.N) continue;
                         float h[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) h[e] = silu(acc[i][j][e]) * acc[i + 4][j][e];
+                        for (int e = 0; e < 4; ++e) h[e] = silu(acc[i][j][e]) * acc[i + NA / 2][j][e];
                         uint2 pk;
                         pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
                         pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
@@ -730,12 +744,12 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
 
     // all ring slots filled up front; stage q lives in slot q % kBNST
     for (int st = 0; st < kBNST && st < total; ++st) issue(st);
-    bf16x8 af[8], bc[4], bn[4];
+    bf16x8 af[NA], bc[4], bn[4];
     if (total > 0) {
         ring_wait_later<L, kBNST - 1>(min(kBNST - 1, total - 1));
         ring_barrier();
 #pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = read_a(0, i);
+        for (int i = 0; i < NA; ++i) af[i] = read_a(0, i);
         read_b(bc, 0);
     }
     int qc = 0;
@@ -750,7 +764,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
         if (qc + kBNST < total) issue((qc + kBNST) % kBNST);
         read_b(bn, qc + 1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NA; ++i) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bc[j], acc[i][j]);
             af[i] = read_a(qc + 1, i);
@@ -779,7 +793,12 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs a) {
 template <int EPI>
 int launch_big(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     if (a.xrows) return PD_EINVAL;   // many-row GEMMs read X rows directly
-    hipLaunchKernelGGL(gemm_big_kernel<EPI>, dim3(p.grid), dim3(512), 0, s, a);
+    if (p.wn == 8)
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, 256>), dim3(p.grid), dim3(512), 0, s, a);
+    else if (p.wn == 4)
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, 128>), dim3(p.grid), dim3(256), 0, s, a);
+    else
+        return PD_EINVAL;
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
@@ -828,17 +847,26 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
     GemmPlan p;
     p.nm = 1;
-    p.kind = M <= 64 ? GEMM_RING : (M < 384 ? GEMM_TILED : GEMM_BIG);
+    // M <= 64: weight-streaming ring. 64 < M < 384: the LM head (max/argmax
+    // epilogue) on 128 x 128 register-staged tiles, the projections on the
+    // ring-fed tile kernel with 128-row tiles; M >= 384: 256-row tiles.
+    // (Measured on the drafting step: the 128-row ring-fed kernel runs the
+    // 224-row projections of the Qwen3-Coder-scale drafter faster than the
+    // register-staged tiles, and the 112..320-row LM heads slower.)
+    p.kind = M <= 64 ? GEMM_RING : ((M < 384 && epi == EPI_ARGMAX) ? GEMM_TILED : GEMM_BIG);
     p.splits = 1;
     p.grid = 0;
     if (p.kind == GEMM_BIG) {
-        // persistent 256 x 256 tiles; K splits (partial planes, summed by the
-        // consumer) chosen to minimise the stages of the busiest of the <= 256
-        // workgroups
+        // persistent tiles of bt x bt: 256 (8 waves, one workgroup per CU) from
+        // 384 rows on, 128 (4 waves, two workgroups per CU) below; K splits
+        // (partial planes, summed by the consumer) chosen to minimise the
+        // stages of the busiest of the resident workgroups
+        const int bt = M >= 384 ? kBT : kBT / 2;
+        const long cap = bt == kBT ? 256 : 512;
         p.mt = 0;
-        p.wn = 8;
-        p.mblocks = (M + kBT - 1) / kBT;
-        const int cols = (epi == EPI_SWIGLU) ? kBT / 2 : kBT;
+        p.wn = bt / 32;
+        p.mblocks = (M + bt - 1) / bt;
+        const int cols = (epi == EPI_SWIGLU) ? bt / 2 : bt;
         const int ntn = (N + cols - 1) / cols;
         const long tiles = (long)ntn * p.mblocks;
         const int ksteps = (K + kBS - 1) / kBS;
@@ -847,16 +875,13 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
             for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
                 const int per = (ksteps + sp - 1) / sp;
                 if ((sp - 1) * per >= ksteps) continue;
-                const long span = ((tiles * sp + 255) / 256) * per;
+                const long span = ((tiles * sp + cap - 1) / cap) * per;
                 if (best < 0 || span < best) { best = span; p.splits = sp; }
             }
         }
         p.ntiles = ntn;
-        // one workgroup per item when they fit in one round (rounding such a
-        // grid down to whole rounds of 8 XCDs would give a few workgroups a
-        // second item and double the launch); otherwise 256, a multiple of 8
         const long items = tiles * p.splits;
-        p.grid = (int)(items < 256 ? items : 256);
+        p.grid = (int)(items < cap ? items : cap);
         return p;
     }
     if (p.kind == GEMM_TILED) {

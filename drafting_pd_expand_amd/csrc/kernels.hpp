@@ -47,15 +47,15 @@ struct GemmArgs {
 
 enum GemmKind : int {
     GEMM_RING = 0,    // M <= 64: persistent LDS-ring weight streaming
-    GEMM_TILED = 1,   // 64 < M < 384: 128 x 128 tiles, two workgroups per CU
-    GEMM_BIG = 2,     // M >= 384: persistent 256 x 256 tiles, 8 waves
+    GEMM_TILED = 1,   // LM head at 64 < M < 384: 128 x 128 register-staged tiles, two workgroups per CU
+    GEMM_BIG = 2,     // other M > 64: persistent ring-fed tiles, 256 x 256 (8 waves) from 384 rows, else 128 x 128
 };
 
 struct GemmPlan {
     int kind;      // GemmKind
     int mt;        // ring: 16-row X tiles (1, 2 or 4)
     int mblocks;   // tiled / big: workgroups along M
-    int wn;        // waves per workgroup
+    int wn;        // waves per workgroup (ring-fed tiles: 8 = 256-row, 4 = 128-row)
     int nm;        // ring: groups of 16 output columns per wave
     int ntiles;    // column tiles (ARGMAX: groups of the max/argmax partial results per row)
     int splits;    // K splits (EPI_PARTIAL: one fp32 plane each)
