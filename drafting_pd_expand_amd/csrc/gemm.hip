@@ -159,40 +159,45 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
         total += max(0, min(ksteps, (sp + 1) * per) - sp * per);
     }
 
-    // issue cursor: (item, stage) of the next stage to load
+    // issue cursor: (item, stage) of the next stage to load; the W sources
+    // of the item (row pointers at each load's chunk, or null past N) are set
+    // once per item, so a stage only adds its K offset
     int iitem = blockIdx.x, iks = 0, ike = 0;
-    if (iitem < nitems) {
+    const uint16_t* wp[WL];
+    bool wfull = true;   // the item's tile lies inside N
+    auto set_item = [&]() {
         const int sp = iitem / ntn;
         iks = sp * per;
         ike = min(ksteps, (sp + 1) * per);
-    }
-    auto issue = [&](int slot) {
-        // skip items without stages (not produced by the planner)
-        while (iitem < nitems && iks >= ike) {
-            iitem += G;
-            if (iitem < nitems) {
-                const int sp = iitem / ntn;
-                iks = sp * per;
-                ike = min(ksteps, (sp + 1) * per);
-            }
-        }
         const int n0 = (iitem % ntn) * TW;
-        const int k0 = iks * kRS;
-        const unsigned sbase = lds0 + (unsigned)(slot * Cf::SE) * 2u;
-        // whole tile inside N and whole stage inside K: no per-lane bounds
-        const bool inner = n0 + TW <= a.N && k0 + kRS <= a.K;
+        wfull = n0 + TW <= a.N;
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
             const int q = j * NT / (16 * 16 * WN);   // row group of this load (compile-time)
             const int nq = n0 + (PAIR ? 0 : q * 16 * WN);
-            const uint16_t* tile = (PAIR && q == 1 ? a.W2 : a.W) + (size_t)nq * a.K + k0;
+            const uint16_t* base = (PAIR && q == 1) ? a.W2 : a.W;
+            wp[j] = (nq + wrr[j] < a.N) ? base + (size_t)nq * a.K + wofs[j] : nullptr;
+        }
+    };
+    if (iitem < nitems) set_item();
+    auto issue = [&](int slot) {
+        // skip items without stages (not produced by the planner)
+        while (iitem < nitems && iks >= ike) {
+            iitem += G;
+            if (iitem < nitems) set_item();
+        }
+        const int k0 = iks * kRS;
+        const unsigned sbase = lds0 + (unsigned)(slot * Cf::SE) * 2u;
+        // whole tile inside N and whole stage inside K: no per-lane bounds
+        const bool kin = k0 + kRS <= a.K;
+        const bool inner = wfull && kin;
+#pragma unroll
+        for (int j = 0; j < WL; ++j) {
             const uint16_t* src;
-            if (inner) {
-                src = tile + wofs[j];
-            } else {
-                const int n = nq + wrr[j], k = k0 + wch[j];
-                src = (n < a.N && k < a.K) ? tile + wofs[j] : zp;
-            }
+            if (inner)
+                src = wp[j] + k0;
+            else
+                src = (wp[j] && k0 + wch[j] < a.K) ? wp[j] + k0 : zp;
             __builtin_amdgcn_global_load_lds((void*)src,
                 (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
                 16, 0, 0);
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < XL; ++j) {
             const int k = k0 + xch[j];
-            const uint16_t* src = (xp[j] && (inner || k < a.K)) ? xp[j] + k : zp;
+            const uint16_t* src = (xp[j] && (kin || k < a.K)) ? xp[j] + k : zp;
             __builtin_amdgcn_global_load_lds((void*)src,
                 (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(Cf::WR * kRS * 2) +
                                                                       (unsigned)(wave * 64 + NT * j) * 16u),
