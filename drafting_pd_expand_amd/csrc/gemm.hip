@@ -592,10 +592,11 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     }
     // The copy sources of the item being issued: row pointers (at the row's
     // chunk) set once per item, so a stage only adds its K offset. Rows past
-    // N / M and chunks past K come from the zero buffer.
+    // N / M point at the zero buffer with a zero K mask; chunks past K (only
+    // in a last, partial stage) also come from the zero buffer.
     int iitem = rpos, iks = 0, ike = 0;
     const uint16_t* rsrc[4];
-    bool rok[4];
+    unsigned kmask[4];
     auto set_item = [&]() {
         const int sp = iitem / tiles;
         iks = sp * per;
@@ -609,12 +610,14 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
                 const int r = rowrel[j];
                 const int n = n0 + (DUAL ? (r & (COLS - 1)) : r);
                 const uint16_t* base = (DUAL && r >= COLS) ? a.W2 : a.W;
-                rok[j] = n < a.N;
-                rsrc[j] = base + (size_t)(rok[j] ? n : 0) * a.K + ch[j];
+                const bool ok = n < a.N;
+                kmask[j] = ok ? ~0u : 0u;
+                rsrc[j] = ok ? base + (size_t)n * a.K + ch[j] : zp;
             } else {
                 const int m = m0 + rowrel[j];
-                rok[j] = m < a.M;
-                rsrc[j] = a.X + (size_t)(rok[j] ? m : 0) * a.ldx + ch[j];
+                const bool ok = m < a.M;
+                kmask[j] = ok ? ~0u : 0u;
+                rsrc[j] = ok ? a.X + (size_t)m * a.ldx + ch[j] : zp;
             }
         }
     };
@@ -625,40 +628,44 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
             if (iitem < nitems) set_item();
         }
         const int k0 = iks * kBS;
-        const bool kin = k0 + kBS <= a.K;
         const unsigned sbase = lds0 + (unsigned)(slot * SE) * 2u;
+        const uint16_t* src[4];
+        if (k0 + kBS <= a.K) {   // the whole stage inside K
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool ok = rok[j] && (kin || k0 + ch[j] < a.K);
-            const uint16_t* src = ok ? rsrc[j] + k0 : zp;
-            __builtin_amdgcn_global_load_lds((void*)src,
+            for (int j = 0; j < 4; ++j) src[j] = rsrc[j] + ((unsigned)k0 & kmask[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) src[j] = (kmask[j] && k0 + ch[j] < a.K) ? rsrc[j] + k0 : zp;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_global_load_lds((void*)src[j],
                 (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
                 16, 0, 0);
-        }
         ++iks;
     };
 
-    // LDS rows of this wave's fragments: W rows for the NA column groups, X rows for 4
-    int wrow[NA];
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-        wrow[i] = DUAL ? (i < NA / 2 ? (BT / 4) * wn + 16 * i : COLS + (BT / 4) * wn + 16 * (i - NA / 2))
-                       : (BT / 2) * wn + 16 * i;
+    // LDS element offsets of this lane's first W and X fragment rows; W
+    // fragment i lies arow(i) rows further (gate rows, then the matching up
+    // rows COLS further for SwiGLU), X fragment j 16 j rows further: both
+    // compile-time, so every fragment read is one base plus an immediate
     const int rsw = (r16 >> 2) & 3;
     const int pos = (g4 ^ rsw) * 8;
+    const int la = ((DUAL ? BT / 4 : BT / 2) * wn + r16) * kBS + pos;
+    const int lb = (BT + 64 * wm + r16) * kBS + pos;
+    auto arow = [](int i) { return DUAL ? (i < NA / 2 ? 16 * i : COLS + 16 * (i - NA / 2)) : 16 * i; };
 
     // one stage's MFMA operands: W fragments a[NA] are overwritten with the
     // next stage's one by one, each right after its last MFMA has been issued;
     // X fragments are double-buffered (read at the start of the previous stage)
     auto read_a = [&](int q, int i) {
-        const uint16_t* Ws = ring + (q % kBNST) * SE;
-        return *reinterpret_cast<const bf16x8*>(Ws + (wrow[i] + r16) * kBS + pos);
+        const uint16_t* Ws = ring + ((unsigned)q % kBNST) * SE + la;
+        return *reinterpret_cast<const bf16x8*>(Ws + arow(i) * kBS);
     };
     auto read_b = [&](bf16x8 (&b)[4], int q) {
-        const uint16_t* Xs = ring + (q % kBNST) * SE + BT * kBS;
+        const uint16_t* Xs = ring + ((unsigned)q % kBNST) * SE + lb;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = *reinterpret_cast<const bf16x8*>(Xs + (64 * wm + 16 * j + r16) * kBS + pos);
+        for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Xs + 16 * j * kBS);
     };
 
     f32x4 acc[NA][4];
@@ -764,9 +771,12 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     // (in-bounds) slot whose values are never used; the waits and barriers
     // are uniform over the workgroup.
     auto stage = [&](bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
-        ring_wait_later<L, kBNST - 2>(max(0, min(kBNST - 2, total - 2 - qc)));
+        // the next stage's copies done: the two later stages stay in flight
+        // while both were issued (qc + 3 < total); near the end wait for all
+        if (qc + 3 < total) ring_wait<L * (kBNST - 2)>();
+        else ring_wait<0>();
         ring_barrier();
-        if (qc + kBNST < total) issue((qc + kBNST) % kBNST);
+        if (qc + kBNST < total) issue((unsigned)(qc + kBNST) % kBNST);
         read_b(bn, qc + 1);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
