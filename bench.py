@@ -559,7 +559,8 @@ def main():
             roof = {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
                     "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         else:         # many rows: MFMA-bound
-            kname = "gemm_tiled_kernel<ARGMAX>" if R < 384 else "gemm_big_kernel<ARGMAX>"
+            kname = ("gemm_tiled_kernel<ARGMAX>" if R < 256 else
+                     "gemm_big_kernel<ARGMAX, 128-row tiles>" if R < 384 else "gemm_big_kernel<ARGMAX>")
             roof = {"bound": "mfma", "kernel": f"{kname} (LM head + fused argmax)",
                     "achieved": 2.0 * R * dm.V * dm.d / k_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:

@@ -14,7 +14,7 @@
 //    one row);
 //  * more rows: persistent tiles fed by a global -> LDS ring, 256 x 256 from
 //    384 rows on, 128 x 128 (two workgroups per CU) below; the LM head below
-//    384 rows uses 128 x 128 tiles staged through registers instead.
+//    256 rows uses 128 x 128 tiles staged through registers instead.
 //
 // Projections with few output columns are split over workgroups along K.
 // Those splits never meet inside the GEMM: each writes an fp32 partial plane,
@@ -321,11 +321,11 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel (the LM head at 64 < M < 384): a 128 x 128 output tile per workgroup,
+// Tiled kernel (the LM head at 64 < M < 256): a 128 x 128 output tile per workgroup,
 // K in steps of 64 staged through LDS (double buffered: the next step's
 // global loads are in registers while the current step's MFMAs run), four
 // waves each owning a 64 x 64 quarter (4 x 4 MFMA tiles); two workgroups fit
-// a CU. Used for the LM head at 64 < M < 384 rows, where the 256-row tiles
+// a CU. Used for the LM head at 64 < M < 256 rows, where the 256-row tiles
 // below would mostly be padding. For SwiGLU the tile's 128 W rows are 64 gate rows then
 // the same 64 up rows, and each wave takes 32 of each: a lane holds matching
 // gate and up columns.
@@ -862,13 +862,14 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
     GemmPlan p;
     p.nm = 1;
-    // M <= 64: weight-streaming ring. 64 < M < 384: the LM head (max/argmax
-    // epilogue) on 128 x 128 register-staged tiles, the projections on the
-    // ring-fed tile kernel with 128-row tiles; M >= 384: 256-row tiles.
-    // (Measured on the drafting step: the 128-row ring-fed kernel runs the
-    // 224-row projections of the Qwen3-Coder-scale drafter faster than the
-    // register-staged tiles, and the 112..320-row LM heads slower.)
-    p.kind = M <= 64 ? GEMM_RING : ((M < 384 && epi == EPI_ARGMAX) ? GEMM_TILED : GEMM_BIG);
+    // M <= 64: weight-streaming ring. 64 < M < 256: the LM head (max/argmax
+    // epilogue) on 128 x 128 register-staged tiles, everything else with more
+    // than 64 rows on the ring-fed tile kernel: 128-row tiles below 384 rows,
+    // 256-row tiles from there. (Measured on the drafting step: the 128-row
+    // ring-fed kernel runs the 224-row projections of the Qwen3-Coder-scale
+    // drafter and a 320-row LM head faster than the register-staged tiles,
+    // a 112-row LM head slower and a 192-row one alike.)
+    p.kind = M <= 64 ? GEMM_RING : ((M < 256 && epi == EPI_ARGMAX) ? GEMM_TILED : GEMM_BIG);
     p.splits = 1;
     p.grid = 0;
     if (p.kind == GEMM_BIG) {

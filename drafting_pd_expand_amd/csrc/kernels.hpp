@@ -47,7 +47,7 @@ struct GemmArgs {
 
 enum GemmKind : int {
     GEMM_RING = 0,    // M <= 64: persistent LDS-ring weight streaming
-    GEMM_TILED = 1,   // LM head at 64 < M < 384: 128 x 128 register-staged tiles, two workgroups per CU
+    GEMM_TILED = 1,   // LM head at 64 < M < 256: 128 x 128 register-staged tiles, two workgroups per CU
     GEMM_BIG = 2,     // other M > 64: persistent ring-fed tiles, 256 x 256 (8 waves) from 384 rows, else 128 x 128
 };
 
