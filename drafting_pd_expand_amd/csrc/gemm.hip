@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 constexpr int kTM = 128, kTN = 128, kTK = 64;
 constexpr int kTRow = kTK + 8;   // padded LDS row (elements): 144 B stride, conflict-free 16-byte reads
 
-template <int EPI>
+template <int EPI, bool WSTREAM>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
     constexpr bool DUAL = (EPI == EPI_SWIGLU);
     __shared__ __align__(16) uint16_t ws_[2][kTN * kTRow];
@@ -397,7 +397,19 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int k = k0 + ((tid + 256 * j) & 7) * 8;
-            wreg[j] = (wok[j] && k < ke) ? *reinterpret_cast<const uint4*>(wsrc[j] + k0) : make_uint4(0, 0, 0, 0);
+            // WSTREAM (one row block: every weight is read once): non-temporal
+            // loads, so the weight stream does not evict the X rows every tile
+            // re-reads from L2; with more row blocks they share each W tile in L2
+            if (wok[j] && k < ke) {
+                typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+                const u32x4* src = reinterpret_cast<const u32x4*>(wsrc[j] + k0);
+                u32x4 t;
+                if constexpr (WSTREAM) t = __builtin_nontemporal_load(src);
+                else t = *src;
+                wreg[j] = make_uint4(t.x, t.y, t.z, t.w);
+            } else {
+                wreg[j] = make_uint4(0, 0, 0, 0);
+            }
             xreg[j] = (xok[j] && k < ke) ? *reinterpret_cast<const uint4*>(xsrc[j] + k0) : make_uint4(0, 0, 0, 0);
         }
     };
@@ -820,7 +832,10 @@ int launch_big(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 template <int EPI>
 int launch_tiled(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     const int chunk = (p.ntiles * p.mblocks + 7) / 8;
-    hipLaunchKernelGGL(gemm_tiled_kernel<EPI>, dim3(8 * chunk, 1, p.splits), dim3(256), 0, s, a);
+    if (p.mblocks == 1)
+        hipLaunchKernelGGL((gemm_tiled_kernel<EPI, true>), dim3(8 * chunk, 1, p.splits), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm_tiled_kernel<EPI, false>), dim3(8 * chunk, 1, p.splits), dim3(256), 0, s, a);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
