@@ -198,9 +198,11 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
                 src = wp[j] + k0;
             else
                 src = (wp[j] && k0 + wch[j] < a.K) ? wp[j] + k0 : zp;
+            // every weight is read once: non-temporal (cache policy 2), so the
+            // stream does not evict the X columns all workgroups re-read
             __builtin_amdgcn_global_load_lds((void*)src,
                 (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
-                16, 0, 0);
+                16, 0, 2);
         }
 #pragma unroll
         for (int j = 0; j < XL; ++j) {
