@@ -962,8 +962,12 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
             if (best < 0 || span < best) { best = span; p.splits = sp; }
         }
     }
+    // as few workgroups as keep every round full: the stream is HBM-bound, so
+    // a last round with few workgroups runs far below the HBM rate (LM head
+    // at C = 1: 3,142 column tiles are 13 rounds of 242, not 12.3 of 256)
     const long items = (long)ntn * p.splits;
-    p.grid = (int)(items < 256 ? items : 256);
+    const long rounds = (items + 255) / 256;
+    p.grid = (int)((items + rounds - 1) / rounds);
     // LM head: one max/argmax partial per row per wave
     p.ntiles = (epi == EPI_ARGMAX) ? p.grid * p.wn : ntn;
     return p;
