@@ -974,18 +974,19 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
 }
 
 // Projections of 17..64 rows take two column groups per wave whenever that
-// plan still spreads over >= 240 of the 256 CUs: with two or four 16-row X
+// plan still spreads over >= 220 of the 256 CUs: with two or four 16-row X
 // tiles the X bytes staged per stage are a large share, and the wider tile
-// halves them per weight byte (LM head at 28 rows in the drafting step: 231
-// -> 228 us). With one X tile the deeper ring of the narrow tile is faster
-// (LM head at 7 rows: 207 vs 210 us), and so is the narrow tile where the
-// wide one leaves CUs idle (the d-wide outputs, whose K splits are capped
-// at 8).
+// halves them per weight byte (LM head at 28 rows in the drafting step, 225
+// workgroups in 7 full rounds: 175 vs 182 us with the narrow tile). With one
+// X tile the deeper ring of the narrow tile is faster (LM head at 7 rows:
+// 207 vs 210 us), and so is the narrow tile where the wide one leaves CUs
+// idle (the d-wide outputs, whose K splits are capped at 8: 184 workgroups,
+// g_c4 step 632 vs 623 us).
 GemmPlan plan_gemm(int M, int N, int K, int epi) {
     const GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
     if (p.kind == GEMM_RING && p.mt >= 2 && epi != EPI_SWIGLU) {
         const GemmPlan w = plan_gemm_nm(M, N, K, epi, 2);
-        if (w.grid >= 240) return w;
+        if (w.grid >= 220) return w;
     }
     return p;
 }
