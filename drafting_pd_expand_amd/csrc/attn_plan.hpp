@@ -16,7 +16,10 @@ namespace pd {
 
 constexpr int kAttnBtMax = 512;                          // block-table entries of one split cached in LDS
 constexpr int kAttnMaxSplitKeys = kAttnBtMax * PD_PAGE;  // keys of one split at most
-// split-kernel workgroups resident at once (two per CU: ~66 KB of LDS each)
+// split-kernel workgroups one round holds (two per CU). At dh 64 over a bf16
+// cache three fit, but counting 768 lets short batches take shorter splits
+// whose extra merge work costs more than it saves (4 x 17.7k keys: 8 us more
+// per step)
 constexpr int kAttnRoundSlots = 512;
 constexpr int kAttnOneRoundMaxKeys = 512;
 constexpr int kAttnPlanThreads = 256;
