@@ -20,14 +20,16 @@ import numpy as np
 import torch
 
 __all__ = [
-    "PD_OK", "PD_EINVAL", "PD_ENOMEM", "PD_EHIP", "PD_PAGE", "PD_MAX_LAYERS",
+    "PD_OK", "PD_EINVAL", "PD_ENOMEM", "PD_EHIP", "PD_ESCRATCH", "PD_PAGE", "PD_MAX_LAYERS",
+    "NOALLOC_SCRATCH_BYTES", "pd_draft_forward_noalloc",
     "KERNEL_LMHEAD", "KERNEL_GEMM", "KERNEL_ATTN", "KERNEL_OTHER",
     "PdError", "library_path", "load", "pd_expand_batch", "pd_draft_forward", "pd_ar_advance", "pd_free",
     "Handle", "batch_dims", "alloc_batch", "device_model", "pack_kv_cache",
     "unpack_kv_cache", "kv_cache_elems",
 ]
 
-PD_OK, PD_EINVAL, PD_ENOMEM, PD_EHIP = 0, -1, -2, -3
+PD_OK, PD_EINVAL, PD_ENOMEM, PD_EHIP, PD_ESCRATCH = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 64 << 20
 PD_PAGE = 16
 PD_MAX_LAYERS = 16
 KERNEL_LMHEAD, KERNEL_GEMM, KERNEL_ATTN, KERNEL_OTHER = 0, 1, 2, 3
@@ -108,6 +110,9 @@ def load():
                                         POINTER(Batch), c_void_p, c_void_p, c_void_p, c_void_p,
                                         POINTER(ForwardOpts), c_void_p]
     lib.pd_draft_forward_ex.restype = c_int
+    lib.pd_draft_forward_noalloc.argtypes = [POINTER(Model), POINTER(BatchDims), POINTER(Batch), c_void_p,
+                                             c_void_p, c_void_p, c_void_p, POINTER(ForwardOpts), c_void_p]
+    lib.pd_draft_forward_noalloc.restype = c_int
     lib.pd_ar_advance.argtypes = [POINTER(BatchDims), POINTER(Batch), c_void_p, c_void_p, POINTER(Batch),
                                   c_void_p]
     lib.pd_ar_advance.restype = c_int
@@ -302,22 +307,13 @@ def _model_struct(m: dict) -> Model:
     return st
 
 
-def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block_table, kv_cache,
-                     draft_ids, logits=None, stream=None, hidden_d=None, hidden_out=None,
-                     kv_scales=None) -> None:
-    """Enqueue the drafter pass (include/pd.h: pd_draft_forward, or
-    pd_draft_forward_ex when hidden_d / hidden_out are given or the cache is
-    fp8). `model` is a dict made by device_model(); `batch` holds the
-    expanded-batch tensors. kv_cache: bf16 (see pack_kv_cache) or uint8 E4M3
-    codes (an fp8 cache; kv_scales then gives the [N][2] per-layer K and V
-    scales, default 1.0).
-    hidden_d: bf16 [T_out][d] projected hidden rows (fc skipped);
-    hidden_out: bf16 [C*K][d] receives the sampled rows' final residual."""
-    lib = load()
+def _forward_args(model: dict, dims: dict, batch: dict, block_table, kv_cache, draft_ids, logits,
+                  hidden_d, hidden_out, kv_scales):
+    """Checked C arguments shared by the forward entry points: (model, dims,
+    batch, block table, cache, draft ids, logits) structs / pointers and the
+    options struct (None when no option is set)."""
     dm = model["dims"]
     C, K = dims["C"], dims["K"]
-    if C == 0:
-        return
     dev = batch["input_ids"].device
     ms = model.get("_struct")
     if ms is None:
@@ -333,11 +329,10 @@ def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block
     kv = _dev(kv_cache, "kv_cache", (torch.uint8,) if fp8 else _BF16, kv_cache_elems(dm, dims["num_blocks"]), dev)
     di = _dev(draft_ids, "draft_ids", (torch.int32,), C * K, dev)
     lg = _dev(logits, "logits", (torch.float32,), C * K * dm.V, dev) if logits is not None else None
-    args = (ctypes.byref(handle.ptr), ctypes.byref(ms), ctypes.byref(d), ctypes.byref(bs), c_void_p(bt),
-            c_void_p(kv), c_void_p(di), c_void_p(lg))
+    refs = (ms, d, bs)
+    args = [bt, kv, di, lg]
     if hidden_d is None and hidden_out is None and not fp8:
-        _check(lib.pd_draft_forward(*args, c_void_p(_stream_ptr(stream))), "pd_draft_forward")
-        return
+        return refs, args, None
     scales = None
     if fp8 and kv_scales is not None:
         sc = np.ascontiguousarray(np.asarray(kv_scales, dtype=np.float32).reshape(dm.N, 2))
@@ -346,7 +341,51 @@ def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block
         _dev(hidden_d, "hidden_d", _BF16, T_out * dm.d, dev) if hidden_d is not None else None,
         _dev(hidden_out, "hidden_out", _BF16, C * K * dm.d, dev) if hidden_out is not None else None,
         1 if fp8 else 0, scales)
-    _check(lib.pd_draft_forward_ex(*args, ctypes.byref(opts), c_void_p(_stream_ptr(stream))),
+    opts._scales = scales   # keep the array alive with the struct
+    return refs, args, opts
+
+
+def pd_draft_forward_noalloc(model: dict, dims: dict, batch: dict, block_table, kv_cache, draft_ids,
+                             logits=None, stream=None, hidden_d=None, hidden_out=None, kv_scales=None) -> None:
+    """Enqueue the drafter pass without a handle and without any device
+    allocation (include/pd.h: pd_draft_forward_noalloc): scratch is the
+    library's static per-GPU array. Same arguments and results as
+    pd_draft_forward; bad device data is reported in batch["status"].
+    Raises PdError(PD_ESCRATCH) when the batch needs more scratch than the
+    array holds."""
+    lib = load()
+    if dims["C"] == 0:
+        return
+    (ms, d, bs), args, opts = _forward_args(model, dims, batch, block_table, kv_cache, draft_ids, logits,
+                                            hidden_d, hidden_out, kv_scales)
+    _check(lib.pd_draft_forward_noalloc(ctypes.byref(ms), ctypes.byref(d), ctypes.byref(bs),
+                                        *[c_void_p(a) for a in args],
+                                        ctypes.byref(opts) if opts is not None else None,
+                                        c_void_p(_stream_ptr(stream))), "pd_draft_forward_noalloc")
+
+
+def pd_draft_forward(handle: Handle, model: dict, dims: dict, batch: dict, block_table, kv_cache,
+                     draft_ids, logits=None, stream=None, hidden_d=None, hidden_out=None,
+                     kv_scales=None) -> None:
+    """Enqueue the drafter pass (include/pd.h: pd_draft_forward, or
+    pd_draft_forward_ex when hidden_d / hidden_out are given or the cache is
+    fp8). `model` is a dict made by device_model(); `batch` holds the
+    expanded-batch tensors. kv_cache: bf16 (see pack_kv_cache) or uint8 E4M3
+    codes (an fp8 cache; kv_scales then gives the [N][2] per-layer K and V
+    scales, default 1.0).
+    hidden_d: bf16 [T_out][d] projected hidden rows (fc skipped);
+    hidden_out: bf16 [C*K][d] receives the sampled rows' final residual."""
+    lib = load()
+    if dims["C"] == 0:
+        return
+    (ms, d, bs), args, opts = _forward_args(model, dims, batch, block_table, kv_cache, draft_ids, logits,
+                                            hidden_d, hidden_out, kv_scales)
+    head = (ctypes.byref(handle.ptr), ctypes.byref(ms), ctypes.byref(d), ctypes.byref(bs),
+            *[c_void_p(a) for a in args])
+    if opts is None:
+        _check(lib.pd_draft_forward(*head, c_void_p(_stream_ptr(stream))), "pd_draft_forward")
+        return
+    _check(lib.pd_draft_forward_ex(*head, ctypes.byref(opts), c_void_p(_stream_ptr(stream))),
            "pd_draft_forward_ex")
 
 

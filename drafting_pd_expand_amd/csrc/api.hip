@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -29,7 +30,33 @@ struct pd_handle {
     std::vector<hipEvent_t> spare;
 };
 
+// Scratch of the allocation-free forward (pd_draft_forward_noalloc): one
+// array per device, held until the process ends. In host code `scratch` only
+// names the symbol; its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is ever
+// passed to kernels or copies.
+constexpr size_t kStaticScratchBytes = PD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+int static_scratch(char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PD_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PD_EHIP;
+        g_scratch_ptr[dev] = static_cast<char*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return PD_OK;
+}
 
 constexpr int kMaxTin = 1 << 20;
 
@@ -65,7 +92,7 @@ struct Timed {
     hipStream_t s;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     Timed(pd_handle* h_, int cls_, hipStream_t s_) : h(h_), cls(cls_), s(s_) {
-        if (h->prof & (1 << cls)) {
+        if (h && (h->prof & (1 << cls))) {
             e0 = take_event(h);
             e1 = take_event(h);
             if (e0 && e1) (void)hipEventRecord(e0, s);
@@ -85,7 +112,11 @@ struct Layout {
     AttnSplit sp;
 };
 
-Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
+// limit != 0: the attention partial planes (sized by the splits per request,
+// scap) shrink until the whole layout fits in `limit` bytes; fewer splits per
+// request only make the device plan pick longer splits. L.total > limit when
+// even the fewest splits the block table needs do not fit.
+Layout plan_layout(const pd_model* m, const pd_batch_dims* d, size_t limit = 0) {
     Layout L;
     const int T = d->T_in + d->C * (d->K - 1);
     const int R = d->C * d->K;
@@ -105,21 +136,34 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d) {
     need(T, m->d, hd);
     need(T, m->d, m->F);
     L.ntilesV = plan_gemm(R, m->V, m->d, EPI_ARGMAX).ntiles;
-    size_t off = 0;
-    auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    L.x = carve((size_t)T * m->d * 4);
-    L.u = carve((size_t)T * 2 * m->d * 2);
-    L.q = carve((size_t)T * hd * 2);
-    L.ao = carve((size_t)T * hd * 2);
-    L.act = carve((size_t)T * m->F * 2);
-    L.ws = carve(ws * 4);
-    L.po = carve((size_t)L.sp.scap * T * hd * 4);
-    L.pml = carve((size_t)L.sp.scap * T * m->Hq * 2 * 4);
-    L.plan = carve(attn_plan_ints(L.sp) * 4);
-    L.xg = carve((size_t)R * m->d * 2);
-    L.amv = carve((size_t)R * L.ntilesV * 4);
-    L.ami = carve((size_t)R * L.ntilesV * 4);
-    L.total = off;
+    auto carve_all = [&]() {
+        size_t off = 0;
+        auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+        L.x = carve((size_t)T * m->d * 4);
+        L.u = carve((size_t)T * 2 * m->d * 2);
+        L.q = carve((size_t)T * hd * 2);
+        L.ao = carve((size_t)T * hd * 2);
+        L.act = carve((size_t)T * m->F * 2);
+        L.ws = carve(ws * 4);
+        L.po = carve((size_t)L.sp.scap * T * hd * 4);
+        L.pml = carve((size_t)L.sp.scap * T * m->Hq * 2 * 4);
+        L.plan = carve(attn_plan_ints(L.sp) * 4);
+        L.xg = carve((size_t)R * m->d * 2);
+        L.amv = carve((size_t)R * L.ntilesV * 4);
+        L.ami = carve((size_t)R * L.ntilesV * 4);
+        L.total = off;
+    };
+    carve_all();
+    if (limit && L.total > limit) {
+        const size_t per_split = align256((size_t)T * hd * 4) + align256((size_t)T * m->Hq * 2 * 4);
+        const size_t fixed = L.total - (size_t)L.sp.scap * per_split;   // upper bound: alignment slack
+        const int need = attn_min_splits(d->max_blocks);
+        const long long fit = fixed < limit ? (long long)((limit - fixed) / per_split) : 0;
+        if (fit >= need && fit < L.sp.scap) {
+            L.sp.scap = (int)fit;
+            carve_all();
+        }
+    }
     return L;
 }
 
@@ -183,49 +227,16 @@ bool batch_ok(const pd_batch* b, bool hidden_optional = false) {
            b->seq_lens && (b->hidden || hidden_optional);
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* pd_strerror(int code) {
-    switch (code) {
-        case PD_OK: return "ok";
-        case PD_EINVAL: return "invalid argument";
-        case PD_ENOMEM: return "device allocation failed";
-        case PD_EHIP: return "HIP launch error";
-        default: return "unknown error";
-    }
-}
-
-int pd_expand_batch(const pd_batch_dims* dims, const pd_expand_in* in, const pd_batch* out,
-                    void* stream) {
-    if (!dims_ok(dims) || !in || !out) return PD_EINVAL;
-    if (dims->C == 0) return PD_OK;
-    if (!in->num_tokens || !in->num_rejected || !in->target_ids || !in->target_pos ||
-        !in->target_hidden || !in->next_token_ids || !in->block_table || !in->h_shared)
-        return PD_EINVAL;
-    if (!batch_ok(out)) return PD_EINVAL;
-    if (((uintptr_t)in->target_hidden | (uintptr_t)in->h_shared | (uintptr_t)out->hidden) & 15)
-        return PD_EINVAL;
-    return launch_expand(*dims, *in, *out, (hipStream_t)stream);
-}
-
-int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
-                     const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
-                     int32_t* draft_ids, float* logits, void* stream) {
-    return pd_draft_forward_ex(hp, m, dims, b, block_table, kv_cache, draft_ids, logits, nullptr,
-                               stream);
-}
-
-int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
-                        const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
-                        int32_t* draft_ids, float* logits, const pd_forward_opts* opts,
-                        void* stream) {
+// Argument checks shared by the forward entry points (nothing is enqueued
+// when they fail).
+int forward_args_ok(const pd_model* m, const pd_batch_dims* dims, const pd_batch* b,
+                    const int32_t* block_table, const uint16_t* kv_cache, const int32_t* draft_ids,
+                    const pd_forward_opts* opts) {
     const uint16_t* hidden_d = opts ? opts->hidden_d : nullptr;
-    uint16_t* hidden_out = opts ? opts->hidden_out : nullptr;
+    const uint16_t* hidden_out = opts ? opts->hidden_out : nullptr;
     const bool fp8 = opts && opts->kv_fp8;
     const float* kv_scales = fp8 ? opts->kv_scales : nullptr;
-    if (!hp || !model_ok(m) || !dims_ok(dims) || !batch_ok(b, hidden_d != nullptr)) return PD_EINVAL;
+    if (!model_ok(m) || !dims_ok(dims) || !batch_ok(b, hidden_d != nullptr)) return PD_EINVAL;
     if (kv_scales)
         for (int i = 0; i < 2 * m->N; ++i)
             if (!(kv_scales[i] > 0.f) || !std::isfinite(kv_scales[i])) return PD_EINVAL;
@@ -236,15 +247,21 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
     if (dims->max_blocks > PD_MAX_BLOCKS) return PD_EINVAL;
     if ((long long)dims->num_blocks * m->Hkv * PD_PAGE * m->dh * 2 * m->N > (1LL << 40))
         return PD_EINVAL;
-    hipStream_t s = (hipStream_t)stream;
+    return PD_OK;
+}
+
+// The launch sequence of one drafter pass on scratch S (carved as L). h may
+// be null (no event timing, no residual snapshots); st is the status word
+// bad device data is reported to (may be null).
+int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_model* m,
+                 const pd_batch_dims* dims, const pd_batch* b, const int32_t* block_table,
+                 uint16_t* kv_cache, int32_t* draft_ids, float* logits, const pd_forward_opts* opts,
+                 hipStream_t s) {
+    const uint16_t* hidden_d = opts ? opts->hidden_d : nullptr;
+    uint16_t* hidden_out = opts ? opts->hidden_out : nullptr;
+    const bool fp8 = opts && opts->kv_fp8;
+    const float* kv_scales = fp8 ? opts->kv_scales : nullptr;
     int rc;
-    if (!*hp) {
-        if ((rc = create_handle(hp)) != PD_OK) return rc;
-    }
-    pd_handle* h = *hp;
-    const Layout L = plan_layout(m, dims);
-    if ((rc = ensure_scratch(h, L.total, s)) != PD_OK) return rc;
-    char* S = h->scratch;
     float* x = (float*)(S + L.x);
     uint16_t* u = (uint16_t*)(S + L.u);
     uint16_t* q = (uint16_t*)(S + L.q);
@@ -257,7 +274,6 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
     const int hd = m->Hq * m->dh;
     // bytes of one K or V plane: bf16 elements or E4M3 codes
     const size_t plane = (size_t)dims->num_blocks * m->Hkv * PD_PAGE * m->dh * (fp8 ? 1 : 2);
-    int32_t* st = h->status;
 
     // one projection; returns its split count through *splits (EPI_PARTIAL)
     auto gemm = [&](int cls, int epi, const uint16_t* X, int ldx, const int32_t* xrows,
@@ -277,7 +293,7 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
         return launch_gemm(epi, p, a, s);
     };
     auto dbg = [&](int slot) -> int {
-        if (!h->dbg) return PD_OK;
+        if (!h || !h->dbg) return PD_OK;
         return hipMemcpyAsync(h->dbg + (size_t)slot * T * d, x, (size_t)T * d * 4,
                               hipMemcpyDeviceToDevice, s) == hipSuccess ? PD_OK : PD_EHIP;
     };
@@ -324,8 +340,8 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
         aa.fp8 = fp8; aa.k_scale = ks; aa.v_scale = vs;
         {
             hipEvent_t e0 = nullptr, e1 = nullptr, e2 = nullptr, e3 = nullptr;
-            if (h->prof & (1 << PD_KERNEL_ATTN)) { e0 = take_event(h); e1 = take_event(h); }
-            if (h->prof & (1 << PD_KERNEL_OTHER)) { e2 = take_event(h); e3 = take_event(h); }
+            if (h && (h->prof & (1 << PD_KERNEL_ATTN))) { e0 = take_event(h); e1 = take_event(h); }
+            if (h && (h->prof & (1 << PD_KERNEL_OTHER))) { e2 = take_event(h); e3 = take_event(h); }
             rc = launch_attention(m->dh, aa, s, e0, e1, e2, e3);
             if (e0 && e1) h->ev[PD_KERNEL_ATTN].emplace_back(e0, e1);
             if (e2 && e3) h->ev[PD_KERNEL_OTHER].emplace_back(e2, e3);
@@ -346,7 +362,7 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
             if (l + 1 < m->N) {
                 // next layer's input norm
                 PD_TRY(launch_resid_norm(ws, sp, x, m->norm_in[l + 1], u, T, d, m->rms_eps, s));
-            } else if (h->dbg) {
+            } else if (h && h->dbg) {
                 // the residual snapshot needs every row's final x
                 PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, u, T, d, m->rms_eps, s));
             } else {
@@ -357,7 +373,7 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
         }
         PD_TRY(dbg(l + 1));
     }
-    if (h->dbg) {
+    if (h && h->dbg) {
         Timed t(h, PD_KERNEL_OTHER, s);
         PD_TRY(launch_resid_norm(nullptr, 0, x, m->norm_final, xg, T, d, m->rms_eps, s,
                                  b->new_token_indices, R, st, hidden_out));
@@ -372,6 +388,73 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
     }
 #undef PD_TRY
     return PD_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+const char* pd_strerror(int code) {
+    switch (code) {
+        case PD_OK: return "ok";
+        case PD_EINVAL: return "invalid argument";
+        case PD_ENOMEM: return "device allocation failed";
+        case PD_EHIP: return "HIP launch error";
+        case PD_ESCRATCH: return "workspace exceeds the static scratch of the allocation-free forward";
+        default: return "unknown error";
+    }
+}
+
+int pd_expand_batch(const pd_batch_dims* dims, const pd_expand_in* in, const pd_batch* out,
+                    void* stream) {
+    if (!dims_ok(dims) || !in || !out) return PD_EINVAL;
+    if (dims->C == 0) return PD_OK;
+    if (!in->num_tokens || !in->num_rejected || !in->target_ids || !in->target_pos ||
+        !in->target_hidden || !in->next_token_ids || !in->block_table || !in->h_shared)
+        return PD_EINVAL;
+    if (!batch_ok(out)) return PD_EINVAL;
+    if (((uintptr_t)in->target_hidden | (uintptr_t)in->h_shared | (uintptr_t)out->hidden) & 15)
+        return PD_EINVAL;
+    return launch_expand(*dims, *in, *out, (hipStream_t)stream);
+}
+
+int pd_draft_forward(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
+                     const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
+                     int32_t* draft_ids, float* logits, void* stream) {
+    return pd_draft_forward_ex(hp, m, dims, b, block_table, kv_cache, draft_ids, logits, nullptr,
+                               stream);
+}
+
+int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* dims,
+                        const pd_batch* b, const int32_t* block_table, uint16_t* kv_cache,
+                        int32_t* draft_ids, float* logits, const pd_forward_opts* opts,
+                        void* stream) {
+    if (!hp) return PD_EINVAL;
+    int rc = forward_args_ok(m, dims, b, block_table, kv_cache, draft_ids, opts);
+    if (rc != PD_OK || dims->C == 0) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (!*hp) {
+        if ((rc = create_handle(hp)) != PD_OK) return rc;
+    }
+    pd_handle* h = *hp;
+    const Layout L = plan_layout(m, dims);
+    if ((rc = ensure_scratch(h, L.total, s)) != PD_OK) return rc;
+    return forward_impl(h, h->scratch, L, h->status, m, dims, b, block_table, kv_cache, draft_ids, logits,
+                        opts, s);
+}
+
+int pd_draft_forward_noalloc(const pd_model* m, const pd_batch_dims* dims, const pd_batch* b,
+                             const int32_t* block_table, uint16_t* kv_cache, int32_t* draft_ids,
+                             float* logits, const pd_forward_opts* opts, void* stream) {
+    int rc = forward_args_ok(m, dims, b, block_table, kv_cache, draft_ids, opts);
+    if (rc != PD_OK || dims->C == 0) return rc;
+    const Layout L = plan_layout(m, dims, kStaticScratchBytes);
+    if (L.total > kStaticScratchBytes) return PD_ESCRATCH;
+    char* S = nullptr;
+    if ((rc = static_scratch(&S)) != PD_OK) return rc;
+    return forward_impl(nullptr, S, L, b->status, m, dims, b, block_table, kv_cache, draft_ids, logits, opts,
+                        (hipStream_t)stream);
 }
 
 int pd_ar_advance(const pd_batch_dims* dims_prev, const pd_batch* prev, const int32_t* draft_ids,

@@ -606,6 +606,11 @@ AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks)
     return p;
 }
 
+int attn_min_splits(int max_blocks) {
+    const long long reach = (long long)max_blocks * PD_PAGE;
+    return (int)std::max(1LL, (reach + kMaxSplitKeys - 1) / kMaxSplitKeys);
+}
+
 int launch_attn_plan(const AttnArgs& a, hipStream_t s) {
     if (a.C <= 0) return PD_OK;
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(kAttnPlanThreads), 0, s, a);

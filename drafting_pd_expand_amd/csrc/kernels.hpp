@@ -106,6 +106,8 @@ struct AttnSplit {
     int max_units;   // capacity of the unit list = grid x of the split kernel
 };
 AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks);
+// the fewest splits per request (scap) that cover max_blocks pages of keys
+int attn_min_splits(int max_blocks);
 // int32 words of the plan: [units, split_len, -, -, ns[PD_MAX_C],
 // unit records[max_units][kPlanRec]]
 constexpr int kPlanNs = 4;

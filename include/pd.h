@@ -20,7 +20,8 @@
  *     it, except where a call says it may synchronize.
  *   - Return codes: PD_OK, or PD_EINVAL for bad host arguments (nothing is
  *     enqueued), PD_ENOMEM when a library scratch allocation fails, PD_EHIP
- *     when a launch reports a HIP error.
+ *     when a launch reports a HIP error, PD_ESCRATCH when a call of the
+ *     allocation-free forward needs more than its static scratch.
  *   - Device data is never trusted for addressing: an index that would fall
  *     outside a buffer is skipped and a bit is set in a device status word
  *     (PD_STATUS_*), which the caller reads after the stream is done.
@@ -39,6 +40,7 @@ extern "C" {
 #define PD_EINVAL (-1)
 #define PD_ENOMEM (-2)
 #define PD_EHIP   (-3)
+#define PD_ESCRATCH (-4)  /* pd_draft_forward_noalloc: the call needs more than its static scratch */
 
 #define PD_MAX_C      1024  /* requests per step (the blog's serving runs allow 1024 sequences) */
 #define PD_MAX_K      16    /* draft depth; the blog's drafter predicts up to 10 tokens */
@@ -254,6 +256,33 @@ int pd_draft_forward_ex(pd_handle** h, const pd_model* m, const pd_batch_dims* d
  * next->status (if given) and gives a row with slot -1. */
 int pd_ar_advance(const pd_batch_dims* dims_prev, const pd_batch* prev, const int32_t* draft_ids,
                   const int32_t* block_table, const pd_batch* next, void* stream);
+
+/* ---- allocation-free forward -------------------------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * pd_draft_forward_noalloc is pd_draft_forward_ex without a handle: its
+ * scratch (activations, split-K partials, attention partials and plan, LM-head
+ * partials) lives in one static device array of PD_NOALLOC_SCRATCH_BYTES per
+ * GPU, which the library holds from its first use on that GPU until the
+ * process ends. The call allocates nothing: no hipMalloc, hipFree or
+ * allocating library routine. Arguments, layouts, kernels and results are
+ * those of pd_draft_forward_ex (opts may be NULL); bad device data sets
+ * PD_STATUS_* bits in batch->status when it is non-NULL.
+ *
+ * Every call on a GPU shares that GPU's array and leaves its contents behind;
+ * calls that overlap on one GPU (other streams, other threads) race and give
+ * undefined results: serialize them. Nothing in the array has to start at
+ * zero. A batch whose workspace does not fit returns PD_ESCRATCH and enqueues
+ * nothing (the attention partials take fewer, longer splits per request before
+ * that: same results up to the order of rounding). With 64 MiB the
+ * GPT-OSS-20B-scale drafter fits up to a few hundred expanded rows.
+ */
+#define PD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int pd_draft_forward_noalloc(const pd_model* m, const pd_batch_dims* dims, const pd_batch* batch,
+                             const int32_t* block_table, uint16_t* kv_cache, int32_t* draft_ids,
+                             float* logits, const pd_forward_opts* opts, void* stream);
 
 /* ---- extras ---------------------------------------------------------------- */
 

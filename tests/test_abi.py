@@ -211,3 +211,25 @@ def test_verify_stub_rejects_bad_calls(lib):
         assert lib.pd_verify_stub(ctypes.byref(d), ctypes.byref(b), *a, None) == pdx.PD_EINVAL, i
     assert lib.pd_verify_stub(ctypes.byref(_dims(K=0)), ctypes.byref(b), *args, None) == pdx.PD_EINVAL
     assert lib.pd_verify_stub(ctypes.byref(_dims(C=0)), ctypes.byref(b), *args, None) == pdx.PD_OK
+
+
+def test_forward_noalloc_rejects_bad_calls_and_oversize(lib):
+    """The allocation-free forward checks its host arguments like
+    pd_draft_forward_ex and refuses, before touching a device, a batch whose
+    workspace exceeds the static scratch (PD_ESCRATCH)."""
+    m, b = _model(), _fake_batch()
+    d = _dims(hidden3=768)
+    f = lib.pd_draft_forward_noalloc
+    assert f(None, ctypes.byref(d), ctypes.byref(b), FAKE, FAKE, FAKE, None, None, None) == pdx.PD_EINVAL
+    assert f(ctypes.byref(m), ctypes.byref(_dims(hidden3=768, K=0)), ctypes.byref(b), FAKE, FAKE, FAKE,
+             None, None, None) == pdx.PD_EINVAL
+    assert f(ctypes.byref(m), ctypes.byref(d), ctypes.byref(b), None, FAKE, FAKE, None, None, None) == pdx.PD_EINVAL
+    assert f(ctypes.byref(m), ctypes.byref(_dims(C=0, T_in=0, hidden3=768)), ctypes.byref(b), FAKE, FAKE, FAKE,
+             None, None, None) == pdx.PD_OK
+    # the GPT-OSS-20B-scale drafter at 64 requests x K = 7 (896 expanded rows):
+    # its split-K planes alone need more than the static array
+    big = _model(d=2880, hidden3=8640, Hq=64, Hkv=8, dh=64, F=7680, N=4, V=201088)
+    dbig = _dims(C=64, K=7, T_in=512, hidden3=8640, max_blocks=1280, num_blocks=90000)
+    assert f(ctypes.byref(big), ctypes.byref(dbig), ctypes.byref(b), FAKE, FAKE, FAKE, None, None,
+             None) == pdx.PD_ESCRATCH
+    assert lib.pd_strerror(pdx.PD_ESCRATCH).startswith(b"workspace exceeds")
