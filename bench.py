@@ -1,18 +1,29 @@
 """Benchmark of the P-EAGLE parallel drafting step on one MI355X.
 
 One step = pd_expand_batch + pd_draft_forward for the whole batch (every row
-of the hot path), on synthetic inputs already resident in HBM. Default
-workload: the GPT-OSS-20B-scale drafter at C=1, context 4096, K=7.
+of the hot path), on synthetic inputs already resident in HBM. Headline
+workload: the GPT-OSS-20B-scale drafter at C=1, context 4096, K=7; then the
+same drafter at C=4 and C=64 (K=7, and K=3 / 5 for the one-pass cost against
+K) and the Qwen3-Coder-30B-scale drafter at C=16, each timed the same way.
 
-    python bench.py [--steps K] [--warmup W] [--workload g_c1|g_c4|g_c64|...]
+    python bench.py [--steps K] [--warmup W] [--workload g_c1] [--configs g_c4,...|none]
 
 Prints ONE JSON line on stdout (progress goes to stderr):
-  value      draft steps/s (drafted tokens/s = value * C * K is reported too)
-  roofline   the dominant kernel's achieved bandwidth (algorithmic bytes per
-             launch / average launch time from HIP events on the launch
-             stream during the timed region) against the 8 TB/s HBM peak
+  value      draft steps/s of the headline workload (drafted tokens/s =
+             value * C * K is reported too)
+  roofline   the headline's dominant kernel: achieved bandwidth or flop rate
+             (algorithmic bytes or flops per launch / average launch time
+             from HIP events on the launch stream during the timed region)
+             against the 8 TB/s HBM or 2.5 PFLOP/s bf16 peak
   cpu_baseline  the fp64 oracle (expand + forward) timed on the host cores on
              a bounded sample of the same workload
+  configs    per workload: us/step, steps/s, drafted tok/s, the step's share
+             of the HBM roofline, the dominant kernel's roofline, the GEMMs'
+             MFMA roofline (flops of the non-rejected rows / summed GEMM
+             launch time, from events around the GEMM launches only, in a
+             second timed region) and the oracle on request 0
+  yardsticks measured-peak references: a streaming read, a device copy and
+             the installed vendor bf16 GEMM (torch.matmul) on two shapes
 """
 from __future__ import annotations
 
@@ -409,27 +420,62 @@ def partition_leg(pdx, stream, reps: int = 20) -> dict:
                          "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "bytes_per_call": alg}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="g_c1", choices=sorted(DESCR))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 512 MiB device copy (counter calibration) and exit")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "the drafting step runs on one GPU only; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+def yardsticks() -> dict:
+    """Measured-peak yardsticks beside the spec peaks (not targets): a plain
+    streaming read (sum of a 2 GiB bf16 tensor, fp32 accumulation in torch),
+    a device-to-device copy of 1 GiB, and torch.matmul in bf16 (the installed
+    vendor GEMM) at the C = 64, K = 7 LM-head shape (448 x 2880 by
+    2880 x 201088) and at a large square shape."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
 
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1000.0
+
+    x = torch.ones(1 << 30, dtype=torch.bfloat16, device=dev)          # 2 GiB
+    t = timed(lambda: x.sum(dtype=torch.float32), 10)
+    out["stream_read_GBps"] = x.numel() * 2 / t / 1e9
+    del x
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)           # 1 GiB
+    b = torch.empty_like(a)
+    t = timed(lambda: b.copy_(a), 10)
+    out["copy_GBps_read_plus_write"] = 2 * a.numel() * 4 / t / 1e9
+    del a, b
+    for name, (M, K, N) in (("lm_head_c64_k7", (448, 2880, 201088)), ("square_8192", (8192, 8192, 8192))):
+        A = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
+        B = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
+        t = timed(lambda: torch.matmul(A, B), 10)
+        out[f"matmul_bf16_{name}"] = {"shape_MKN": [M, K, N], "us": t * 1e6,
+                                      "TFLOPs": 2.0 * M * N * K / t / 1e12,
+                                      "frac_of_2500": 2.0 * M * N * K / t / 1e12 / BF16_PEAK_TFLOPS}
+        del A, B
+    torch.cuda.empty_cache()
+    log(f"[bench] yardsticks: read {out['stream_read_GBps']:.0f} GB/s, copy {out['copy_GBps_read_plus_write']:.0f} "
+        f"GB/s, matmul LM head {out['matmul_bf16_lm_head_c64_k7']['TFLOPs']:.0f} TFLOP/s, "
+        f"8192^3 {out['matmul_bf16_square_8192']['TFLOPs']:.0f} TFLOP/s")
+    return out
+
+
+def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu_s: float = 10.0) -> dict:
+    """One workload: warm-up, a timed region of plain launches (HIP events on
+    the launch stream around each step and around the dominant kernel's
+    launches), a second timed region with events around every GEMM launch
+    (projections + LM head) for the GEMM roofline, and optionally the report
+    extras (hipGraph replay, autoregressive baseline, sequence partitioning,
+    fp8 cache, multi-round loop) and the CPU oracle baseline."""
     import torch
     import synth
     import drafting_pd_expand_amd as pdx
+
     def i32(a, dev):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
@@ -437,12 +483,10 @@ def main():
         a = np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)
         return torch.from_numpy(a).to(dev).view(torch.bfloat16)
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    pdx.load()
     dev = torch.device("cuda:0")
-    w = synth.get_workload(args.workload)
+    w = synth.get_workload(workload)
     dm = w.model
-    log(f"[bench] {args.workload}: generating model + inputs")
+    log(f"[bench] {workload}: generating model + inputs")
     t0 = time.perf_counter()
     model_np = synth.make_model(dm, seed=1234)
     b = synth.make_batch(w)
@@ -458,6 +502,9 @@ def main():
     }
     out = pdx.alloc_batch(dims, dev)
     cache = pdx.pack_kv_cache(bf16(pool["k"], dev), bf16(pool["v"], dev))
+    if not cpu:
+        del pool
+        pool = None
     R = b["C"] * w.K
     draft = torch.empty(R, dtype=torch.int32, device=dev)
     h = pdx.Handle()
@@ -467,54 +514,127 @@ def main():
         pdx.pd_expand_batch(dims, inp, out, strm)
         pdx.pd_draft_forward(h, mdev, dims, out, inp["block_table"], cache, draft, None, strm)
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
+    log(f"[bench] warmup {warmup}")
+    for _ in range(max(1, warmup)):
         step(stream)
     torch.cuda.synchronize()
     st = h.status() | int(out["status"].item())
     if st:
-        raise SystemExit(f"device status {st} after warmup")
+        raise SystemExit(f"{workload}: device status {st} after warmup")
     eager_ids = draft.clone()
 
-    # breakdown pass (not the timed region): events around every kernel class
-    nb = min(5, args.steps)
-    h.profile((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_GEMM) | (1 << pdx.KERNEL_ATTN) | (1 << pdx.KERNEL_OTHER))
-    for _ in range(nb):
-        step(stream)
+    # which kernel dominates: the LM head (one launch) or the attention kernel
+    # (one per layer), from one step with events around those two classes
+    h.profile((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_ATTN))
+    step(stream)
     torch.cuda.synchronize()
-    cls_us = {}
-    for name, k in (("lm_head", pdx.KERNEL_LMHEAD), ("gemm", pdx.KERNEL_GEMM), ("attention", pdx.KERNEL_ATTN),
-                    ("other", pdx.KERNEL_OTHER)):
-        t_ms, n = h.profile_read(k)
-        cls_us[name] = {"us_per_step": t_ms * 1000.0 / nb, "launches_per_step": n // nb,
-                        "us_per_launch": t_ms * 1000.0 / max(n, 1)}
+    lm_ms, lm_n = h.profile_read(pdx.KERNEL_LMHEAD)
+    at_ms, at_n = h.profile_read(pdx.KERNEL_ATTN)
     h.profile(0)
-    # the dominant single kernel: the LM head (one launch) or the attention kernel (one per layer)
-    dom = "lm_head" if cls_us["lm_head"]["us_per_launch"] >= cls_us["attention"]["us_per_launch"] else "attention"
+    dom = "lm_head" if lm_ms / max(lm_n, 1) >= at_ms / max(at_n, 1) else "attention"
     dom_cls = pdx.KERNEL_LMHEAD if dom == "lm_head" else pdx.KERNEL_ATTN
 
-    # timed region: plain launches; HIP events around the dominant kernel only
-    h.profile(1 << dom_cls)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps (plain launches)")
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    def timed_region(class_mask):
+        h.profile(class_mask)
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            step(stream)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+        return evs[0].elapsed_time(evs[-1]) / steps, per
+
+    # timed region: plain launches; events around the dominant kernel only
+    log(f"[bench] {workload}: timing {steps} steps (plain launches)")
     w0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step(stream)
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
+    ms_step, per = timed_region(1 << dom_cls)
     wall = time.perf_counter() - w0
-    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
-    ms = evs[0].elapsed_time(evs[-1])
     k_ms, k_n = h.profile_read(dom_cls)
     h.profile(0)
-    ms_step = ms / args.steps
     steps_s = 1000.0 / ms_step
     k_avg_s = k_ms / max(k_n, 1) / 1000.0
 
-    # the same step as one hipGraph replayed; every replay's draft ids must equal the eager ones
-    graph = None
+    # second timed region: events around every GEMM launch (and nothing else)
+    ms_g, _ = timed_region((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_GEMM))
+    g_ms, g_n = h.profile_read(pdx.KERNEL_GEMM)
+    l_ms, l_n = h.profile_read(pdx.KERNEL_LMHEAD)
+    h.profile(0)
+    gemm_us = (g_ms + l_ms) * 1000.0 / steps
+    proj_us = g_ms * 1000.0 / steps
+    lm_us = l_ms * 1000.0 / steps
+    gf = gemm_flops(dm, b, w.K)
+    lm_flops = 2.0 * R * dm.V * dm.d
+
+    if dom == "lm_head":
+        if R <= 64:   # weight-streaming ring kernel: HBM-bound
+            roof = {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
+                    "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+        else:         # many rows: MFMA-bound
+            kname = ("gemm_tiled_kernel<ARGMAX>" if R < 256 else
+                     "gemm_big_kernel<ARGMAX, 128-row tiles>" if R < 384 else "gemm_big_kernel<ARGMAX>")
+            roof = {"bound": "mfma", "kernel": f"{kname} (LM head + fused argmax)",
+                    "achieved": lm_flops / k_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "kernel": f"attn_split_kernel<{dm.dh}> (paged split-KV attention)",
+                "achieved": attn_bytes(dm, b, w.K) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = recorded_traffic(workload) if dom == "lm_head" and R <= 64 else None
+    roof["us_per_launch"] = k_avg_s * 1e6
+    sb = step_bytes(dm, b, w.K)
+    v = b["num_tokens"] - b["num_rejected"]
+    T_eff = int((v + w.K - 1).sum())
+    log(f"[bench] {workload}: {ms_step * 1000:.1f} us/step ({steps_s:.1f} steps/s, {steps_s * R:.0f} drafted tok/s); "
+        f"dominant {dom} {k_avg_s * 1e6:.1f} us = {roof['achieved']:.0f} {roof['unit']} ({roof['frac']:.2f}); "
+        f"step {sb / 1e9:.3f} GB = {sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS:.2f} of HBM; GEMMs {gemm_us:.0f} us "
+        f"(in a {ms_g * 1000:.0f} us step) = {gf / (gemm_us * 1e-6) / 1e12:.0f} TFLOP/s on {T_eff} rows")
+    leg = {
+        "workload": f"{workload}: {DESCR[workload]}",
+        "C": w.C, "K": w.K, "T_in": b["T_in"], "T_out": b["T_in"] + w.C * (w.K - 1), "T_eff": T_eff,
+        "us_per_step": ms_step * 1000.0,
+        "steps_per_s": steps_s,
+        "drafted_tok_per_s": steps_s * R,
+        "ms_per_step_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
+        "wall_us_per_step": wall * 1e6 / steps,
+        "step_algorithmic_bytes": sb,
+        "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roof,
+        "gemm_roofline": {
+            "bound": "mfma", "kernels": "every projection GEMM + the LM head",
+            "flops_per_step": gf, "rows_credited": T_eff,
+            "us_per_step": gemm_us, "projections_us": proj_us, "lm_head_us": lm_us,
+            "launches_per_step": (g_n + l_n) // steps,
+            "achieved": gf / (gemm_us * 1e-6) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": gf / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "step_us_in_this_region": ms_g * 1000.0,
+        },
+    }
+    if extras:
+        leg["hipgraph"] = graph_leg(step, draft, eager_ids, stream, steps)
+        ar = ar_baseline(pdx, mdev, b, w, inp, cache, draft, stream, steps)
+        ar["parallel_speedup"] = ar["ms_per_step"] / ms_step
+        leg["ar_baseline"] = ar
+        leg["seq_partition"] = partition_leg(pdx, stream)
+        leg["kv_fp8"] = fp8_leg(pdx, mdev, w, b, dims, inp, cache, stream, max(5, steps // 2), eager_ids,
+                                at_ms * 1000.0 / max(at_n, 1))
+        leg["multi_round"] = rounds_leg(pdx, mdev, w, stream)
+    h.free()
+    del cache, mdev, inp, out
+    torch.cuda.empty_cache()
+    if cpu:
+        log(f"[bench] {workload}: timing the CPU oracle on a bounded sample")
+        c = cpu_baseline(w, model_np, b, pool, min_s=cpu_s)
+        log(f"[bench] oracle {c['seconds']:.2f} s on {c['cores']} cores")
+        c.pop("seconds")
+        leg["cpu_baseline"] = c
+    return leg
+
+
+def graph_leg(step, draft, eager_ids, stream, steps: int) -> dict:
+    """The same step captured once as a hipGraph and replayed; every
+    replay's draft ids must equal the eager ones."""
+    import torch
     try:
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
@@ -534,86 +654,91 @@ def main():
             ok = ok and bool(torch.equal(draft, eager_ids))
         ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ge0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(steps):
             g.replay()
         ge1.record(stream)
         torch.cuda.synchronize()
-        g_ms = ge0.elapsed_time(ge1) / args.steps
-        graph = {"steps_per_s": 1000.0 / g_ms, "ms_per_step": g_ms, "replays_match_eager": ok}
+        g_ms = ge0.elapsed_time(ge1) / steps
         log(f"[bench] hipGraph replay {g_ms * 1000:.1f} us/step, draft ids match eager: {ok}")
         del g
+        return {"steps_per_s": 1000.0 / g_ms, "ms_per_step": g_ms, "replays_match_eager": ok}
     except Exception as ex:  # graph capture is a report extra; the plain-launch number stands
         log(f"[bench] hipGraph replay skipped: {ex}")
-        graph = {"error": str(ex)[:200]}
+        return {"error": str(ex)[:200]}
 
-    ar = ar_baseline(pdx, mdev, b, w, inp, cache, draft, stream, args.steps)
-    ar["parallel_speedup"] = ar["ms_per_step"] / ms_step
-    part = partition_leg(pdx, stream)
-    kv8 = fp8_leg(pdx, mdev, w, b, dims, inp, cache, stream, max(5, args.steps // 2), eager_ids,
-                  cls_us["attention"]["us_per_launch"])
-    multi = rounds_leg(pdx, mdev, w, stream)
 
-    R = b["C"] * w.K
-    if dom == "lm_head":
-        if R <= 64:   # weight-streaming ring kernel: HBM-bound
-            roof = {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
-                    "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        else:         # many rows: MFMA-bound
-            kname = ("gemm_tiled_kernel<ARGMAX>" if R < 256 else
-                     "gemm_big_kernel<ARGMAX, 128-row tiles>" if R < 384 else "gemm_big_kernel<ARGMAX>")
-            roof = {"bound": "mfma", "kernel": f"{kname} (LM head + fused argmax)",
-                    "achieved": 2.0 * R * dm.V * dm.d / k_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "kernel": f"attn_split_kernel<{dm.dh}> (paged split-KV attention)",
-                "achieved": attn_bytes(dm, b, w.K) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(args.workload) if dom == "lm_head" and R <= 64 else None
-    roof["us_per_launch"] = k_avg_s * 1e6
-    sb = step_bytes(dm, b, w.K)
-    gf = gemm_flops(dm, b, w.K)
-    gemm_us = cls_us["gemm"]["us_per_step"] + cls_us["lm_head"]["us_per_step"]
-    log(f"[bench] {ms_step * 1000:.1f} us/step ({steps_s:.1f} steps/s, wall {wall * 1000 / args.steps:.1f} us/step); "
-        f"dominant {dom} {k_avg_s * 1e6:.1f} us = {roof['achieved']:.0f} {roof['unit']}; whole step "
-        f"{sb / 1e9:.3f} GB algorithmic = {sb / (ms_step / 1000) / 1e9:.0f} GB/s; GEMMs {gemm_us:.0f} us = "
-        f"{gf / (gemm_us * 1e-6) / 1e12:.0f} TFLOP/s")
+CONFIG_LEGS = ["g_c4", "g_c64", "g_c64_k3", "g_c64_k5", "q_c16"]
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w, model_np, b, pool)
-        log(f"[bench] oracle {cpu['seconds']:.2f} s on {cpu['cores']} cores")
-        cpu.pop("seconds")
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="g_c1", choices=sorted(DESCR),
+                    help="the headline workload (value, roofline, cpu_baseline and the report extras)")
+    ap.add_argument("--configs", default=",".join(CONFIG_LEGS),
+                    help="comma-separated further workloads timed after the headline one ('none' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the headline leg's report extras")
+    ap.add_argument("--no-yardsticks", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "the drafting step runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import drafting_pd_expand_amd as pdx
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pdx.load()
+    legs = [c for c in args.configs.split(",") if c and c != "none" and c != args.workload]
+    for c in legs:
+        if c not in DESCR:
+            raise SystemExit(f"unknown workload {c}")
+    head = run_leg(args.workload, args.steps, args.warmup, extras=not args.no_extras,
+                   cpu=not args.no_cpu_baseline, cpu_s=10.0)
+    configs = {args.workload: {k: head[k] for k in ("us_per_step", "steps_per_s", "drafted_tok_per_s",
+                                                     "step_hbm_frac", "roofline", "gemm_roofline")}}
+    for c in legs:
+        leg = run_leg(c, args.steps, max(2, args.warmup // 2), extras=False, cpu=not args.no_cpu_baseline,
+                      cpu_s=4.0)
+        configs[c] = leg
+    ys = None if args.no_yardsticks else yardsticks()
 
     res = {
         "metric": "draft steps/s & drafted tok/s (K=7) at C=1/4/64; % HBM / MFMA roofline",
-        "value": steps_s,
+        "value": head["steps_per_s"],
         "unit": "draft steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["us_per_step"] / 1000.0,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "C": w.C, "K": w.K,
-                   "T_in": b["T_in"], "T_out": b["T_in"] + w.C * (w.K - 1)},
-        "drafted_tok_per_s": steps_s * R,
-        "ms_per_step_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
-        "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
-        "step_algorithmic_bytes": sb,
-        "gemm_mfma_frac": gf / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
-        "kernel_classes_us_per_step": {k: round(v["us_per_step"], 1) for k, v in cls_us.items()},
-        "hipgraph": graph,
-        "ar_baseline": ar,
-        "seq_partition": part,
-        "kv_fp8": kv8,
-        "multi_round": multi,
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "config": {"workload": head["workload"], "C": head["C"], "K": head["K"], "T_in": head["T_in"],
+                   "T_out": head["T_out"]},
+        "drafted_tok_per_s": head["drafted_tok_per_s"],
+        "ms_per_step_p10_p50_p90": head["ms_per_step_p10_p50_p90"],
+        "step_hbm_frac": head["step_hbm_frac"],
+        "step_algorithmic_bytes": head["step_algorithmic_bytes"],
+        "gemm_mfma_frac": head["gemm_roofline"]["frac"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "configs": configs,
+        "yardsticks": ys,
     }
-    h.free()
+    for k in ("hipgraph", "ar_baseline", "seq_partition", "kv_fp8", "multi_round"):
+        if k in head:
+            res[k] = head[k]
     print(json.dumps(res))
 
 

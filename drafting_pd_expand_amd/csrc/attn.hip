@@ -360,7 +360,19 @@ __global__ __launch_bounds__((64 * AttnCfg<DH, F8>::NW)) void attn_split_kernel(
                         vf[j] = fp8x8_to_bf16(w.x, w.y);
                     }
                 }
-                const int t0 = p0 + 8 * g4;   // keys t0 .. t0+7 in this lane's scores
+                const int t0 = p0 + 8 * g4;   // keys t0 .. t0+7 in this lane's scores (and V fragments)
+                if (p0 + 2 * PD_PAGE > ke) {
+                    // the pair reaches past the split's last key: the slots from ke on
+                    // are not part of the context and may hold anything (NaN / Inf
+                    // codes included), and a masked key's zero weight would not
+                    // cancel them in the PV product, so their V elements are zeroed
+                    const int nin = ke - t0;   // keys t0 .. t0+nin-1 are inside
+#pragma unroll
+                    for (int j = 0; j < OT; ++j)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (e >= nin) vf[j][e] = (__bf16)0.0f;
+                }
 #pragma unroll
                 for (int tt = 0; tt < TPW; ++tt) {
                     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};

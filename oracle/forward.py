@@ -19,7 +19,10 @@ Readings taken where the pages leave a step open:
   * combine = concatenation (the Input_i equation's direct-sum sign and the
     blog's "concatenated"): layer 0 consumes [RMSNorm(emb; g_e) || RMSNorm(
     fc(h); g_h)] (2d wide) in its QKV projection, and the residual stream
-    starts at fc(h); layers 1..N-1 are plain pre-norm LLaMA layers;
+    starts at fc(h); layers 1..N-1 are plain pre-norm LLaMA layers. The other
+    reading (the paper's "embedding + projected hidden state": the residual
+    starts at emb + fc(h), layer 0 is a plain layer) is kept as
+    combine="sum";
   * h_shared is 3d wide and goes through fc like any target row;
   * every non-rejected row is computed (the whole copied verify window plus
     the MASK rows), not only the K sampled rows;
@@ -86,7 +89,8 @@ def _softmax(s: np.ndarray) -> np.ndarray:
 
 
 def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
-                  requests=None, block_size: int = 16, return_layers: bool = False, kv_fp8=None) -> dict:
+                  requests=None, block_size: int = 16, return_layers: bool = False, kv_fp8=None,
+                  combine: str = "concat") -> dict:
     """Run the drafter over the expanded batch `exp` (the oracle's own expansion).
 
     model: bf16-bit weights as made by synth.make_model (row-major [out][in]).
@@ -105,12 +109,22 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
     is stored as the code of value / scale (oracle.fp8) and read back as
     code value * scale; kv then holds uint8 codes (or values already read
     back).
+    combine: how the token embedding and the projected hidden state meet.
+    "concat" (the reading taken everywhere else: the Input_i equation's
+    direct-sum sign in [Blog] "P-EAGLE core method") -- layer 0's QKV reads
+    [RMSNorm(emb; norm_emb) || RMSNorm(fc(h); norm_hid)], 2d wide, and the
+    residual starts at fc(h). "sum" (the other reading, [Paper] sec. 2
+    architecture: the embedding plus the projected hidden state) -- the
+    residual starts at emb + fc(h) and layer 0 is a plain pre-norm layer
+    (norm_in of layer 0, a d-wide QKV).
     Returns logits [R][V] and draft_ids [R] for the K sampled rows of each
     requested request (request-major, NTP row first), hidden_out [R][d] (their
     final residual, before the final norm), the K/V each layer wrote (slots,
     k, v), and optionally the residual stream after fc and after every layer.
     """
     m = model["dims"]
+    if combine not in ("concat", "sum"):
+        raise ValueError(f"combine must be 'concat' or 'sum', not {combine!r}")
     eps, theta = m.rms_eps, m.rope_theta
     G = m.Hq // m.Hkv
     cu = np.asarray(exp["cu_out"], np.int64)
@@ -151,11 +165,13 @@ def draft_forward(model: dict, exp: dict, block_table, kv: dict, K: int,
     if use_d.any():
         x[use_d] = np.asarray(exp["hidden_d"], np.float64)[rows[use_d]]
     e = bf16_to_f64(np.asarray(model["embed"])[ids])
+    if combine == "sum":
+        x = x + e
     layers_out = [x.copy()] if return_layers else None
     written = []
 
     for l, L in enumerate(model["layers"]):
-        if l == 0:
+        if l == 0 and combine == "concat":
             u = np.concatenate([rms_norm(e, bf16_to_f64(model["norm_emb"]), eps),
                                 rms_norm(x, bf16_to_f64(model["norm_hid"]), eps)], axis=-1)
         else:

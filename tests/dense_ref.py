@@ -40,11 +40,14 @@ def _fp8_cache(t, scale):
     return c.to(torch.float64) * scale
 
 
-def dense_prefill_logits(model, prompt_ids, prompt_hidden, next_token, K, mask_id, kv_fp8=None):
+def dense_prefill_logits(model, prompt_ids, prompt_hidden, next_token, K, mask_id, kv_fp8=None,
+                         combine="concat"):
     """Logits [K][V] of the K sampled rows (NTP, then MASK rows) for a prompt
     of n tokens at positions 0..n-1 with target hidden rows prompt_hidden.
     kv_fp8: {"k_scale": [N], "v_scale": [N]} to read K and V as an fp8
-    cache holds them."""
+    cache holds them. combine="sum": the drafter input is emb + fc(h) (the
+    paper's architecture wording) and layer 0 is a plain pre-norm layer;
+    "concat": layer 0 reads the two RMSNorm'd halves side by side."""
     m = model["dims"]
     n = len(prompt_ids)
     toks = list(prompt_ids[1:]) + [int(next_token)] + [mask_id] * (K - 1)
@@ -55,8 +58,10 @@ def dense_prefill_logits(model, prompt_ids, prompt_hidden, next_token, K, mask_i
     x = _w(hid) @ _w(model["fc"]).T
     e = _w(model["embed"])[torch.tensor(toks)]
     eps = m.rms_eps
+    if combine == "sum":
+        x = torch.add(x, e)
     for l, L in enumerate(model["layers"]):
-        if l == 0:
+        if l == 0 and combine == "concat":
             u = torch.cat([F.rms_norm(e, (m.d,), _w(model["norm_emb"]), eps),
                            F.rms_norm(x, (m.d,), _w(model["norm_hid"]), eps)], dim=-1)
         else:

@@ -209,3 +209,24 @@ def test_bad_token_and_page_flagged_in_forward():
     st = c.handle.status()
     assert st & 8 and st & 4
     c.close()
+
+
+@pytest.mark.parametrize("dims,C,K,ctx,L", [(GQA64, 5, 5, "lognormal", 0), (GQA128, 3, 7, "fixed", 1001)],
+                         ids=["gqa64", "gqa128"])
+def test_nonfinite_cache_tails_do_not_leak(dims, C, K, ctx, L):
+    """Slots past a request's last key inside its last page are not context:
+    filled with NaN / +-Inf bf16 codes they must not reach any output."""
+    import drafting_pd_expand_amd as pdx
+    from harness import bf16, poison_slots, tail_slots
+    w = synth.Workload(f"{dims.name}-nan-tail-c{C}k{K}", dims, C=C, K=K, context=ctx, L=L, seed=61 + C)
+    _say(f"[forward] {w.name}")
+    c = Case(w)
+    sl = tail_slots(c.b, c.mnp["h_shared"], K)
+    assert len(sl) > 0
+    poison_slots(c.pool, sl, [0x7FC0, 0x7F80, 0xFF80, 0xFFC1])
+    c.cache = pdx.pack_kv_cache(bf16(c.pool["k"], c.dev), bf16(c.pool["v"], c.dev))
+    c.run()
+    assert c.status() == 0
+    res = check_case(c)
+    _say(f"  {len(sl)} poisoned slots; worst logit err/RMS {res['worst_logit_ratio']:.4g}")
+    c.close()

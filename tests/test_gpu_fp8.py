@@ -193,3 +193,21 @@ def test_fp8_rejects_bad_scales():
             pdx.pd_draft_forward(c.handle, c.mdev, c.dims, c.out, c.inp["block_table"], c.cache, c.draft,
                                  c.logits, kv_scales=pairs)
     c.handle.free()
+
+
+def test_fp8_nan_codes_in_cache_tails_do_not_leak():
+    """E4M3 NaN codes (0x7F, 0xFF) in the slots past each request's last key
+    (inside its last page) must not reach any output."""
+    import drafting_pd_expand_amd as pdx
+    from harness import poison_slots, tail_slots
+    w = synth.Workload("gqa64-fp8-nan-tail", GQA64, C=5, K=5, context="lognormal", seed=71)
+    _say(f"[fp8] {w.name}")
+    c = Fp8Case(w)
+    sl = tail_slots(c.b, c.mnp["h_shared"], w.K)
+    assert len(sl) > 0
+    poison_slots(c.pool, sl, [0x7F, 0xFF])
+    c.cache = pdx.pack_kv_cache_fp8(_codes(c.pool["k"], c.dev), _codes(c.pool["v"], c.dev))
+    c.run()
+    assert c.status() == 0
+    check_fp8_case(c)
+    c.handle.free()

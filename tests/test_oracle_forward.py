@@ -125,6 +125,41 @@ def test_prefill_matches_dense_library_forward(dims, n, K):
     assert _rel(got["logits"], want) < 1e-10
 
 
+def _sum_model(model, seed):
+    """The same weights with a d-wide layer-0 QKV (fresh N(0, 0.02) draws):
+    the shape the combine="sum" reading needs."""
+    dims = model["dims"]
+    rng = np.random.default_rng(seed)
+    w = synth.f32_to_bf16_bits((0.02 * rng.standard_normal((dims.qkv_out, dims.d))).astype(np.float32))
+    out = dict(model)
+    out["layers"] = [dict(model["layers"][0], w_qkv=w)] + list(model["layers"][1:])
+    return out
+
+
+@pytest.mark.parametrize("dims,n,K", [(MINI, 21, 5), (MINI, 4, 1)])
+def test_prefill_combine_sum_matches_dense_library_forward(dims, n, K):
+    """The other reading of how emb and h meet (emb + fc(h), [Paper] sec. 2
+    architecture wording) against the dense library forward with the same
+    reading; it differs from the concatenation reading."""
+    model, ids, hidden, nxt = _prefill_case(dims, n, K, seed=12)
+    ms = _sum_model(model, 99)
+    n_ = len(ids)
+    bs, pages = 4, -(-(n_ + K) // 4)
+    rng = np.random.default_rng(3)
+    nb = pages + 3
+    bt = rng.permutation(nb)[:pages][None]
+    pool = {"k": rng.standard_normal((dims.N, nb * bs, dims.Hkv, dims.dh)),
+            "v": rng.standard_normal((dims.N, nb * bs, dims.Hkv, dims.dh))}
+    exp = oracle.expand([n_], [0], ids, np.arange(n_), hidden, [nxt], bt, model["h_shared"], K, dims.V - 1, bs)
+    got = oracle.draft_forward(ms, exp, bt, pool, K, block_size=bs, combine="sum")
+    want = dense_prefill_logits(ms, ids, hidden, nxt, K, dims.V - 1, combine="sum")
+    assert _rel(got["logits"], want) < 1e-10
+    other = dense_prefill_logits(model, ids, hidden, nxt, K, dims.V - 1, combine="concat")
+    assert _rel(got["logits"], other) > 1e-3
+    with pytest.raises(ValueError):
+        oracle.draft_forward(ms, exp, bt, pool, K, block_size=bs, combine="add")
+
+
 @pytest.mark.parametrize("L,n,v,K", [(13, 6, 4, 5), (9, 4, 1, 3), (16, 8, 8, 7), (30, 2, 2, 1)])
 def test_decode_over_written_cache_matches_dense_prefill(L, n, v, K):
     """Prefix prefill of L tokens writes K/V into scattered pages; a decode step
