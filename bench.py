@@ -83,6 +83,14 @@ def gemm_flops(dm, b, K: int) -> int:
     return 2 * T_eff * per_row + 2 * b["C"] * K * dm.V * dm.d
 
 
+def forward_bytes(dm, b, K: int) -> int:
+    """Algorithmic bytes of the drafter pass alone (pd_draft_forward): the
+    step's bytes without the expansion's own traffic (the verify rows it reads
+    and writes out; the pass reads the expanded rows once)."""
+    T_in = b["T_in"]
+    return step_bytes(dm, b, K) - (T_in + 1) * dm.hidden3 * 2
+
+
 def step_bytes(dm, b, K: int) -> int:
     """Algorithmic bytes of one whole step (weights once, visible KV once per
     layer and kv head, KV writes, hidden rows in and out, ids)."""
@@ -523,16 +531,21 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
         raise SystemExit(f"{workload}: device status {st} after warmup")
     eager_ids = draft.clone()
 
-    # which kernel dominates: the LM head (one launch) or the attention kernel
-    # (one per layer), from one step with events around those two classes
-    h.profile((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_ATTN))
+    # which kernel dominates: the persistent decode kernel (the whole pass in
+    # one launch, at few rows), else the LM head (one launch) or the attention
+    # kernel (one per layer), from one step with events around those classes
+    h.profile((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_ATTN) | (1 << pdx.KERNEL_DECODE))
     step(stream)
     torch.cuda.synchronize()
     lm_ms, lm_n = h.profile_read(pdx.KERNEL_LMHEAD)
     at_ms, at_n = h.profile_read(pdx.KERNEL_ATTN)
+    de_ms, de_n = h.profile_read(pdx.KERNEL_DECODE)
     h.profile(0)
-    dom = "lm_head" if lm_ms / max(lm_n, 1) >= at_ms / max(at_n, 1) else "attention"
-    dom_cls = pdx.KERNEL_LMHEAD if dom == "lm_head" else pdx.KERNEL_ATTN
+    if de_n > 0:
+        dom = "decode"
+    else:
+        dom = "lm_head" if lm_ms / max(lm_n, 1) >= at_ms / max(at_n, 1) else "attention"
+    dom_cls = {"decode": pdx.KERNEL_DECODE, "lm_head": pdx.KERNEL_LMHEAD, "attention": pdx.KERNEL_ATTN}[dom]
 
     def timed_region(class_mask):
         h.profile(class_mask)
@@ -556,7 +569,8 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
     steps_s = 1000.0 / ms_step
     k_avg_s = k_ms / max(k_n, 1) / 1000.0
 
-    # second timed region: events around every GEMM launch (and nothing else)
+    # second timed region: events around every GEMM launch (and nothing else);
+    # the decode kernel runs its GEMMs inside one launch, so there are none
     ms_g, _ = timed_region((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_GEMM))
     g_ms, g_n = h.profile_read(pdx.KERNEL_GEMM)
     l_ms, l_n = h.profile_read(pdx.KERNEL_LMHEAD)
@@ -567,7 +581,11 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
     gf = gemm_flops(dm, b, w.K)
     lm_flops = 2.0 * R * dm.V * dm.d
 
-    if dom == "lm_head":
+    if dom == "decode":
+        fb = forward_bytes(dm, b, w.K)
+        roof = {"bound": "hbm", "kernel": "decode_kernel (persistent: the whole drafter pass in one launch)",
+                "achieved": fb / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": fb}
+    elif dom == "lm_head":
         if R <= 64:   # weight-streaming ring kernel: HBM-bound
             roof = {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
                     "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
@@ -588,7 +606,7 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
     log(f"[bench] {workload}: {ms_step * 1000:.1f} us/step ({steps_s:.1f} steps/s, {steps_s * R:.0f} drafted tok/s); "
         f"dominant {dom} {k_avg_s * 1e6:.1f} us = {roof['achieved']:.0f} {roof['unit']} ({roof['frac']:.2f}); "
         f"step {sb / 1e9:.3f} GB = {sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS:.2f} of HBM; GEMMs {gemm_us:.0f} us "
-        f"(in a {ms_g * 1000:.0f} us step) = {gf / (gemm_us * 1e-6) / 1e12:.0f} TFLOP/s on {T_eff} rows")
+        f"(in a {ms_g * 1000:.0f} us step) = {gf / max(gemm_us * 1e-6, 1e-12) / 1e12:.0f} TFLOP/s on {T_eff} rows")
     leg = {
         "workload": f"{workload}: {DESCR[workload]}",
         "C": w.C, "K": w.K, "T_in": b["T_in"], "T_out": b["T_in"] + w.C * (w.K - 1), "T_eff": T_eff,
@@ -600,13 +618,13 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
         "step_algorithmic_bytes": sb,
         "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
         "roofline": roof,
-        "gemm_roofline": {
+        "gemm_roofline": None if (g_n + l_n) == 0 else {
             "bound": "mfma", "kernels": "every projection GEMM + the LM head",
             "flops_per_step": gf, "rows_credited": T_eff,
             "us_per_step": gemm_us, "projections_us": proj_us, "lm_head_us": lm_us,
             "launches_per_step": (g_n + l_n) // steps,
-            "achieved": gf / (gemm_us * 1e-6) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": gf / (gemm_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS,
+            "achieved": gf / max(gemm_us * 1e-6, 1e-12) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": gf / max(gemm_us * 1e-6, 1e-12) / 1e12 / BF16_PEAK_TFLOPS,
             "step_us_in_this_region": ms_g * 1000.0,
         },
     }
@@ -730,7 +748,7 @@ def main():
         "ms_per_step_p10_p50_p90": head["ms_per_step_p10_p50_p90"],
         "step_hbm_frac": head["step_hbm_frac"],
         "step_algorithmic_bytes": head["step_algorithmic_bytes"],
-        "gemm_mfma_frac": head["gemm_roofline"]["frac"],
+        "gemm_mfma_frac": head["gemm_roofline"]["frac"] if head["gemm_roofline"] else None,
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
         "configs": configs,

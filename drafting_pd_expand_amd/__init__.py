@@ -22,7 +22,7 @@ import torch
 __all__ = [
     "PD_OK", "PD_EINVAL", "PD_ENOMEM", "PD_EHIP", "PD_ESCRATCH", "PD_PAGE", "PD_MAX_LAYERS",
     "NOALLOC_SCRATCH_BYTES", "pd_draft_forward_noalloc",
-    "KERNEL_LMHEAD", "KERNEL_GEMM", "KERNEL_ATTN", "KERNEL_OTHER",
+    "KERNEL_LMHEAD", "KERNEL_GEMM", "KERNEL_ATTN", "KERNEL_OTHER", "KERNEL_DECODE",
     "PdError", "library_path", "load", "pd_expand_batch", "pd_draft_forward", "pd_ar_advance", "pd_free",
     "Handle", "batch_dims", "alloc_batch", "device_model", "pack_kv_cache",
     "unpack_kv_cache", "kv_cache_elems",
@@ -32,7 +32,7 @@ PD_OK, PD_EINVAL, PD_ENOMEM, PD_EHIP, PD_ESCRATCH = 0, -1, -2, -3, -4
 NOALLOC_SCRATCH_BYTES = 64 << 20
 PD_PAGE = 16
 PD_MAX_LAYERS = 16
-KERNEL_LMHEAD, KERNEL_GEMM, KERNEL_ATTN, KERNEL_OTHER = 0, 1, 2, 3
+KERNEL_LMHEAD, KERNEL_GEMM, KERNEL_ATTN, KERNEL_OTHER, KERNEL_DECODE = 0, 1, 2, 3, 4
 STATUS_BAD_CHAIN, STATUS_BAD_BOUNDS = 32, 64
 PART_MAX_K, PART_MAX_S, PART_MAX_POS = 16, 256, 1 << 19
 
@@ -129,6 +129,8 @@ def load():
     lib.pd_status.restype = c_int
     lib.pd_set_debug_resid.argtypes = [c_void_p, c_void_p]
     lib.pd_set_debug_resid.restype = c_int
+    lib.pd_set_decode_timeline.argtypes = [c_void_p, c_void_p]
+    lib.pd_set_decode_timeline.restype = c_int
     lib.pd_profile.argtypes = [c_void_p, c_int]
     lib.pd_profile.restype = c_int
     lib.pd_profile_read.argtypes = [c_void_p, c_int, POINTER(c_double), POINTER(c_int64)]
@@ -268,6 +270,12 @@ class Handle:
     def set_debug_resid(self, t):
         _check(load().pd_set_debug_resid(self.ptr, c_void_p(t.data_ptr() if t is not None else None)),
                "pd_set_debug_resid")
+
+    def set_decode_timeline(self, t):
+        """Phase timestamps of the persistent decode kernel into t (int64
+        [(4 + 9 N) * CUs], device) on later calls; None stops."""
+        _check(load().pd_set_decode_timeline(self.ptr, c_void_p(t.data_ptr() if t is not None else None)),
+               "pd_set_decode_timeline")
 
     def profile(self, class_mask: int):
         """Record events around launches of the kernel classes in class_mask

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpdexpand.so")
-SOURCES = ["expand.hip", "gemm.hip", "rows.hip", "attn.hip", "partition.hip", "api.hip"]
+SOURCES = ["expand.hip", "gemm.hip", "rows.hip", "attn.hip", "decode.hip", "partition.hip", "api.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -29,7 +29,8 @@ FLAGS = [
 # per-source extra flags: the attention kernels keep MFMA operands and
 # accumulators in arch VGPRs (no AGPR <-> VGPR copies around the softmax), and
 # take max/min without NaN canonicalisation (no NaN reaches the softmax)
-FILE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+FILE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+              "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -25,6 +26,7 @@ struct pd_handle {
     size_t scratch_bytes = 0;
     int32_t* status = nullptr;
     float* dbg = nullptr;
+    uint64_t* timeline = nullptr;   // decode kernel phase timestamps, or null
     int prof = 0;  // bit mask of recorded kernel classes
     std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[PD_KERNEL_CLASSES];
     std::vector<hipEvent_t> spare;
@@ -107,16 +109,26 @@ struct Timed {
 };
 
 struct Layout {
-    size_t x, u, q, ao, act, ws, po, pml, plan, xg, amv, ami, total;
-    int T, R, ntilesV;
+    size_t sync, x, u, q, ao, act, ws, po, pml, plan, xg, amv, ami, total;
+    int T, R, ntilesV;   // ntilesV: argmax partials per row of the LM-head GEMM kernel
+    int amax_cap;        // partials per row the scratch holds (also the decode pass's)
     AttnSplit sp;
+    DecodePlan dp;   // the persistent decode pass, when it applies (dp.ok)
 };
+
+// The persistent decode kernel serves passes of up to 64 rows when the
+// environment sets PD_DECODE=1; otherwise every pass runs as separate
+// kernels (measured faster so far).
+bool decode_enabled() {
+    const char* e = std::getenv("PD_DECODE");
+    return e && e[0] == '1';
+}
 
 // limit != 0: the attention partial planes (sized by the splits per request,
 // scap) shrink until the whole layout fits in `limit` bytes; fewer splits per
 // request only make the device plan pick longer splits. L.total > limit when
 // even the fewest splits the block table needs do not fit.
-Layout plan_layout(const pd_model* m, const pd_batch_dims* d, size_t limit = 0) {
+Layout plan_layout(const pd_model* m, const pd_batch_dims* d, bool fp8, size_t limit = 0) {
     Layout L;
     const int T = d->T_in + d->C * (d->K - 1);
     const int R = d->C * d->K;
@@ -136,21 +148,35 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d, size_t limit = 0) 
     need(T, m->d, hd);
     need(T, m->d, m->F);
     L.ntilesV = plan_gemm(R, m->V, m->d, EPI_ARGMAX).ntiles;
+    L.amax_cap = L.ntilesV;
+    L.dp = plan_decode(*m, T, R, fp8);
+    if (!decode_enabled()) L.dp.ok = false;
+    int u_slots = 1, l_slots = 1;   // activation slots (the decode pass writes each once)
+    if (L.dp.ok) {
+        ws = std::max(ws, L.dp.ws_floats);
+        L.amax_cap = std::max(L.amax_cap, L.dp.lm_ntiles);
+        L.sp = plan_attn_split_grid(d->C, T, m->Hq, m->Hkv, m->dh, d->max_blocks, L.dp.grid);
+        u_slots = 2 * m->N;
+        l_slots = m->N;
+    }
     auto carve_all = [&]() {
         size_t off = 0;
         auto carve = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+        // barrier words of the decode kernel: always first, so that no other
+        // use of the scratch ever writes them (they must start at zero)
+        L.sync = carve(kDecodeSyncWords * 4);
         L.x = carve((size_t)T * m->d * 4);
-        L.u = carve((size_t)T * 2 * m->d * 2);
+        L.u = carve((size_t)u_slots * T * 2 * m->d * 2);
         L.q = carve((size_t)T * hd * 2);
-        L.ao = carve((size_t)T * hd * 2);
-        L.act = carve((size_t)T * m->F * 2);
+        L.ao = carve((size_t)l_slots * T * hd * 2);
+        L.act = carve((size_t)l_slots * T * m->F * 2);
         L.ws = carve(ws * 4);
         L.po = carve((size_t)L.sp.scap * T * hd * 4);
         L.pml = carve((size_t)L.sp.scap * T * m->Hq * 2 * 4);
         L.plan = carve(attn_plan_ints(L.sp) * 4);
         L.xg = carve((size_t)R * m->d * 2);
-        L.amv = carve((size_t)R * L.ntilesV * 4);
-        L.ami = carve((size_t)R * L.ntilesV * 4);
+        L.amv = carve((size_t)R * L.amax_cap * 4);
+        L.ami = carve((size_t)R * L.amax_cap * 4);
         L.total = off;
     };
     carve_all();
@@ -181,6 +207,8 @@ int ensure_scratch(pd_handle* h, size_t bytes, hipStream_t s) {
         return PD_ENOMEM;
     }
     h->scratch_bytes = want;
+    // the decode kernel's barrier words start at zero (scratch offset 0)
+    if (hipMemsetAsync(h->scratch, 0, kDecodeSyncWords * 4, s) != hipSuccess) return PD_EHIP;
     return PD_OK;
 }
 
@@ -311,6 +339,53 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
     aa.part_o = (float*)(S + L.po); aa.part_ml = (float*)(S + L.pml);
     aa.out = ao; aa.status = st;
 
+    if (L.dp.ok) {
+        // the whole pass as one persistent launch (few rows: a chain of weight streams)
+        DecodeArgs da;
+        std::memset(&da, 0, sizeof(da));
+        da.embed = m->embed; da.fc = m->fc; da.norm_emb = m->norm_emb; da.norm_hid = m->norm_hid;
+        da.norm_final = m->norm_final; da.lm_head = m->lm_head;
+        for (int l = 0; l < m->N; ++l) {
+            da.norm_in[l] = m->norm_in[l]; da.w_qkv[l] = m->w_qkv[l]; da.w_o[l] = m->w_o[l];
+            da.norm_post[l] = m->norm_post[l]; da.w_gate[l] = m->w_gate[l]; da.w_up[l] = m->w_up[l];
+            da.w_down[l] = m->w_down[l];
+        }
+        da.d = d; da.Hq = m->Hq; da.Hkv = m->Hkv; da.dh = m->dh; da.F = m->F; da.NL = m->N; da.V = m->V;
+        da.hidden3 = m->hidden3; da.eps = m->rms_eps;
+        da.inv_step = std::pow((double)m->rope_theta, -2.0 / m->dh);
+        da.ids = b->input_ids; da.positions = b->positions; da.slots = b->slot_mapping;
+        da.new_idx = b->new_token_indices; da.hidden = b->hidden; da.hidden_d = hidden_d;
+        da.hidden_out = hidden_out; da.T = T; da.R = R;
+        da.kv = reinterpret_cast<char*>(kv_cache); da.plane_bytes = plane; da.num_blocks = dims->num_blocks;
+        da.draft_ids = draft_ids; da.logits = logits;
+        da.x = x; da.u = u; da.q = q; da.ao = ao; da.act = act; da.xg = xg; da.ws = ws;
+        da.u_slot = (size_t)T * 2 * d;
+        da.ao_slot = (size_t)T * hd;
+        da.act_slot = (size_t)T * m->F;
+        da.rows0 = L.dp.rows0;
+        da.lm_in_kernel = L.dp.lm_in_kernel;
+        da.amax_v = (float*)(S + L.amv); da.amax_i = (int*)(S + L.ami);
+        da.dbg = h ? h->dbg : nullptr;
+        da.timeline = h ? h->timeline : nullptr;
+        da.sync = reinterpret_cast<unsigned*>(S + L.sync);
+        da.status = st;
+        da.sp_fc = L.dp.sp_fc; da.sp_qkv0 = L.dp.sp_qkv0; da.sp_qkv = L.dp.sp_qkv; da.sp_o = L.dp.sp_o;
+        da.sp_down = L.dp.sp_down;
+        da.g_fc = L.dp.g_fc; da.g_qkv0 = L.dp.g_qkv0; da.g_qkv = L.dp.g_qkv; da.g_o = L.dp.g_o;
+        da.g_gu = L.dp.g_gu; da.g_down = L.dp.g_down; da.g_lm = L.dp.g_lm;
+        da.at = aa;
+        {
+            Timed t(h, PD_KERNEL_DECODE, s);
+            PD_TRY(launch_decode(L.dp, da, s));
+        }
+        if (L.dp.lm_in_kernel) return PD_OK;
+        // LM head on the packed sampled rows the pass left in xg, greedy argmax
+        PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, xg, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
+                    nullptr, 0, nullptr));
+        Timed t(h, PD_KERNEL_OTHER, s);
+        return launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV, draft_ids, st, s);
+    }
+
     // fc projection 3d -> d (starts the residual stream; skipped when the
     // projected rows are given), then the layer-0 input
     if (!hidden_d)
@@ -438,7 +513,7 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
         if ((rc = create_handle(hp)) != PD_OK) return rc;
     }
     pd_handle* h = *hp;
-    const Layout L = plan_layout(m, dims);
+    const Layout L = plan_layout(m, dims, opts && opts->kv_fp8);
     if ((rc = ensure_scratch(h, L.total, s)) != PD_OK) return rc;
     return forward_impl(h, h->scratch, L, h->status, m, dims, b, block_table, kv_cache, draft_ids, logits,
                         opts, s);
@@ -449,7 +524,7 @@ int pd_draft_forward_noalloc(const pd_model* m, const pd_batch_dims* dims, const
                              float* logits, const pd_forward_opts* opts, void* stream) {
     int rc = forward_args_ok(m, dims, b, block_table, kv_cache, draft_ids, opts);
     if (rc != PD_OK || dims->C == 0) return rc;
-    const Layout L = plan_layout(m, dims, kStaticScratchBytes);
+    const Layout L = plan_layout(m, dims, opts && opts->kv_fp8, kStaticScratchBytes);
     if (L.total > kStaticScratchBytes) return PD_ESCRATCH;
     char* S = nullptr;
     if ((rc = static_scratch(&S)) != PD_OK) return rc;
@@ -526,6 +601,12 @@ int pd_status(pd_handle* h, int32_t* out, void* stream) {
 int pd_set_debug_resid(pd_handle* h, float* dst) {
     if (!h) return PD_EINVAL;
     h->dbg = dst;
+    return PD_OK;
+}
+
+int pd_set_decode_timeline(pd_handle* h, uint64_t* dst) {
+    if (!h) return PD_EINVAL;
+    h->timeline = dst;
     return PD_OK;
 }
 

@@ -27,12 +27,15 @@ constexpr int kAttnPlanThreads = 256;
 // Reads cu_out / seq_lens of every request (requests 4t .. 4t+3 on thread
 // t), validates them, picks the split length and writes the per-request
 // split counts and the unit records {r, s, ns, row0, row1, kb, ke, 0}.
-__device__ inline void attn_plan_block(const AttnArgs& a) {
+// CG: other workgroups of the same launch read the plan (coherent stores).
+// MAXC: requests the caller guarantees at most (sizes the LDS tables).
+template <bool CG = false, int MAXC = PD_MAX_C>
+__device__ __forceinline__ void attn_plan_block(const AttnArgs& a) {
     __shared__ long long s_sum[4];
     __shared__ int s_max[4];
     __shared__ int s_cnt[4];
-    __shared__ int s_incl[PD_MAX_C];   // inclusive prefix of the split counts
-    __shared__ int4 s_req[PD_MAX_C];   // validated {row0, row1, seq} of every request
+    __shared__ int s_incl[MAXC];   // inclusive prefix of the split counts
+    __shared__ int4 s_req[MAXC];   // validated {row0, row1, seq} of every request
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     int seq[4];
     long long sv = 0;
@@ -41,7 +44,7 @@ __device__ inline void attn_plan_block(const AttnArgs& a) {
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * tid + i;
         seq[i] = 0;
-        if (r < a.C) {
+        if (r < a.C && r < MAXC) {
             const int row0 = a.cu_out[r], row1 = a.cu_out[r + 1];
             int sq = a.seq_lens[r];
             const bool ok = row0 >= 0 && row1 <= a.T && row1 >= row0 && sq >= 1 &&
@@ -79,7 +82,7 @@ __device__ inline void attn_plan_block(const AttnArgs& a) {
     // than the longer splits: C = 4 with 17.7k keys, 22 us at 304 keys / 472
     // workgroups vs 27 us at 128 keys / 1120 and at 256 keys / 568 (26 us
     // at 512 keys / 288); with 13k keys, 19 us at 224 keys vs 22 at 128.
-    const long long free_slots = kAttnRoundSlots - (long long)a.Hkv * a.C;
+    const long long free_slots = (long long)a.sp.round_slots - (long long)a.Hkv * a.C;
     if (free_slots > 0) {
         const long long one = (total * a.Hkv + free_slots - 1) / free_slots;
         if (one <= kAttnOneRoundMaxKeys) sl = max(sl, one);
@@ -118,15 +121,15 @@ __device__ inline void attn_plan_block(const AttnArgs& a) {
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * tid + i;
         run += ns[i];
-        if (r < a.C) {
-            a.plan[kPlanNs + r] = ns[i];
+        if (r < a.C && r < MAXC) {
+            stc<CG>(a.plan + kPlanNs + r, ns[i]);
             s_incl[r] = run;
         }
     }
     if (tid == 0) {
         if (units > a.sp.max_units) flag(a.status, PD_STATUS_BAD_ROW);   // excluded by the host's bound
-        a.plan[0] = min(units, a.sp.max_units);
-        a.plan[1] = split_len;
+        stc<CG>(a.plan, min(units, a.sp.max_units));
+        stc<CG>(a.plan + 1, split_len);
     }
     __syncthreads();
     // unit records, spread over the block: unit u belongs to the first
@@ -145,8 +148,8 @@ __device__ inline void attn_plan_block(const AttnArgs& a) {
         const int kb = sq * split_len;
         const int ke = min(rq.z, kb + split_len);
         int4* rec = reinterpret_cast<int4*>(a.plan + kPlanUnits + (size_t)u * kPlanRec);
-        rec[0] = make_int4(q, sq, nsq, rq.x);
-        rec[1] = make_int4(rq.y, kb, ke, 0);
+        stc<CG>(rec, make_int4(q, sq, nsq, rq.x));
+        stc<CG>(rec + 1, make_int4(rq.y, kb, ke, 0));
     }
 }
 

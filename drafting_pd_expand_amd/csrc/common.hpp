@@ -72,4 +72,58 @@ __device__ __forceinline__ void flag(int32_t* status, int bits) {
     if (status) atomicOr(status, bits);
 }
 
+// Loads and stores of data that another workgroup of the same launch wrote
+// or will read (the persistent decode kernel hands activations from phase to
+// phase inside one launch). Each XCD has its own L2, which keeps no coherence
+// with the others: with CG these accesses carry the device-scope cache bit
+// (sc1), so a store is written through to memory and a load is served from
+// memory, not from a stale line of the reader's L2. They are relaxed atomic
+// accesses of 4 or 8 bytes (16-byte values go as two 8-byte halves); without
+// CG they are plain accesses.
+template <bool CG, typename T>
+__device__ __forceinline__ T ldc(const T* p) {
+    if constexpr (!CG) {
+        return *p;
+    } else if constexpr (sizeof(T) == 4) {
+        const uint32_t v = __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_bit_cast(T, v);
+    } else if constexpr (sizeof(T) == 8) {
+        const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_bit_cast(T, v);
+    } else {
+        static_assert(sizeof(T) == 16, "4, 8 or 16 bytes");
+        const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+        typedef __attribute__((ext_vector_type(2))) uint64_t u64x2;
+        u64x2 v;
+        v[0] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return __builtin_bit_cast(T, v);
+    }
+}
+
+template <bool CG, typename T>
+__device__ __forceinline__ void stc(T* p, const T& v) {
+    if constexpr (!CG) {
+        *p = v;
+    } else if constexpr (sizeof(T) == 2) {
+        __hip_atomic_store(reinterpret_cast<uint16_t*>(p), __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (sizeof(T) == 4) {
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (sizeof(T) == 8) {
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        static_assert(sizeof(T) == 16, "2, 4, 8 or 16 bytes");
+        typedef __attribute__((ext_vector_type(2))) uint64_t u64x2;
+        const u64x2 w = __builtin_bit_cast(u64x2, v);
+        uint64_t* q = reinterpret_cast<uint64_t*>(p);
+        __hip_atomic_store(q, (uint64_t)w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(q + 1, (uint64_t)w[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 }  // namespace pd

@@ -104,8 +104,12 @@ struct AttnSplit {
     int target_wg;   // workgroups the split length aims at
     int scap;        // splits per request at most (partial planes allocated)
     int max_units;   // capacity of the unit list = grid x of the split kernel
+    int round_slots; // split workgroups resident at once (the one-round rule)
 };
 AttnSplit plan_attn_split(int C, int T, int Hq, int Hkv, int dh, int max_blocks);
+// The same plan for a fixed grid of `grid` workgroups, one item each at most
+// when the keys allow (the persistent decode kernel).
+AttnSplit plan_attn_split_grid(int C, int T, int Hq, int Hkv, int dh, int max_blocks, int grid);
 // the fewest splits per request (scap) that cover max_blocks pages of keys
 int attn_min_splits(int max_blocks);
 // int32 words of the plan: [units, split_len, -, -, ns[PD_MAX_C],
@@ -144,5 +148,73 @@ int launch_attn_plan(const AttnArgs& a, hipStream_t s);
 int launch_attention(int dh, const AttnArgs& a, hipStream_t s, hipEvent_t split_begin,
                      hipEvent_t split_end, hipEvent_t merge_begin = nullptr,
                      hipEvent_t merge_end = nullptr);
+
+// Everything one decode launch needs (by value, in the kernel arguments).
+struct DecodeArgs {
+    // model (bf16 [out][in])
+    const uint16_t *embed, *fc, *norm_emb, *norm_hid, *norm_final, *lm_head;
+    const uint16_t* norm_in[PD_MAX_LAYERS];
+    const uint16_t* w_qkv[PD_MAX_LAYERS];
+    const uint16_t* w_o[PD_MAX_LAYERS];
+    const uint16_t* norm_post[PD_MAX_LAYERS];
+    const uint16_t* w_gate[PD_MAX_LAYERS];
+    const uint16_t* w_up[PD_MAX_LAYERS];
+    const uint16_t* w_down[PD_MAX_LAYERS];
+    int d, Hq, Hkv, dh, F, NL, V, hidden3;
+    float eps;
+    double inv_step;                  // theta^(-2/dh)
+    // the expanded batch (written by pd_expand_batch, an earlier launch)
+    const int32_t *ids, *positions, *slots, *new_idx;
+    const uint16_t* hidden;           // [T][hidden3] or null with hidden_d
+    const uint16_t* hidden_d;         // [T][d] projected rows given directly, or null
+    uint16_t* hidden_out;             // [R][d] final residual of the sampled rows, or null
+    int T, R;
+    char* kv;                         // bf16 cache base
+    size_t plane_bytes;               // bytes of one K or V plane
+    int num_blocks;
+    int32_t* draft_ids;
+    float* logits;                    // [R][V] or null
+    // scratch. Activations that a projection reads as its X operand are
+    // written once per launch, each into a slot of its own (plain loads may
+    // then be served from L2: no XCD holds a stale copy of a slot):
+    // u slot 0 = layer-0 input [T][2d], slot 2l + 1 = layer l's post-attention
+    // norm, slot 2l + 2 = layer l + 1's input norm; ao and act one slot per layer
+    float* x;                         // fp32 residual [T][d]
+    uint16_t *u, *q, *ao, *act, *xg;
+    size_t u_slot, ao_slot, act_slot; // elements per slot
+    int rows0;                        // workgroups rows0 .. rows0 + T - 1 do the row phases
+    int lm_in_kernel;                 // the LM head and argmax run as the last phases
+    float* ws;                        // split-K planes
+    float* amax_v;
+    int* amax_i;
+    float* dbg;                       // [N+1][T][d] residual snapshots, or null
+    unsigned* sync;                   // barrier words: [0] release, [64 + i] arrival of workgroup i
+    int32_t* status;
+    uint64_t* timeline;               // or null: [phase][workgroup] end of the phase's work, then
+                                      // [phase] barrier release, then the start (100 MHz clock)
+    // projections: K splits and workgroups taking part
+    int sp_fc, sp_qkv0, sp_qkv, sp_o, sp_down;
+    int g_fc, g_qkv0, g_qkv, g_o, g_gu, g_down, g_lm;
+    AttnArgs at;                      // plan, partials, split sizes; q / planes set per layer
+};
+
+// Plan of the persistent decode kernel: K splits and workgroups taking part
+// in each projection (grid = the device's CUs, one workgroup each).
+struct DecodePlan {
+    bool ok;         // the pass fits the kernel (rows, head size, cache type, device)
+    int mt;          // 16-row activation tiles (1, 2 or 4)
+    int grid;        // workgroups of the launch
+    int rows0;       // first row workgroup (= grid - T); projections use workgroups below it
+    int lm_in_kernel;
+    int sp_fc, sp_qkv0, sp_qkv, sp_o, sp_down;
+    int g_fc, g_qkv0, g_qkv, g_o, g_gu, g_down, g_lm;
+    size_t ws_floats;   // split-K planes the pass needs
+    int lm_ntiles;      // argmax partials per sampled row
+};
+// T expanded rows, R sampled rows; fp8: the cache holds E4M3 codes.
+DecodePlan plan_decode(const pd_model& m, int T, int R, bool fp8);
+// Sync words the decode kernel keeps in scratch (zero before the first launch).
+constexpr size_t kDecodeSyncWords = 64 + 256;
+int launch_decode(const DecodePlan& p, const DecodeArgs& a, hipStream_t s);
 
 }  // namespace pd

@@ -56,6 +56,7 @@ extern "C" {
 #define PD_STATUS_BAD_ROW     16  /* row bookkeeping (cu_out / new-token index) inconsistent */
 #define PD_STATUS_BAD_CHAIN   32  /* pd_seq_partition: a kept position whose dependency is not placeable */
 #define PD_STATUS_BAD_BOUNDS  64  /* pd_seq_partition: segment boundaries not 0 = b_0 <= ... <= b_S = n */
+#define PD_STATUS_SYNC_TIMEOUT 128 /* pd_draft_forward: a grid-wide wait of the persistent decode pass gave up */
 
 /* Sizes of one draft step. [host]
  *   C             requests, 0..PD_MAX_C (0 = nothing to do)
@@ -298,12 +299,23 @@ int pd_status(pd_handle* h, int32_t* out, void* stream);
  * each layer). Pass NULL to stop. */
 int pd_set_debug_resid(pd_handle* h, float* dst);
 
+/* Optional phase timestamps of the persistent decode kernel (the pass of up
+ * to 64 rows in one launch): when dst [dev] is non-NULL, later
+ * pd_draft_forward calls that take that kernel write uint64 readings of the
+ * device's constant 100 MHz clock: [p][w] = when workgroup w finished the work
+ * of phase p (p < P - 1, P = 4 + 9 N phases, w < the device's CU count G),
+ * then [P - 1][p] = when phase p's grid barrier released, and
+ * [P - 1][P - 1] = the start of the launch. dst holds P * G words. Pass NULL
+ * to stop. For profiling only. */
+int pd_set_decode_timeline(pd_handle* h, uint64_t* dst);
+
 /* Per-kernel timing with HIP events on the launch stream. Kernel classes: */
 #define PD_KERNEL_LMHEAD  0   /* LM-head GEMM with the fused argmax partials     */
 #define PD_KERNEL_GEMM    1   /* every other GEMM (fc, QKV, O, gate/up, down)    */
 #define PD_KERNEL_ATTN    2   /* split-KV paged attention (not the merge)         */
 #define PD_KERNEL_OTHER   3   /* norms, RoPE+cache, split plan, merge, argmax reduce */
-#define PD_KERNEL_CLASSES 4
+#define PD_KERNEL_DECODE  4   /* the persistent decode kernel: a whole pass of up to 64 rows */
+#define PD_KERNEL_CLASSES 5
 /* class_mask != 0 starts recording an event pair around every launch of the
  * kernel classes whose bit (1 << PD_KERNEL_*) is set, for later
  * pd_draft_forward calls with this handle; 0 stops. Either way the records
