@@ -58,7 +58,7 @@ class BatchDims(ctypes.Structure):
 class ExpandIn(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in
                 ("num_tokens", "num_rejected", "target_ids", "target_pos", "target_hidden",
-                 "next_token_ids", "block_table", "h_shared")]
+                 "next_token_ids", "block_table", "h_shared", "live_counts")]
 
 
 _BATCH_FIELDS = ("input_ids", "positions", "slot_mapping", "is_rejected", "is_masked",
@@ -223,7 +223,9 @@ def _batch_struct(b: dict, dims: dict, device=None, hidden_optional: bool = Fals
 
 
 def pd_expand_batch(dims: dict, inp: dict, out: dict, stream=None) -> None:
-    """Enqueue the batch expansion (include/pd.h: pd_expand_batch)."""
+    """Enqueue the batch expansion (include/pd.h: pd_expand_batch). inp may
+    hold "live_counts" (int32 [2] device: live C and T_in of a bucketed
+    batch whose capacity dims gives)."""
     lib = load()
     C, T_in = dims["C"], dims["T_in"]
     dev = inp["num_tokens"].device if C else None
@@ -236,6 +238,8 @@ def pd_expand_batch(dims: dict, inp: dict, out: dict, stream=None) -> None:
         _dev(inp["next_token_ids"], "next_token_ids", (torch.int32,), C, dev),
         _dev(inp["block_table"], "block_table", (torch.int32,), C * dims["max_blocks"], dev),
         _dev(inp["h_shared"], "h_shared", _BF16, dims["hidden3"], dev),
+        _dev(inp["live_counts"], "live_counts", (torch.int32,), 2, dev) if inp.get("live_counts") is not None
+        else None,
     ) if C else ExpandIn()
     bs = _batch_struct(out, dims, dev) if C else Batch()
     d = _dims_struct(dims)

@@ -49,9 +49,20 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
     __shared__ int s_wsum[4];
     __shared__ int s_bad;
 
-    const int C = a.d.C, K = a.d.K, tid = threadIdx.x;
-    const int T_in = a.d.T_in;
+    // capacity (the bucket the launch is sized for) and live sizes: with
+    // live counts, requests C .. Cb-1 and rows T_out .. T_outb-1 are padding
+    const int Cb = a.d.C, K = a.d.K, tid = threadIdx.x;
+    int C = Cb, T_in = a.d.T_in;
     int32_t* status = a.out.status;
+    if (a.in.live_counts) {
+        C = a.in.live_counts[0];
+        T_in = a.in.live_counts[1];
+        if (C < 0 || C > Cb || T_in < C || T_in > a.d.T_in) {
+            if (blockIdx.x == 0 && tid == 0) flag(status, PD_STATUS_BAD_COUNTS);
+            return;
+        }
+    }
+    const int T_out = T_in + C * (K - 1);   // live rows
     if (tid == 0) s_bad = 0;
     __syncthreads();
 
@@ -109,20 +120,43 @@ __global__ __launch_bounds__(256) void expand_kernel(ExpandArgs a) {
     const int H3 = a.d.hidden3;
     const int bs = a.d.block_size, maxb = a.d.max_blocks, nb = a.d.num_blocks;
 
-    // per-request outputs: block 0 writes them
+    // per-request outputs: block 0 writes them. Padding requests own no rows
+    // (cu_out = the live T_out, one visible key so that nothing reads as bad),
+    // sample the last expanded row, and the padding input rows map nowhere.
     if (blockIdx.x == 0) {
-        for (int r = tid; r < C; r += 256) {
-            const int in0 = s_in[r];
-            const int p_ntp = a.in.target_pos[in0 + s_v[r] - 1];
-            a.out.cu_out[r] = in0 + r * (K - 1);
-            a.out.seq_lens[r] = p_ntp + K;
+        for (int r = tid; r < Cb; r += 256) {
+            if (r < C) {
+                const int in0 = s_in[r];
+                const int p_ntp = a.in.target_pos[in0 + s_v[r] - 1];
+                a.out.cu_out[r] = in0 + r * (K - 1);
+                a.out.seq_lens[r] = p_ntp + K;
+            } else {
+                a.out.cu_out[r] = T_out;
+                a.out.seq_lens[r] = 1;
+                for (int m = 0; m < K; ++m) a.out.new_token_indices[r * K + m] = a.T_out - 1;
+            }
         }
-        if (tid == 0) a.out.cu_out[C] = a.T_out;
+        for (int j = T_in + tid; j < a.d.T_in; j += 256) a.out.hidden_state_mapping[j] = -1;
+        if (tid == 0) a.out.cu_out[Cb] = T_out;
     }
 
     for (int rr = 0; rr < a.rows_per_block; ++rr) {
         const int o = blockIdx.x * a.rows_per_block + rr;
         if (o >= a.T_out) break;
+        if (o >= T_out) {
+            // padding row: a rejected MASK-id row with zero hidden state (finite
+            // everywhere, writes no KV, never sampled by a live request)
+            if (tid == 0) {
+                a.out.input_ids[o] = a.d.mask_token_id;
+                a.out.positions[o] = 0;
+                a.out.is_rejected[o] = 1;
+                a.out.is_masked[o] = 0;
+                a.out.slot_mapping[o] = -1;
+            }
+            uint4* d4 = reinterpret_cast<uint4*>(a.out.hidden + (size_t)o * a.d.hidden3);
+            for (int c = tid; c < a.d.hidden3 / 8; c += 256) d4[c] = make_uint4(0, 0, 0, 0);
+            continue;
+        }
         // request of row o: the last r whose first output row is <= o
         int lo = 0, hi = C - 1;
         while (lo < hi) {

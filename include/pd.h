@@ -82,6 +82,7 @@ typedef struct {
     const int32_t*  next_token_ids; /* [C]  the token the target sampled for request r          */
     const int32_t*  block_table;    /* [C][max_blocks] page numbers                              */
     const uint16_t* h_shared;       /* [hidden3] bf16 learned shared hidden state                */
+    const int32_t*  live_counts;    /* [2] {C, T_in} of the live batch, or NULL (= dims); see below */
 } pd_expand_in;
 
 /* The expanded (draft) batch: written by pd_expand_batch, read by
@@ -123,6 +124,21 @@ typedef struct {
  *     with p_ntp = target_pos[a_r+v_r-1]; hidden = h_shared.
  *   seq_lens[r] = p_ntp + K.
  * The hidden rows are copied bit-for-bit.
+ *
+ * Bucketed batches (live_counts != NULL): dims give the capacity a captured
+ * graph was sized for ([Blog] "vLLM engineering details": the draft step runs
+ * under graph capture, its range extended to hold the larger draft batch), and
+ * the device words live_counts = {C, T_in} the batch actually present, 0 <= C
+ * <= dims->C, C <= T_in <= dims->T_in; the inputs hold that batch in their
+ * first C requests / T_in rows. The live rows come out exactly as for a call
+ * with those sizes. Requests C .. dims->C-1 are padding: cu_out = the live
+ * T_out (also cu_out[dims->C]), seq_lens = 1, their K new-token indices =
+ * the last expanded row. Rows from the live T_out to dims' T_out are padding:
+ * mask_token_id, position 0, rejected, slot -1, zero hidden rows. Padding
+ * input rows map to -1. pd_draft_forward then runs at the capacity's sizes:
+ * padding rows write no KV and change no live row's result, and the draft ids
+ * of padding requests are meaningless. Bad live counts set
+ * PD_STATUS_BAD_COUNTS and write nothing.
  *
  * Errors: PD_EINVAL if dims/in/out or a required pointer is NULL, C outside
  * [0, PD_MAX_C], K outside [1, PD_MAX_K], T_in < C, hidden3 <= 0 or not a
