@@ -67,18 +67,33 @@ constexpr int kRS = 128;   // reduction elements per ring stage (256 B of each r
 // 16 zero bytes: the source of out-of-range chunks (zero-initialised at load)
 __device__ __align__(16) uint16_t g_gemm_zero[8];
 
-template <int WN, int NM, int MT>
+// KRS: reduction elements per stage (128: rows of 16 16-byte chunks; 64: rows
+// of 8 chunks, for 8 X tiles, whose X rows would otherwise crowd the ring).
+template <int WN, int NM, int MT, int KRS = kRS>
 struct RingCfg {
     static constexpr int NT = 64 * WN;
+    static constexpr int CH = KRS / 8;        // 16-byte chunks per staged row
     static constexpr int WR = 16 * WN * NM;   // W rows per stage (64 or 128)
     static constexpr int XR = 16 * MT;        // X rows per stage
-    static constexpr int WL = WR * 16 / NT;   // 16-byte W loads per thread per stage
-    static constexpr int XL = XR * 16 / NT;   // 16-byte X loads per thread per stage
+    static constexpr int WL = WR * CH / NT;   // 16-byte W loads per thread per stage
+    static constexpr int XL = XR * CH / NT;   // 16-byte X loads per thread per stage
     static constexpr int L = WL + XL;
-    static constexpr int SE = (WR + XR) * kRS;   // elements per stage
-    static constexpr int NST = WR == 64 ? (MT == 1 ? 6 : (MT == 2 ? 5 : 4)) : (MT == 1 ? 4 : 3);
-    static_assert(WL * NT == WR * 16 && XL * NT == XR * 16, "whole loads per thread");
+    static constexpr int SE = (WR + XR) * KRS;   // elements per stage
+    static constexpr int NST = KRS == 64 ? 4
+                               : (WR == 64 ? (MT == 1 ? 6 : (MT == 2 ? 5 : 4)) : (MT == 1 ? 4 : 3));
+    static_assert(WL * NT == WR * CH && XL * NT == XR * CH, "whole loads per thread");
 };
+
+// Chunk permutation of a staged row: the 16 lanes one LDS cycle serves read
+// rows r .. r+15 at one chunk. With 16 chunks a row fills a 256-byte bank
+// line and the chunk is XORed with r & 15; with 8 chunks two rows share a
+// line (the row's parity picks the half) and the chunk is XORed with
+// (r >> 1) & 7. Either way the 16 lanes hit 16 distinct 16-byte slots.
+template <int CH>
+__device__ __forceinline__ int ring_sw(int row) {
+    if constexpr (CH == 16) return row & 15;
+    else return (row >> 1) & 7;
+}
 
 template <int N>
 __device__ __forceinline__ void ring_wait() {
@@ -105,10 +120,10 @@ __device__ __forceinline__ unsigned ring_lds(void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)p);
 }
 
-template <int WN, int NM, int MT, int EPI>
+template <int WN, int NM, int MT, int EPI, int KRS = kRS>
 __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
-    using Cf = RingCfg<WN, NM, MT>;
-    constexpr int NT = Cf::NT, NST = Cf::NST, L = Cf::L, WL = Cf::WL, XL = Cf::XL;
+    using Cf = RingCfg<WN, NM, MT, KRS>;
+    constexpr int NT = Cf::NT, NST = Cf::NST, L = Cf::L, WL = Cf::WL, XL = Cf::XL, CH = Cf::CH;
     constexpr bool PAIR = (EPI == EPI_SWIGLU);          // row groups = gate, up of the same columns
     constexpr int TW = 16 * WN * (PAIR ? 1 : NM);       // output columns per tile
     __shared__ __align__(16) uint16_t ring[NST * Cf::SE];
@@ -116,7 +131,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
 
-    const int ksteps = (a.K + kRS - 1) / kRS;
+    const int ksteps = (a.K + KRS - 1) / KRS;
     const int per = (ksteps + a.splits - 1) / a.splits;
     const int ntn = (a.N + TW - 1) / TW;   // column tiles
     const int nitems = ntn * a.splits;
@@ -127,17 +142,17 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
     int wrr[WL], wch[WL], wofs[WL];
 #pragma unroll
     for (int j = 0; j < WL; ++j) {
-        const int u = tid + NT * j, wr = u >> 4;
+        const int u = tid + NT * j, wr = u / CH;
         wrr[j] = wr % (16 * WN);
-        wch[j] = ((u & 15) ^ (wr & 15)) * 8;
+        wch[j] = ((u % CH) ^ ring_sw<CH>(wr)) * 8;
         wofs[j] = wrr[j] * a.K + wch[j];   // element offset from the tile's first row, k = 0
     }
     const uint16_t* xp[XL];
     int xch[XL];
 #pragma unroll
     for (int j = 0; j < XL; ++j) {
-        const int u = tid + NT * j, m = u >> 4;
-        xch[j] = ((u & 15) ^ (m & 15)) * 8;
+        const int u = tid + NT * j, m = u / CH;
+        xch[j] = ((u % CH) ^ ring_sw<CH>(m)) * 8;
         int row = m;
         bool ok = m < a.M;
         if (ok && a.xrows) {
@@ -173,7 +188,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
         wfull = n0 + TW <= a.N;
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
-            const int q = j * NT / (16 * 16 * WN);   // row group of this load (compile-time)
+            const int q = j * NT / (CH * 16 * WN);   // row group of this load (compile-time)
             const int nq = n0 + (PAIR ? 0 : q * 16 * WN);
             const uint16_t* base = (PAIR && q == 1) ? a.W2 : a.W;
             wp[j] = (nq + wrr[j] < a.N) ? base + (size_t)nq * a.K + wofs[j] : nullptr;
@@ -186,10 +201,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             iitem += G;
             if (iitem < nitems) set_item();
         }
-        const int k0 = iks * kRS;
+        const int k0 = iks * KRS;
         const unsigned sbase = lds0 + (unsigned)(slot * Cf::SE) * 2u;
         // whole tile inside N and whole stage inside K: no per-lane bounds
-        const bool kin = k0 + kRS <= a.K;
+        const bool kin = k0 + KRS <= a.K;
         const bool inner = wfull && kin;
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             const int k = k0 + xch[j];
             const uint16_t* src = (xp[j] && (kin || k < a.K)) ? xp[j] + k : zp;
             __builtin_amdgcn_global_load_lds((void*)src,
-                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(Cf::WR * kRS * 2) +
+                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(Cf::WR * KRS * 2) +
                                                                       (unsigned)(wave * 64 + NT * j) * 16u),
                 16, 0, 0);
         }
@@ -244,17 +259,19 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             ring_barrier();
             if (qc + NST - 1 < total) issue((qc + NST - 1) % NST);
             const uint16_t* Ws = ring + (qc % NST) * Cf::SE;
-            const uint16_t* Xs = Ws + Cf::WR * kRS;
+            const uint16_t* Xs = Ws + Cf::WR * KRS;
 #pragma unroll
-            for (int j = 0; j < kRS / 32; ++j) {
-                const int pos = ((4 * j + g4) ^ r16) * 8;
+            for (int j = 0; j < KRS / 32; ++j) {
+                // every staged row here is 16t + r16 for some t: its permutation
+                // depends on r16 alone
+                const int pos = ((4 * j + g4) ^ ring_sw<CH>(r16)) * 8;
                 bf16x8 wf[NM];
 #pragma unroll
                 for (int q = 0; q < NM; ++q)
-                    wf[q] = *reinterpret_cast<const bf16x8*>(Ws + (q * 16 * WN + 16 * wave + r16) * kRS + pos);
+                    wf[q] = *reinterpret_cast<const bf16x8*>(Ws + (q * 16 * WN + 16 * wave + r16) * KRS + pos);
 #pragma unroll
                 for (int t = 0; t < MT; ++t) {
-                    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(Xs + (16 * t + r16) * kRS + pos);
+                    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(Xs + (16 * t + r16) * KRS + pos);
 #pragma unroll
                     for (int q = 0; q < NM; ++q) acc[t][q] = mfma_16x16x32(wf[q], xf, acc[t][q]);
                 }
@@ -849,6 +866,14 @@ int launch_ring_nm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
         case 1: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 1, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
         case 2: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 2, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
         case 4: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 4, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
+        case 8:
+            if constexpr (EPI == EPI_ARGMAX && NM == 2) {
+                if (p.krs != 64) return PD_EINVAL;
+                hipLaunchKernelGGL((gemm_ring_kernel<WN, 2, 8, EPI_ARGMAX, 64>), dim3(p.grid), dim3(64 * WN), 0, s, a);
+                break;
+            } else {
+                return PD_EINVAL;
+            }
         default: return PD_EINVAL;
     }
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
@@ -889,6 +914,24 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
     p.kind = M <= 64 ? GEMM_RING : ((M < 256 && epi == EPI_ARGMAX) ? GEMM_TILED : GEMM_BIG);
     p.splits = 1;
     p.grid = 0;
+    p.krs = kRS;
+    if (epi == EPI_ARGMAX && M > 64 && M <= 128) {
+        // the LM head at 65..128 rows is still a weight stream (~128 flop per
+        // weight byte, below the ridge): the ring with all 8 X tiles, two
+        // column groups per wave and 64-element stages (the X rows would
+        // otherwise fill the ring); every weight is read once
+        p.kind = GEMM_RING;
+        p.mt = 8;
+        p.mblocks = 1;
+        p.wn = 4;
+        p.nm = 2;
+        p.krs = 64;
+        const long items = (N + 127) / 128;
+        const long rounds = (items + 255) / 256;
+        p.grid = (int)((items + rounds - 1) / rounds);
+        p.ntiles = p.grid * p.wn;
+        return p;
+    }
     if (p.kind == GEMM_BIG) {
         // persistent tiles of bt x bt: 256 (8 waves, one workgroup per CU) from
         // 384 rows on, 128 (4 waves, two workgroups per CU) below; K splits
@@ -984,7 +1027,7 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
 // g_c4 step 632 vs 623 us).
 GemmPlan plan_gemm(int M, int N, int K, int epi) {
     const GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
-    if (p.kind == GEMM_RING && p.mt >= 2 && epi != EPI_SWIGLU) {
+    if (p.kind == GEMM_RING && p.mt >= 2 && p.mt <= 4 && epi != EPI_SWIGLU) {
         const GemmPlan w = plan_gemm_nm(M, N, K, epi, 2);
         if (w.grid >= 220) return w;
     }

@@ -61,13 +61,15 @@ def test_small_models_all_rows(dims, C, K, ctx, L):
 # column and row tiles. The batch shapes pick the kernel by row count: 768
 # expanded rows and 384 sampled rows (256-row ring-fed tiles), 576 expanded
 # and 288 sampled rows (the LM head on 128-row ring-fed tiles), 128 rows
-# (the projections on 128-row ring-fed tiles), 64 and 10 sampled rows and 20
+# (the projections on 128-row ring-fed tiles), 96 sampled rows (the LM head on
+# the 8-tile weight-streaming ring with 64-element stages: a partial last
+# column tile and a partial last stage), 64 and 10 sampled rows and 20
 # expanded rows (weight-streaming kernel).
 RAGGED = synth.ModelDims("ragged", d=208, Hq=4, Hkv=2, dh=64, F=688, N=2, V=1008)
 
 
-@pytest.mark.parametrize("C,K,L", [(48, 8, 90), (36, 8, 60), (8, 8, 300), (2, 5, 33)],
-                         ids=["rows768", "rows576", "rows128", "rows16"])
+@pytest.mark.parametrize("C,K,L", [(48, 8, 90), (36, 8, 60), (12, 8, 40), (8, 8, 300), (2, 5, 33)],
+                         ids=["rows768", "rows576", "rows192-lm96", "rows128", "rows16"])
 def test_ragged_widths_all_rows(C, K, L):
     w = synth.Workload(f"ragged-c{C}k{K}", RAGGED, C=C, K=K, context="fixed", L=L, seed=5 + C)
     _say(f"[forward] {w.name}")
