@@ -29,6 +29,9 @@
 #include <float.h>
 #include <limits.h>
 
+#include <utility>
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -334,6 +337,236 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             if (g4 == 0 && m < a.M) {
                 a.amax_v[(size_t)m * a.ntiles + blockIdx.x * WN + wave] = bv;
                 a.amax_i[(size_t)m * a.ntiles + blockIdx.x * WN + wave] = bi;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weight-only ring (17..64 rows: the projections of the few-request steps).
+// The ring kernel above stages the X columns in its LDS stages next to the
+// weights; at 33..64 rows they fill half of every stage, and a CU keeps only
+// ~48 KB of weights in flight, which is what bounds a latency-limited stream
+// (the gate/up stream runs ~1.5x slower at 56 rows than at 7, the ratio of
+// the weight bytes in flight). Here the LDS ring holds weights only: NST = 8
+// stages of 64 W rows x 128 reduction elements (16 KB each; 7 stages = 112 KB
+// in flight while one is read). Each of the four waves owns one 16-row X tile
+// and all 64 columns of the stage, and loads its X fragments straight into
+// registers, from L2 (X is a few hundred KB that every workgroup re-reads).
+// The X loads of a stage are issued with the stage's weight loads, NST - 1
+// stages ahead, so the ring's in-order vmcnt waits cover them too; the
+// register slot of stage q is q mod NST, and the stage loop runs in whole
+// passes of NST stages, unrolled, so that every slot index is a compile-time
+// constant. Padding rows of a partial X tile read zeros; their MFMAs cost
+// nothing in a stream this far below the ridge.
+//
+// The compiler adds its own waits before the X registers are used; they stay
+// partial (NST - 2 stages of loads may remain in flight) because the weight
+// copies use the buffer form (see below). A workgroup owns exactly one
+// (column tile, K split) item and writes it after the loop. Projections
+// only (fp32 partial planes, SwiGLU): measured on the 4-request step, the
+// projections run 24 us faster per step than on the ring kernel (7 vs 3
+// stages of weights in flight), the 28-row LM head 20 us slower.
+constexpr int kWRingStages = 8;
+// word 3 of a raw buffer descriptor on gfx9 (no format conversion, no swizzle)
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// f(integral_constant<int, I>) for I = 0, 1, ... in order
+template <int... I, class F>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
+    constexpr int NST = kWRingStages;
+    constexpr int NT = 256, CH = kRS / 8;
+    constexpr int WR = 64;                 // W rows per stage: 4 groups of 16, all read by every wave
+    constexpr int WL = WR * CH / NT;       // W loads per thread per stage (4): load j = group j
+    constexpr int XLD = kRS / 32;          // X fragment loads per lane per stage (4)
+    constexpr int L = WL + XLD;            // vector memory ops per thread per stage
+    constexpr int SE = WR * kRS;           // elements per stage
+    constexpr bool PAIR = (EPI == EPI_SWIGLU);
+    static_assert(EPI == EPI_PARTIAL || EPI == EPI_SWIGLU, "projections");
+    constexpr int TW = PAIR ? WR / 2 : WR;      // output columns per tile
+    static_assert((NST - 2) * L <= 63, "the waits fit the vmcnt field");
+    static_assert(WL == 4 && NT / CH == 16, "load j of a thread is row tid / 16 of group j");
+    __shared__ __align__(16) uint16_t ring[NST * SE];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // = the wave's X tile
+    const int r16 = lane & 15, g4 = lane >> 4;
+    const int m = 16 * wave + r16;   // this lane's output row
+
+    const int ksteps = (a.K + kRS - 1) / kRS;
+    const int per = (ksteps + a.splits - 1) / a.splits;
+    const int ntn = (a.N + TW - 1) / TW;
+    const int nitems = ntn * a.splits;
+    const int item = blockIdx.x;   // the plan launches one workgroup per item
+    if (item >= nitems) return;    // whole workgroup
+
+    // This thread's W loads of every stage: load j copies row tid / 16 of
+    // group j (staged row 16 j + tid / 16) at LDS chunk tid % 16, which holds
+    // global chunk (tid % 16) ^ (tid / 16). SwiGLU: groups 0, 1 are gate
+    // columns 0..31 of the tile, groups 2, 3 the up rows of the same columns.
+    const int wrow = tid >> 4;
+    const int wchb = (((tid & 15) ^ wrow) * 8) * 2;   // byte offset of the chunk within a row stage
+    // this lane's X row, or none past M
+    int xrow = -1;
+    if (m < a.M) {
+        int row = m;
+        if (a.xrows) {
+            row = a.xrows[m];
+            if (row < 0 || row >= a.xrows_limit) {
+                row = -1;
+                flag(a.status, PD_STATUS_BAD_ROW);
+            }
+        }
+        xrow = row;
+    }
+    const unsigned lds0 = ring_lds(ring);
+
+    // Copies go through buffer descriptors: weights global -> LDS (the MUBUF
+    // form: the compiler treats the global form as a FLAT access that may
+    // touch LDS, and while one is in flight it turns every wait of its own
+    // for the X registers into a full drain), X into registers. A whole
+    // stage adds its K offset as the scalar soffset, so it costs 4 M0 moves
+    // and 8 loads. The range check covers the per-lane offset only (not
+    // soffset): a stage that reaches past K adds its K offset per lane
+    // instead, so that reads past the last weight row come back as zeros;
+    // weight chunks past K otherwise read the next row, which only meets X
+    // chunks that are zero there. Offsets past the range (kOut) read zeros
+    // and touch no memory: W rows past N, X rows past M or badly gathered,
+    // X chunks past K, and every load of a stage past the last one. The
+    // planner keeps N * K * 2 below 2^31.
+    constexpr unsigned kOut = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.W, 0, a.N * a.K * 2, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t wrs2 =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(PAIR ? a.W2 : a.W), 0, a.N * a.K * 2, kBufferRsrcWord3);
+    const int xrows_n = a.xrows ? a.xrows_limit : a.M;
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.X, 0, xrows_n * a.ldx * 2, kBufferRsrcWord3);
+    unsigned xvo[XLD];   // byte offset of this lane's X chunk j at k = 0
+#pragma unroll
+    for (int j = 0; j < XLD; ++j)
+        xvo[j] = xrow >= 0 ? (unsigned)((xrow * a.ldx + 32 * j + 8 * g4) * 2) : kOut;
+
+    // the item: column tile n0, K split sp = stages kb0 .. kb0 + kcnt - 1
+    const int sp = item / ntn;
+    const int n0 = (item % ntn) * TW;
+    const int kb0 = sp * per;
+    const int total = max(0, min(ksteps, (sp + 1) * per) - kb0);
+    const int kcnt = max(1, total);
+    unsigned wvo[WL];   // byte offset of this thread's chunk j at k = 0, or kOut past N
+#pragma unroll
+    for (int j = 0; j < WL; ++j) {
+        const int col = n0 + (PAIR ? (j & 1) * 16 : 16 * j) + wrow;
+        wvo[j] = col < a.N ? (unsigned)(col * a.K * 2 + wchb) : kOut;
+    }
+    // the stages start at a point set by the column tile, so that workgroups
+    // sharing a K split read different X lines at any moment
+    const int rot = (item % ntn) % kcnt;
+    int iks = 0;   // stages issued
+    // Loads of the next stage into LDS slot `slot` and register slot xd.
+    // Every call issues the same L loads, also past the last stage (live
+    // false), so the loads in flight behind a stage are the same on every
+    // path; only their offsets depend on the case.
+    auto issue = [&](int slot, bf16x8 (&xd)[XLD], bool live) __attribute__((always_inline)) {
+        const int k0 = (kb0 + (iks + rot) % kcnt) * kRS;
+        const unsigned sbase = lds0 + (unsigned)(slot * SE) * 2u;
+        unsigned so = (unsigned)k0 * 2u;
+        unsigned wv[WL], xv[XLD];
+#pragma unroll
+        for (int j = 0; j < WL; ++j) wv[j] = wvo[j];
+#pragma unroll
+        for (int j = 0; j < XLD; ++j) xv[j] = xvo[j];
+        if (!live || k0 + kRS > a.K) {
+            so = 0;
+#pragma unroll
+            for (int j = 0; j < WL; ++j) wv[j] = (live && wvo[j] != kOut) ? wvo[j] + (unsigned)k0 * 2u : kOut;
+#pragma unroll
+            for (int j = 0; j < XLD; ++j)
+                xv[j] = (live && k0 + 32 * j + 8 * g4 < a.K) ? xvo[j] + (unsigned)k0 * 2u : kOut;
+        }
+#pragma unroll
+        for (int j = 0; j < WL; ++j)   // every weight is read once: non-temporal (cache policy 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((PAIR && j >= 2) ? wrs2 : wrs,
+                (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
+                16, wv[j], so, 0, 2);
+#pragma unroll
+        for (int j = 0; j < XLD; ++j)
+            xd[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xrs, xv[j], so, 0));
+        if (live) ++iks;
+    };
+
+    bf16x8 xr[NST][XLD];
+    ring_wait<0>();   // row gathers done before the ring starts counting
+    // the ring's waits count whole stages: the compiler must not move the X
+    // loads (plain reads) of one stage across another's, hence the fence
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st) {
+        issue(st, xr[st], st < total);
+        asm volatile("" ::: "memory");
+    }
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // One stage: qc = the stage, us = qc mod NST (a compile-time constant at
+    // every call: the LDS slot and the register slot of the stage).
+    auto step = [&](const int qc, auto usc) __attribute__((always_inline)) {
+        constexpr int us = decltype(usc)::value;
+        // loads of stage qc done (the NST - 2 stages after it may stay in
+        // flight), then every wave's
+        ring_wait<(NST - 2) * L>();
+        ring_barrier();
+        issue((us + NST - 1) % NST, xr[(us + NST - 1) % NST], qc + NST - 1 < total);
+        const uint16_t* Ws = ring + us * SE;
+#pragma unroll
+        for (int j = 0; j < kRS / 32; ++j) {
+            const int pos = ((4 * j + g4) ^ r16) * 8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16x8 wf = *reinterpret_cast<const bf16x8*>(Ws + (16 * q + r16) * kRS + pos);
+                acc[q] = mfma_16x16x32(wf, xr[us][j], acc[q]);
+            }
+        }
+    };
+    // Whole passes of NST stages, then the last < NST stages in straight
+    // code, so that no edge leads from inside a pass back to its start.
+    int q0 = 0;
+    for (; q0 + NST <= total; q0 += NST)
+        for_each_index(std::make_integer_sequence<int, NST>{}, [&](auto i) __attribute__((always_inline)) {
+            step(q0 + decltype(i)::value, i);
+        });
+    for_each_index(std::make_integer_sequence<int, NST>{}, [&](auto i) __attribute__((always_inline)) {
+        if (q0 + decltype(i)::value < total) step(q0 + decltype(i)::value, i);
+    });
+    ring_wait<0>();   // the zero-page loads past the last stage have landed
+
+    if (total == 0) return;
+    if constexpr (EPI == EPI_PARTIAL) {
+        if (m < a.M) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + 16 * q + 4 * g4;
+                if (n < a.N) *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[q];
+            }
+        }
+    } else {
+        if (m < a.M) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int n = n0 + 16 * q + 4 * g4;
+                if (n >= a.N) continue;
+                float h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = silu(acc[q][e]) * acc[q + 2][e];
+                uint2 pk;
+                pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
+                pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
+                *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
             }
         }
     }
@@ -890,10 +1123,23 @@ int launch_ring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     }
 }
 
+// weight-only ring (17..64 rows, projections)
+template <int EPI>
+int launch_wring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
+    if constexpr (EPI == EPI_ARGMAX) {
+        return PD_EINVAL;
+    } else {
+        if (p.mt != 4 || p.nm != 4 || p.grid < p.ntiles * p.splits) return PD_EINVAL;   // one item per workgroup
+        hipLaunchKernelGGL((gemm_wring_kernel<EPI>), dim3(p.grid), dim3(256), 0, s, a);
+        return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+    }
+}
+
 template <int EPI>
 int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     switch (p.kind) {
         case GEMM_RING: return launch_ring<EPI>(p, a, s);
+        case GEMM_WRING: return launch_wring<EPI>(p, a, s);
         case GEMM_TILED: return launch_tiled<EPI>(p, a, s);
         default: return launch_big<EPI>(p, a, s);
     }
@@ -1025,7 +1271,41 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
 // 207 vs 210 us), and so is the narrow tile where the wide one leaves CUs
 // idle (the d-wide outputs, whose K splits are capped at 8: 184 workgroups,
 // g_c4 step 632 vs 623 us).
+// Weight-only ring for the projections of 17..64 rows (see
+// gemm_wring_kernel), always with its four X tiles (padding rows read zeros;
+// their MFMAs cost nothing in a stream this far below the ridge), one
+// workgroup per (column tile, K split) item; K splits chosen as for the ring
+// kernel.
+static GemmPlan plan_wring(int N, int K, int epi) {
+    GemmPlan p;
+    p.kind = GEMM_WRING;
+    p.mt = 4;
+    p.mblocks = 1;
+    p.wn = 4;
+    p.nm = 4;
+    p.krs = kRS;
+    p.splits = 1;
+    const int tw = epi == EPI_SWIGLU ? 32 : 64;
+    const int ntn = (N + tw - 1) / tw;
+    const int ksteps = (K + kRS - 1) / kRS;
+    if (epi == EPI_PARTIAL) {
+        long best = -1;
+        for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
+            const int per = (ksteps + sp - 1) / sp;
+            if ((sp - 1) * per >= ksteps) continue;
+            const long items = (long)ntn * sp;
+            const long span = ((items + 255) / 256) * per;
+            if (best < 0 || span < best) { best = span; p.splits = sp; }
+        }
+    }
+    p.grid = ntn * p.splits;
+    p.ntiles = ntn;
+    return p;
+}
+
 GemmPlan plan_gemm(int M, int N, int K, int epi) {
+    // (the weight-only ring addresses a matrix with 32-bit byte offsets)
+    if (M > 16 && M <= 64 && epi != EPI_ARGMAX && (long long)N * K * 2 < (1LL << 31)) return plan_wring(N, K, epi);
     const GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
     if (p.kind == GEMM_RING && p.mt >= 2 && p.mt <= 4 && epi != EPI_SWIGLU) {
         const GemmPlan w = plan_gemm_nm(M, N, K, epi, 2);
