@@ -377,21 +377,35 @@ __device__ __forceinline__ void for_each_index(std::integer_sequence<int, I...>,
     (f(std::integral_constant<int, I>{}), ...);
 }
 
-template <int EPI>
+// GW groups of 16 W rows per stage (every wave reads all of them). Four, one
+// workgroup per CU: two groups in a 64 KB ring with two workgroups per CU
+// ran the 4-request step 59 us slower. (The per-thread arrays below have
+// the fixed size 4 >= GW: local arrays
+// whose size depends on the template parameter, used inside the lambdas,
+// make the host pass drop the launch stub.)
+template <int GW>
+struct WRingCfg {
+    static constexpr int NST = kWRingStages;
+    static constexpr int NT = 256, CH = kRS / 8;
+    static constexpr int WR = 16 * GW;       // W rows per stage
+    static constexpr int WL = WR * CH / NT;  // W loads per thread per stage: load j = group j
+    static constexpr int XLD = kRS / 32;     // X fragment loads per lane per stage (4)
+    static constexpr int L = WL + XLD;       // vector memory ops per thread per stage
+    static constexpr int SE = WR * kRS;      // elements per stage
+};
+
+template <int EPI, int GW>
 __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
-    constexpr int NST = kWRingStages;
-    constexpr int NT = 256, CH = kRS / 8;
-    constexpr int WR = 64;                 // W rows per stage: 4 groups of 16, all read by every wave
-    constexpr int WL = WR * CH / NT;       // W loads per thread per stage (4): load j = group j
-    constexpr int XLD = kRS / 32;          // X fragment loads per lane per stage (4)
-    constexpr int L = WL + XLD;            // vector memory ops per thread per stage
-    constexpr int SE = WR * kRS;           // elements per stage
+    using Cf = WRingCfg<GW>;
+    constexpr int NST = Cf::NST, NT = Cf::NT, CH = Cf::CH, WR = Cf::WR, WL = Cf::WL, XLD = Cf::XLD;
+    constexpr int L = Cf::L, SE = Cf::SE;
     constexpr bool PAIR = (EPI == EPI_SWIGLU);
     static_assert(EPI == EPI_PARTIAL || EPI == EPI_SWIGLU, "projections");
     constexpr int TW = PAIR ? WR / 2 : WR;      // output columns per tile
     static_assert((NST - 2) * L <= 63, "the waits fit the vmcnt field");
-    static_assert(WL == 4 && NT / CH == 16, "load j of a thread is row tid / 16 of group j");
-    __shared__ __align__(16) uint16_t ring[NST * SE];
+    static_assert(WL == GW && WL <= 4 && XLD == 4 && NT / CH == 16, "load j of a thread is row tid / 16 of group j");
+    static_assert(!PAIR || GW % 2 == 0, "gate and up groups in pairs");
+    __shared__ __align__(16) uint16_t ring[Cf::NST * Cf::SE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // = the wave's X tile
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -406,8 +420,8 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
 
     // This thread's W loads of every stage: load j copies row tid / 16 of
     // group j (staged row 16 j + tid / 16) at LDS chunk tid % 16, which holds
-    // global chunk (tid % 16) ^ (tid / 16). SwiGLU: groups 0, 1 are gate
-    // columns 0..31 of the tile, groups 2, 3 the up rows of the same columns.
+    // global chunk (tid % 16) ^ (tid / 16). SwiGLU: groups 0 .. GW/2 - 1 are
+    // gate columns of the tile, the rest the up rows of the same columns.
     const int wrow = tid >> 4;
     const int wchb = (((tid & 15) ^ wrow) * 8) * 2;   // byte offset of the chunk within a row stage
     // this lane's X row, or none past M
@@ -446,7 +460,7 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
     const int xrows_n = a.xrows ? a.xrows_limit : a.M;
     const __amdgpu_buffer_rsrc_t xrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.X, 0, xrows_n * a.ldx * 2, kBufferRsrcWord3);
-    unsigned xvo[XLD];   // byte offset of this lane's X chunk j at k = 0
+    unsigned xvo[Cf::XLD];   // byte offset of this lane's X chunk j at k = 0
 #pragma unroll
     for (int j = 0; j < XLD; ++j)
         xvo[j] = xrow >= 0 ? (unsigned)((xrow * a.ldx + 32 * j + 8 * g4) * 2) : kOut;
@@ -457,10 +471,10 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
     const int kb0 = sp * per;
     const int total = max(0, min(ksteps, (sp + 1) * per) - kb0);
     const int kcnt = max(1, total);
-    unsigned wvo[WL];   // byte offset of this thread's chunk j at k = 0, or kOut past N
+    unsigned wvo[4];   // byte offset of this thread's chunk j at k = 0, or kOut past N
 #pragma unroll
     for (int j = 0; j < WL; ++j) {
-        const int col = n0 + (PAIR ? (j & 1) * 16 : 16 * j) + wrow;
+        const int col = n0 + (PAIR ? (j % (GW / 2)) * 16 : 16 * j) + wrow;
         wvo[j] = col < a.N ? (unsigned)(col * a.K * 2 + wchb) : kOut;
     }
     // the stages start at a point set by the column tile, so that workgroups
@@ -471,11 +485,11 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
     // Every call issues the same L loads, also past the last stage (live
     // false), so the loads in flight behind a stage are the same on every
     // path; only their offsets depend on the case.
-    auto issue = [&](int slot, bf16x8 (&xd)[XLD], bool live) __attribute__((always_inline)) {
+    auto issue = [&](int slot, bf16x8 (&xd)[Cf::XLD], bool live) __attribute__((always_inline)) {
         const int k0 = (kb0 + (iks + rot) % kcnt) * kRS;
         const unsigned sbase = lds0 + (unsigned)(slot * SE) * 2u;
         unsigned so = (unsigned)k0 * 2u;
-        unsigned wv[WL], xv[XLD];
+        unsigned wv[4], xv[4];
 #pragma unroll
         for (int j = 0; j < WL; ++j) wv[j] = wvo[j];
 #pragma unroll
@@ -490,7 +504,7 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < WL; ++j)   // every weight is read once: non-temporal (cache policy 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds((PAIR && j >= 2) ? wrs2 : wrs,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds((PAIR && j >= GW / 2) ? wrs2 : wrs,
                 (__attribute__((address_space(3))) void*)(uintptr_t)(sbase + (unsigned)(wave * 64 + NT * j) * 16u),
                 16, wv[j], so, 0, 2);
 #pragma unroll
@@ -499,7 +513,7 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
         if (live) ++iks;
     };
 
-    bf16x8 xr[NST][XLD];
+    bf16x8 xr[Cf::NST][Cf::XLD];
     ring_wait<0>();   // row gathers done before the ring starts counting
     // the ring's waits count whole stages: the compiler must not move the X
     // loads (plain reads) of one stage across another's, hence the fence
@@ -511,7 +525,7 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
 
     f32x4 acc[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < GW; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // One stage: qc = the stage, us = qc mod NST (a compile-time constant at
     // every call: the LDS slot and the register slot of the stage).
@@ -527,7 +541,7 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
         for (int j = 0; j < kRS / 32; ++j) {
             const int pos = ((4 * j + g4) ^ r16) * 8;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < GW; ++q) {
                 const bf16x8 wf = *reinterpret_cast<const bf16x8*>(Ws + (16 * q + r16) * kRS + pos);
                 acc[q] = mfma_16x16x32(wf, xr[us][j], acc[q]);
             }
@@ -549,7 +563,7 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
     if constexpr (EPI == EPI_PARTIAL) {
         if (m < a.M) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < GW; ++q) {
                 const int n = n0 + 16 * q + 4 * g4;
                 if (n < a.N) *reinterpret_cast<f32x4*>(a.ws + ((size_t)sp * a.M + m) * a.N + n) = acc[q];
             }
@@ -557,12 +571,12 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
     } else {
         if (m < a.M) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
+            for (int q = 0; q < GW / 2; ++q) {
                 const int n = n0 + 16 * q + 4 * g4;
                 if (n >= a.N) continue;
                 float h[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = silu(acc[q][e]) * acc[q + 2][e];
+                for (int e = 0; e < 4; ++e) h[e] = silu(acc[q][e]) * acc[q + GW / 2][e];
                 uint2 pk;
                 pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
                 pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
@@ -1130,7 +1144,7 @@ int launch_wring(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
         return PD_EINVAL;
     } else {
         if (p.mt != 4 || p.nm != 4 || p.grid < p.ntiles * p.splits) return PD_EINVAL;   // one item per workgroup
-        hipLaunchKernelGGL((gemm_wring_kernel<EPI>), dim3(p.grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((gemm_wring_kernel<EPI, 4>), dim3(p.grid), dim3(256), 0, s, a);
         return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
     }
 }
@@ -1285,7 +1299,7 @@ static GemmPlan plan_wring(int N, int K, int epi) {
     p.nm = 4;
     p.krs = kRS;
     p.splits = 1;
-    const int tw = epi == EPI_SWIGLU ? 32 : 64;
+    const int tw = epi == EPI_SWIGLU ? 8 * p.nm : 16 * p.nm;
     const int ntn = (N + tw - 1) / tw;
     const int ksteps = (K + kRS - 1) / kRS;
     if (epi == EPI_PARTIAL) {
