@@ -155,16 +155,16 @@ def copy_calibration(mib: int = 512, reps: int = 4):
     print(json.dumps({"copy_calibration_bytes_per_launch": mib * (1 << 20), "launches": reps}))
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_g_c1_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_g_c1_q_c16_traffic.md")
 
 
 def recorded_traffic(workload: str):
     """HBM bytes per LM-head launch recorded by the FETCH_SIZE / WRITE_SIZE
-    counter passes (profiles/lmhead_g_c1_traffic.md), or None when they were
-    taken on another workload or on a different GEMM source than the one
-    built now."""
+    counter passes (profiles/lmhead_g_c1_q_c16_traffic.md) for this
+    workload, or None when none were taken on it or they were taken on a
+    different GEMM source than the one built now."""
     import hashlib
-    if workload != "g_c1" or not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
     for line in open(TRAFFIC_FILE):
@@ -173,9 +173,10 @@ def recorded_traffic(workload: str):
             vals[k.strip()] = v.strip()
     src = os.path.join(ROOT, "drafting_pd_expand_amd", "csrc", "gemm.hip")
     digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if vals.get("gemm_source_sha256_16") != digest or "traffic_bytes_per_launch" not in vals:
+    key = f"traffic_bytes_per_launch_{workload}"
+    if vals.get("gemm_source_sha256_16") != digest or key not in vals:
         return None
-    return float(vals["traffic_bytes_per_launch"])
+    return float(vals[key])
 
 
 def ar_baseline(pdx, mdev, b, w, inp, cache, par_draft, stream, steps: int) -> dict:
@@ -433,7 +434,8 @@ def yardsticks() -> dict:
     streaming read (sum of a 2 GiB bf16 tensor, fp32 accumulation in torch),
     a device-to-device copy of 1 GiB, and torch.matmul in bf16 (the installed
     vendor GEMM) at the C = 64, K = 7 LM-head shape (448 x 2880 by
-    2880 x 201088) and at a large square shape."""
+    2880 x 201088), at the two largest projection shapes of that step (896
+    rows: gate and up together, and down) and at a large square shape."""
     import torch
     dev = torch.device("cuda:0")
     out = {}
@@ -458,7 +460,8 @@ def yardsticks() -> dict:
     t = timed(lambda: b.copy_(a), 10)
     out["copy_GBps_read_plus_write"] = 2 * a.numel() * 4 / t / 1e9
     del a, b
-    for name, (M, K, N) in (("lm_head_c64_k7", (448, 2880, 201088)), ("square_8192", (8192, 8192, 8192))):
+    for name, (M, K, N) in (("lm_head_c64_k7", (448, 2880, 201088)), ("gate_up_c64_k7", (896, 2880, 15360)),
+                            ("down_c64_k7", (896, 7680, 2880)), ("square_8192", (8192, 8192, 8192))):
         A = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
         B = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
         t = timed(lambda: torch.matmul(A, B), 10)
@@ -469,6 +472,7 @@ def yardsticks() -> dict:
     torch.cuda.empty_cache()
     log(f"[bench] yardsticks: read {out['stream_read_GBps']:.0f} GB/s, copy {out['copy_GBps_read_plus_write']:.0f} "
         f"GB/s, matmul LM head {out['matmul_bf16_lm_head_c64_k7']['TFLOPs']:.0f} TFLOP/s, "
+        f"gate/up {out['matmul_bf16_gate_up_c64_k7']['TFLOPs']:.0f}, down {out['matmul_bf16_down_c64_k7']['TFLOPs']:.0f}, "
         f"8192^3 {out['matmul_bf16_square_8192']['TFLOPs']:.0f} TFLOP/s")
     return out
 
@@ -586,8 +590,9 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
         roof = {"bound": "hbm", "kernel": "decode_kernel (persistent: the whole drafter pass in one launch)",
                 "achieved": fb / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": fb}
     elif dom == "lm_head":
-        if R <= 64:   # weight-streaming ring kernel: HBM-bound
-            roof = {"bound": "hbm", "kernel": "gemm_ring_kernel<ARGMAX> (LM head + fused argmax)",
+        if R <= 128:   # weight-streaming ring kernel (R flop per weight byte, below the ridge): HBM-bound
+            kname = "gemm_ring_kernel<ARGMAX>" if R <= 64 else "gemm_ring_kernel<ARGMAX, 8 X tiles>"
+            roof = {"bound": "hbm", "kernel": f"{kname} (LM head + fused argmax)",
                     "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
         else:         # many rows: MFMA-bound
             kname = ("gemm_tiled_kernel<ARGMAX>" if R < 256 else
@@ -598,7 +603,7 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
         roof = {"bound": "hbm", "kernel": f"attn_split_kernel<{dm.dh}> (paged split-KV attention)",
                 "achieved": attn_bytes(dm, b, w.K) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(workload) if dom == "lm_head" and R <= 64 else None
+    roof["traffic"] = recorded_traffic(workload) if dom == "lm_head" else None
     roof["us_per_launch"] = k_avg_s * 1e6
     sb = step_bytes(dm, b, w.K)
     v = b["num_tokens"] - b["num_rejected"]
