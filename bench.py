@@ -460,15 +460,18 @@ def yardsticks() -> dict:
     t = timed(lambda: b.copy_(a), 10)
     out["copy_GBps_read_plus_write"] = 2 * a.numel() * 4 / t / 1e9
     del a, b
+    # the drafter's layout: weights row-major [N][K] (out x in), Y = X W^T
+    # (a 2-D product with a transposed-view right operand: one library call,
+    # no copy)
     for name, (M, K, N) in (("lm_head_c64_k7", (448, 2880, 201088)), ("gate_up_c64_k7", (896, 2880, 15360)),
                             ("down_c64_k7", (896, 7680, 2880)), ("square_8192", (8192, 8192, 8192))):
         A = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
-        B = torch.randn(K, N, dtype=torch.bfloat16, device=dev)
-        t = timed(lambda: torch.matmul(A, B), 10)
-        out[f"matmul_bf16_{name}"] = {"shape_MKN": [M, K, N], "us": t * 1e6,
+        W = torch.randn(N, K, dtype=torch.bfloat16, device=dev)
+        t = timed(lambda: torch.matmul(A, W.t()), 10)
+        out[f"matmul_bf16_{name}"] = {"shape_MKN": [M, K, N], "layout": "X[M][K] @ W[N][K]^T", "us": t * 1e6,
                                       "TFLOPs": 2.0 * M * N * K / t / 1e12,
                                       "frac_of_2500": 2.0 * M * N * K / t / 1e12 / BF16_PEAK_TFLOPS}
-        del A, B
+        del A, W
     torch.cuda.empty_cache()
     log(f"[bench] yardsticks: read {out['stream_read_GBps']:.0f} GB/s, copy {out['copy_GBps_read_plus_write']:.0f} "
         f"GB/s, matmul LM head {out['matmul_bf16_lm_head_c64_k7']['TFLOPs']:.0f} TFLOP/s, "
