@@ -110,11 +110,23 @@ struct Timed {
 
 struct Layout {
     size_t sync, x, u, q, ao, act, ws, po, pml, plan, xg, amv, ami, total;
+    // row compaction (compact): gathered hidden rows, ids, positions, slots,
+    // row map, request starts, sampled-row indices, {kept rows, split count}
+    size_t hid_c, ids_c, pos_c, slot_c, rowmap, cu_c, nti_c, cnt;
+    bool compact;
     int T, R, ntilesV;   // ntilesV: argmax partials per row of the LM-head GEMM kernel
     int amax_cap;        // partials per row the scratch holds (also the decode pass's)
     AttnSplit sp;
     DecodePlan dp;   // the persistent decode pass, when it applies (dp.ok)
 };
+
+// Passes of more than 64 rows compute only their rows that are not rejected
+// (gathered to the front by a compaction launch, counted on the device);
+// PD_COMPACT=0 in the environment computes every row instead.
+bool compact_enabled() {
+    const char* e = std::getenv("PD_COMPACT");
+    return !(e && e[0] == '0');
+}
 
 // The persistent decode kernel serves passes of up to 64 rows when the
 // environment sets PD_DECODE=1; otherwise every pass runs as separate
@@ -128,7 +140,8 @@ bool decode_enabled() {
 // scap) shrink until the whole layout fits in `limit` bytes; fewer splits per
 // request only make the device plan pick longer splits. L.total > limit when
 // even the fewest splits the block table needs do not fit.
-Layout plan_layout(const pd_model* m, const pd_batch_dims* d, bool fp8, size_t limit = 0) {
+// hidden_d: the caller gives the projected hidden rows (no fc projection).
+Layout plan_layout(const pd_model* m, const pd_batch_dims* d, bool fp8, bool hidden_d, size_t limit = 0) {
     Layout L;
     const int T = d->T_in + d->C * (d->K - 1);
     const int R = d->C * d->K;
@@ -137,16 +150,21 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d, bool fp8, size_t l
     const int qkvw = (m->Hq + 2 * m->Hkv) * m->dh;
     const int hd = m->Hq * m->dh;
     L.sp = plan_attn_split(d->C, T, m->Hq, m->Hkv, m->dh, d->max_blocks);
+    L.compact = compact_enabled() && T > 64 && T <= kCompactMaxRows && !hidden_d;
     size_t ws = 0;
     auto need = [&](int M, int N, int K) {
-        GemmPlan p = plan_gemm(M, N, K, EPI_PARTIAL);
+        GemmPlan p = plan_gemm(M, N, K, EPI_PARTIAL, L.compact);
         ws = std::max(ws, gemm_ws_floats(p, M, N, EPI_PARTIAL));
     };
-    need(T, m->d, m->hidden3);
-    need(T, qkvw, 2 * m->d);
-    need(T, qkvw, m->d);
-    need(T, m->d, hd);
-    need(T, m->d, m->F);
+    auto need_all = [&]() {
+        ws = 0;
+        need(T, m->d, m->hidden3);
+        need(T, qkvw, 2 * m->d);
+        need(T, qkvw, m->d);
+        need(T, m->d, hd);
+        need(T, m->d, m->F);
+    };
+    need_all();
     L.ntilesV = plan_gemm(R, m->V, m->d, EPI_ARGMAX).ntiles;
     L.amax_cap = L.ntilesV;
     L.dp = plan_decode(*m, T, R, fp8);
@@ -177,9 +195,24 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d, bool fp8, size_t l
         L.xg = carve((size_t)R * m->d * 2);
         L.amv = carve((size_t)R * L.amax_cap * 4);
         L.ami = carve((size_t)R * L.amax_cap * 4);
+        const int tc = L.compact ? T : 0;
+        L.hid_c = carve((size_t)tc * m->hidden3 * 2);
+        L.ids_c = carve((size_t)tc * 4);
+        L.pos_c = carve((size_t)tc * 4);
+        L.slot_c = carve((size_t)tc * 4);
+        L.rowmap = carve((size_t)tc * 4);
+        L.cu_c = carve(L.compact ? (size_t)(d->C + 1) * 4 : 0);
+        L.nti_c = carve(L.compact ? (size_t)R * 4 : 0);
+        L.cnt = carve(L.compact ? 2 * 4 : 0);
         L.total = off;
     };
     carve_all();
+    if (limit && L.total > limit && L.compact) {   // the bounded scratch: every row computed
+        L.compact = false;
+        need_all();
+        if (L.dp.ok) ws = std::max(ws, L.dp.ws_floats);
+        carve_all();
+    }
     if (limit && L.total > limit) {
         const size_t per_split = align256((size_t)T * hd * 4) + align256((size_t)T * m->Hq * 2 * 4);
         const size_t fixed = L.total - (size_t)L.sp.scap * per_split;   // upper bound: alignment slack
@@ -304,13 +337,25 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
     const size_t plane = (size_t)dims->num_blocks * m->Hkv * PD_PAGE * m->dh * (fp8 ? 1 : 2);
 
     // one projection; returns its split count through *splits (EPI_PARTIAL)
+    // compacted pass: the kept-row count and the split count of the latest
+    // projection, both on the device
+    int32_t* cnt = L.compact ? (int32_t*)(S + L.cnt) : nullptr;
+    int32_t* t_dev = cnt;
+    int32_t* s_dev = cnt ? cnt + 1 : nullptr;
+    // one projection; returns its split count through *splits (EPI_PARTIAL;
+    // with device row counts the most planes, the count itself in s_dev)
     auto gemm = [&](int cls, int epi, const uint16_t* X, int ldx, const int32_t* xrows,
                     int xlimit, const uint16_t* W, const uint16_t* W2, int M, int N, int K,
-                    uint16_t* yb, int ldyb, int* splits) -> int {
-        GemmPlan p = plan_gemm(M, N, K, epi);
+                    uint16_t* yb, int ldyb, int* splits, bool dev_rows = false) -> int {
+        dev_rows = dev_rows && L.compact;
+        GemmPlan p = plan_gemm(M, N, K, epi, dev_rows);
         if (splits) *splits = p.splits;
         GemmArgs a;
         std::memset(&a, 0, sizeof(a));
+        if (dev_rows) {
+            a.m_dev = t_dev;
+            if (epi == EPI_PARTIAL) a.splits_out = s_dev;
+        }
         a.X = X; a.ldx = ldx; a.xrows = xrows; a.xrows_limit = xlimit;
         a.W = W; a.W2 = W2; a.M = M; a.N = N; a.K = K;
         a.ws = ws; a.yb = yb; a.ldyb = ldyb;
@@ -322,6 +367,11 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
     };
     auto dbg = [&](int slot) -> int {
         if (!h || !h->dbg) return PD_OK;
+        if (L.compact) {   // compacted rows back to their places (rejected rows are left as they are)
+            Timed t(h, PD_KERNEL_OTHER, s);
+            return launch_scatter_rows(x, h->dbg + (size_t)slot * T * d, (const int32_t*)(S + L.rowmap), t_dev,
+                                       T, d, s);
+        }
         return hipMemcpyAsync(h->dbg + (size_t)slot * T * d, x, (size_t)T * d * 4,
                               hipMemcpyDeviceToDevice, s) == hipSuccess ? PD_OK : PD_EHIP;
     };
@@ -386,30 +436,56 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
         return launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV, draft_ids, st, s);
     }
 
+    // Row compaction: the rows that are not rejected, in order, at the front
+    // of every row buffer; the projections and row kernels stop at their
+    // count (t_dev), attention sees the compacted request starts and no
+    // rejected rows, and the LM head's sampled rows are renumbered.
+    const uint16_t* hid = b->hidden;
+    const int32_t* ids = b->input_ids;
+    const int32_t* pos = b->positions;
+    const int32_t* slots = b->slot_mapping;
+    const int32_t* nti = b->new_token_indices;
+    if (L.compact) {
+        int32_t* cu_c = (int32_t*)(S + L.cu_c);
+        int32_t* nti_c = (int32_t*)(S + L.nti_c);
+        uint16_t* hid_c = (uint16_t*)(S + L.hid_c);
+        int32_t* ids_c = (int32_t*)(S + L.ids_c);
+        int32_t* pos_c = (int32_t*)(S + L.pos_c);
+        int32_t* slot_c = (int32_t*)(S + L.slot_c);
+        {
+            Timed t(h, PD_KERNEL_OTHER, s);
+            PD_TRY(launch_compact_rows(b->is_rejected, b->input_ids, b->positions, b->slot_mapping, b->cu_out,
+                                       b->new_token_indices, b->hidden, T, dims->C, R, m->hidden3, hid_c, ids_c,
+                                       pos_c, slot_c, cu_c, nti_c, (int32_t*)(S + L.rowmap), t_dev, st, s));
+        }
+        hid = hid_c; ids = ids_c; pos = pos_c; slots = slot_c; nti = nti_c;
+        aa.positions = pos_c;
+        aa.is_rejected = nullptr;
+        aa.cu_out = cu_c;
+    }
     // fc projection 3d -> d (starts the residual stream; skipped when the
     // projected rows are given), then the layer-0 input
     if (!hidden_d)
-        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, b->hidden, m->hidden3, nullptr, 0, m->fc, nullptr, T,
-                    d, m->hidden3, nullptr, 0, &sp));
+        PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, hid, m->hidden3, nullptr, 0, m->fc, nullptr, T,
+                    d, m->hidden3, nullptr, 0, &sp, true));
     {
         Timed t(h, PD_KERNEL_OTHER, s);
         // the attention split plan runs as one more workgroup of this launch
-        PD_TRY(launch_layer0_input(hidden_d, ws, sp, b->input_ids, m->embed, m->V, x, m->norm_emb,
-                                   m->norm_hid, u, T, d, m->rms_eps, st, s, &aa));
+        PD_TRY(launch_layer0_input(hidden_d, ws, sp, ids, m->embed, m->V, x, m->norm_emb,
+                                   m->norm_hid, u, T, d, m->rms_eps, st, s, &aa, t_dev, s_dev));
     }
     PD_TRY(dbg(0));
     for (int l = 0; l < m->N; ++l) {
         const int in_l = (l == 0) ? 2 * d : d;
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, u, in_l, nullptr, 0, m->w_qkv[l], nullptr, T, qkvw,
-                    in_l, nullptr, 0, &sp));
+                    in_l, nullptr, 0, &sp, true));
         char* kpl = reinterpret_cast<char*>(kv_cache) + (size_t)(2 * l) * plane;
         char* vpl = reinterpret_cast<char*>(kv_cache) + (size_t)(2 * l + 1) * plane;
         const float ks = kv_scales ? kv_scales[2 * l] : 1.0f, vs = kv_scales ? kv_scales[2 * l + 1] : 1.0f;
         {
             Timed t(h, PD_KERNEL_OTHER, s);
-            PD_TRY(launch_rope_cache(ws, sp, b->positions, b->slot_mapping, T, m->Hq, m->Hkv, m->dh,
-                                     m->rope_theta, q, kpl, vpl, dims->num_blocks, st, s, fp8 ? 1 : 0, ks,
-                                     vs));
+            PD_TRY(launch_rope_cache(ws, sp, pos, slots, T, m->Hq, m->Hkv, m->dh, m->rope_theta, q, kpl, vpl,
+                                     dims->num_blocks, st, s, fp8 ? 1 : 0, ks, vs, t_dev, s_dev));
         }
         aa.q = q; aa.kplane = kpl; aa.vplane = vpl;
         aa.fp8 = fp8; aa.k_scale = ks; aa.v_scale = vs;
@@ -423,35 +499,38 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
             if (rc != PD_OK) return rc;
         }
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, ao, hd, nullptr, 0, m->w_o[l], nullptr, T, d, hd,
-                    nullptr, 0, &sp));
+                    nullptr, 0, &sp, true));
         {
             Timed t(h, PD_KERNEL_OTHER, s);
-            PD_TRY(launch_resid_norm(ws, sp, x, m->norm_post[l], u, T, d, m->rms_eps, s));
+            PD_TRY(launch_resid_norm(ws, sp, x, m->norm_post[l], u, T, d, m->rms_eps, s, nullptr, 0, nullptr,
+                                     nullptr, t_dev, s_dev));
         }
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_SWIGLU, u, d, nullptr, 0, m->w_gate[l], m->w_up[l], T, m->F,
-                    d, act, m->F, nullptr));
+                    d, act, m->F, nullptr, true));
         PD_TRY(gemm(PD_KERNEL_GEMM, EPI_PARTIAL, act, m->F, nullptr, 0, m->w_down[l], nullptr, T, d,
-                    m->F, nullptr, 0, &sp));
+                    m->F, nullptr, 0, &sp, true));
         {
             Timed t(h, PD_KERNEL_OTHER, s);
             if (l + 1 < m->N) {
                 // next layer's input norm
-                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_in[l + 1], u, T, d, m->rms_eps, s));
+                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_in[l + 1], u, T, d, m->rms_eps, s, nullptr, 0,
+                                         nullptr, nullptr, t_dev, s_dev));
             } else if (h && h->dbg) {
                 // the residual snapshot needs every row's final x
-                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, u, T, d, m->rms_eps, s));
+                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, u, T, d, m->rms_eps, s, nullptr, 0, nullptr,
+                                         nullptr, t_dev, s_dev));
             } else {
                 // final norm of the K sampled rows of every request, packed for the LM head
-                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, xg, T, d, m->rms_eps, s,
-                                         b->new_token_indices, R, st, hidden_out));
+                PD_TRY(launch_resid_norm(ws, sp, x, m->norm_final, xg, T, d, m->rms_eps, s, nti, R, st,
+                                         hidden_out, nullptr, s_dev));
             }
         }
         PD_TRY(dbg(l + 1));
     }
     if (h && h->dbg) {
         Timed t(h, PD_KERNEL_OTHER, s);
-        PD_TRY(launch_resid_norm(nullptr, 0, x, m->norm_final, xg, T, d, m->rms_eps, s,
-                                 b->new_token_indices, R, st, hidden_out));
+        PD_TRY(launch_resid_norm(nullptr, 0, x, m->norm_final, xg, T, d, m->rms_eps, s, nti, R, st,
+                                 hidden_out));
     }
     // LM head on the packed sampled rows, greedy argmax
     PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, xg, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
@@ -513,7 +592,7 @@ int pd_draft_forward_ex(pd_handle** hp, const pd_model* m, const pd_batch_dims* 
         if ((rc = create_handle(hp)) != PD_OK) return rc;
     }
     pd_handle* h = *hp;
-    const Layout L = plan_layout(m, dims, opts && opts->kv_fp8);
+    const Layout L = plan_layout(m, dims, opts && opts->kv_fp8, opts && opts->hidden_d);
     if ((rc = ensure_scratch(h, L.total, s)) != PD_OK) return rc;
     return forward_impl(h, h->scratch, L, h->status, m, dims, b, block_table, kv_cache, draft_ids, logits,
                         opts, s);
@@ -524,7 +603,7 @@ int pd_draft_forward_noalloc(const pd_model* m, const pd_batch_dims* dims, const
                              float* logits, const pd_forward_opts* opts, void* stream) {
     int rc = forward_args_ok(m, dims, b, block_table, kv_cache, draft_ids, opts);
     if (rc != PD_OK || dims->C == 0) return rc;
-    const Layout L = plan_layout(m, dims, opts && opts->kv_fp8, kStaticScratchBytes);
+    const Layout L = plan_layout(m, dims, opts && opts->kv_fp8, opts && opts->hidden_d, kStaticScratchBytes);
     if (L.total > kStaticScratchBytes) return PD_ESCRATCH;
     char* S = nullptr;
     if ((rc = static_scratch(&S)) != PD_OK) return rc;

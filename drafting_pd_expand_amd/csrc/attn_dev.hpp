@@ -221,7 +221,7 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
             qrow[tt] = row0 + (qok[tt] ? qi / G : 0);
             qh[tt] = g * G + (qok[tt] ? qi % G : 0);
             // row0 <= qrow < row1 <= T: both loads are in bounds for every lane
-            const bool rej = a.is_rejected[qrow[tt]] != 0;
+            const bool rej = a.is_rejected && a.is_rejected[qrow[tt]] != 0;   // (null: none rejected)
             const int pos = a.positions[qrow[tt]];
             qrej[tt] = !qok[tt] || rej;
             // keys this query may see: t <= lim (rejected / padding queries: no limit, not used)
@@ -503,7 +503,7 @@ __device__ __forceinline__ void attn_merge_wave(const AttnArgs& a, int pair0) {
     const bool inr = found && row < a.cu_out[r + 1];
     const int nsr = ldc<CG>(a.plan + kPlanNs + r);
     if (inr && nsr == 1) return;
-    const int ns = (inr && !a.is_rejected[row]) ? min(nsr, kMaxSplits) : 0;
+    const int ns = (inr && !(a.is_rejected && a.is_rejected[row])) ? min(nsr, kMaxSplits) : 0;
     const size_t stride = (size_t)a.T * a.Hq;   // between splits, in (row, head) units
     const size_t base0 = (size_t)row * a.Hq + h0;
     const int sub = lane / LPS, dq = lane % LPS;   // split within an instruction, dim quad

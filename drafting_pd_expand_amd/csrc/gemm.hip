@@ -837,13 +837,21 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     const int r16 = lane & 15, g4 = lane >> 4;
     const int wn = wave & 1, wm = wave >> 1;   // 2 column halves x (BT / 64) groups of 64 rows
 
-    const int mblocks = (a.M + BT - 1) / BT;
+    // rows present (a device count when given): only their row blocks are
+    // tiled, and the K split count is chosen here for that many tiles
+    const int meff = a.m_dev ? min(a.M, max(0, *a.m_dev)) : a.M;
+    const int mblocks = (meff + BT - 1) / BT;
     const int ntn = (a.N + COLS - 1) / COLS;
     const int tiles = ntn * mblocks;
     const int ksteps = (a.K + kBS - 1) / kBS;
-    const int per = (ksteps + a.splits - 1) / a.splits;
-    const int nitems = tiles * a.splits;
     const int G = gridDim.x;
+    int splits = a.splits;
+    if constexpr (EPI == EPI_PARTIAL) {
+        if (a.m_dev) splits = big_splits(tiles, ksteps, G, a.splits);
+        if (a.splits_out && blockIdx.x == 0 && threadIdx.x == 0) a.splits_out[0] = splits;
+    }
+    const int per = (ksteps + splits - 1) / splits;
+    const int nitems = tiles * splits;
     // workgroups go round-robin to the 8 XCDs: XCD x holds blocks x, x+8, ...;
     // give it a contiguous run of item positions (any G: the first G % 8
     // XCDs hold one block more)
@@ -893,7 +901,7 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
                 rsrc[j] = ok ? base + (size_t)n * a.K + ch[j] : zp;
             } else {
                 const int m = m0 + rowrel[j];
-                const bool ok = m < a.M;
+                const bool ok = m < meff;
                 kmask[j] = ok ? ~0u : 0u;
                 rsrc[j] = ok ? a.X + (size_t)m * a.ldx + ch[j] : zp;
             }
@@ -1006,7 +1014,7 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int m = m0 + 64 * wm + 16 * j + r16;
-                if (m >= a.M) continue;
+                if (m >= meff) continue;
                 if constexpr (EPI == EPI_PARTIAL) {
 #pragma unroll
                     for (int i = 0; i < NA; ++i) {
@@ -1155,7 +1163,8 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
         case GEMM_RING: return launch_ring<EPI>(p, a, s);
         case GEMM_WRING: return launch_wring<EPI>(p, a, s);
         case GEMM_TILED: return launch_tiled<EPI>(p, a, s);
-        default: return launch_big<EPI>(p, a, s);
+        case GEMM_BIG: return launch_big<EPI>(p, a, s);
+        default: return PD_EINVAL;
     }
 }
 
@@ -1206,15 +1215,7 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
         const int ntn = (N + cols - 1) / cols;
         const long tiles = (long)ntn * p.mblocks;
         const int ksteps = (K + kBS - 1) / kBS;
-        if (epi == EPI_PARTIAL) {
-            long best = -1;
-            for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
-                const int per = (ksteps + sp - 1) / sp;
-                if ((sp - 1) * per >= ksteps) continue;
-                const long span = ((tiles * sp + cap - 1) / cap) * per;
-                if (best < 0 || span < best) { best = span; p.splits = sp; }
-            }
-        }
+        if (epi == EPI_PARTIAL) p.splits = big_splits(tiles, ksteps, cap, 8);
         p.ntiles = ntn;
         const long items = tiles * p.splits;
         p.grid = (int)(items < cap ? items : cap);
@@ -1317,7 +1318,20 @@ static GemmPlan plan_wring(int N, int K, int epi) {
     return p;
 }
 
-GemmPlan plan_gemm(int M, int N, int K, int epi) {
+GemmPlan plan_gemm(int M, int N, int K, int epi, bool rows_on_device) {
+    if (rows_on_device) {
+        // the many-row kernel picks its K splits on the device (at most 8
+        // planes, or one per K step); the grid covers every resident slot
+        GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
+        if (p.kind != GEMM_BIG || epi == EPI_ARGMAX) { p.kind = -1; return p; }
+        const int bt = p.wn * 32;
+        const long cap = bt == kBT ? 256 : 512;
+        const int ksteps = (K + kBS - 1) / kBS;
+        p.splits = epi == EPI_PARTIAL ? (ksteps < 8 ? ksteps : 8) : 1;
+        const long items = (long)p.ntiles * p.mblocks * p.splits;
+        p.grid = (int)(items < cap ? items : cap);
+        return p;
+    }
     // (the weight-only ring addresses a matrix with 32-bit byte offsets)
     if (M > 16 && M <= 64 && epi != EPI_ARGMAX && (long long)N * K * 2 < (1LL << 31)) return plan_wring(N, K, epi);
     const GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
@@ -1333,6 +1347,8 @@ size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi) {
 }
 
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s) {
+    // device row counts: many-row kernel only, not with the max/argmax epilogue
+    if ((a.m_dev || a.splits_out) && (p.kind != GEMM_BIG || epi == EPI_ARGMAX)) return PD_EINVAL;
     a.splits = p.splits;
     a.ntiles = p.ntiles;
     switch (epi) {

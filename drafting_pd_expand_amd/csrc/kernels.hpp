@@ -43,6 +43,13 @@ struct GemmArgs {
     float* logits; int ldlog;
     float* amax_v; int* amax_i; int ntiles;
     int32_t* status;
+    // Optional, many-row kernel only (plan_gemm with rows_on_device): m_dev[0]
+    // = rows present (<= M), read on the device; only their row blocks are
+    // computed, and (EPI_PARTIAL) the K split count is chosen there for
+    // those blocks, at most `splits`, and written to splits_out[0] for the
+    // consumer of the planes.
+    const int32_t* m_dev;
+    int32_t* splits_out;
 };
 
 enum GemmKind : int {
@@ -64,7 +71,23 @@ struct GemmPlan {
     int krs;       // ring: reduction elements per stage (128, or 64 with 8 X tiles)
 };
 
-GemmPlan plan_gemm(int M, int N, int K, int epi);
+// rows_on_device: the rows present are counted on the device (GemmArgs::m_dev,
+// M > 64, not EPI_ARGMAX); `splits` is then the most planes the kernel may
+// write and `grid` covers that many.
+GemmPlan plan_gemm(int M, int N, int K, int epi, bool rows_on_device = false);
+// K splits of the many-row kernel: the count (<= smax) that minimises the K
+// steps of the busiest of `slots` resident workgroups over `tiles` tiles
+__host__ __device__ inline int big_splits(long tiles, int ksteps, long slots, int smax) {
+    int best_sp = 1;
+    long best = -1;
+    for (int sp = 1; sp <= smax && sp <= ksteps; ++sp) {
+        const int per = (ksteps + sp - 1) / sp;
+        if ((sp - 1) * per >= ksteps) continue;   // no empty split
+        const long span = ((tiles * sp + slots - 1) / slots) * per;
+        if (best < 0 || span < best) { best = span; best_sp = sp; }
+    }
+    return best_sp;
+}
 GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm);
 size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi);
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
@@ -76,20 +99,45 @@ int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 // plan != nullptr: the attention split plan (launch_attn_plan's work) runs as
 // one more workgroup of the same launch.
 struct AttnArgs;
+// t_dev (all row kernels, optional): rows present, on the device (<= T); rows
+// at or past it are skipped. s_dev (optional): the split-plane count, on the
+// device (written by a projection that chose it there), in place of S.
 int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32_t* ids,
                         const uint16_t* embed, int V, float* x, const uint16_t* g_emb,
                         const uint16_t* g_hid, uint16_t* u, int T, int d, float eps,
-                        int32_t* status, hipStream_t s, const AttnArgs* plan = nullptr);
+                        int32_t* status, hipStream_t s, const AttnArgs* plan = nullptr,
+                        const int32_t* t_dev = nullptr, const int32_t* s_dev = nullptr);
 // rows != nullptr: output row o = norm of row rows[o] (o < nrows), x untouched;
 // xout (row-list mode) also gets the bf16 residual row itself.
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
                       int d, float eps, hipStream_t s, const int32_t* rows = nullptr, int nrows = 0,
-                      int32_t* status = nullptr, uint16_t* xout = nullptr);
+                      int32_t* status = nullptr, uint16_t* xout = nullptr, const int32_t* t_dev = nullptr,
+                      const int32_t* s_dev = nullptr);
 // fp8: the planes hold E4M3 codes of value / k_scale (K) and value / v_scale (V)
 int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
                       int Hq, int Hkv, int dh, float theta, uint16_t* q_out, void* kplane,
                       void* vplane, int num_blocks, int32_t* status, hipStream_t s, int fp8 = 0,
-                      float k_scale = 1.0f, float v_scale = 1.0f);
+                      float k_scale = 1.0f, float v_scale = 1.0f, const int32_t* t_dev = nullptr,
+                      const int32_t* s_dev = nullptr);
+
+// Row compaction of a many-row pass: the rows that are not rejected, in
+// order, get consecutive indices c = (kept rows before them). Gathers their
+// hidden rows (bf16 [T][h3] -> hid_c), token ids, positions and slots, and
+// writes rowmap[c] = original row, the compacted request starts cu_c[0..C],
+// the compacted indices of the sampled rows nti_c[0..R) and the kept count
+// t_eff[0]. A sampled row outside [0, T), and request starts outside
+// [0, T] or decreasing, are flagged (PD_STATUS_BAD_ROW); a sampled row that
+// is outside [0, T) or rejected (a padding request's) maps to 0.
+// T <= kCompactMaxRows.
+constexpr int kCompactMaxRows = 4096;
+int launch_compact_rows(const uint8_t* is_rejected, const int32_t* ids, const int32_t* positions,
+                        const int32_t* slots, const int32_t* cu_out, const int32_t* nti,
+                        const uint16_t* hidden, int T, int C, int R, int h3, uint16_t* hid_c,
+                        int32_t* ids_c, int32_t* pos_c, int32_t* slot_c, int32_t* cu_c, int32_t* nti_c,
+                        int32_t* rowmap, int32_t* t_eff, int32_t* status, hipStream_t s);
+// dst[rowmap[c]] = src[c] for c < t_eff[0] (fp32 rows of d; residual snapshots)
+int launch_scatter_rows(const float* src, float* dst, const int32_t* rowmap, const int32_t* t_eff, int T, int d,
+                        hipStream_t s);
 int launch_argmax_reduce(const float* amax_v, const int* amax_i, int M, int ntiles, int32_t* out,
                          int32_t* status, hipStream_t s);
 
@@ -128,7 +176,7 @@ struct AttnArgs {
     const void* kplane;           // this layer's K plane [num_blocks][Hkv][16][dh] (bf16 or fp8 codes)
     const void* vplane;           // this layer's V plane [num_blocks][Hkv][dh][16]
     const int32_t* positions;
-    const uint8_t* is_rejected;
+    const uint8_t* is_rejected;   // may be null: no row rejected (compacted rows)
     const int32_t* cu_out;        // [C+1]
     const int32_t* seq_lens;      // [C]
     const int32_t* block_table;   // [C][max_blocks]

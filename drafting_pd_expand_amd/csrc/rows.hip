@@ -69,9 +69,12 @@ template <int NC>
 __global__ __launch_bounds__(256) void resid_norm_kernel(const float* ws, int S, float* x,
                                                          const uint16_t* gamma, uint16_t* y, int T,
                                                          int d, float eps, const int32_t* rows,
-                                                         int32_t* status, uint16_t* xout) {
+                                                         int32_t* status, uint16_t* xout, const int32_t* t_dev,
+                                                         const int32_t* s_dev) {
     __shared__ float red[4];
     const int o = blockIdx.x;
+    if (!rows && t_dev && o >= *t_dev) return;   // past the rows present (whole workgroup)
+    if (s_dev) S = *s_dev;                       // planes the projection chose on the device
     int i = o;
     bool ok = true;
     if (rows) {
@@ -120,13 +123,16 @@ __global__ __launch_bounds__(256) void layer0_input_kernel(const float* ws, int 
                                                            const uint16_t* g_emb,
                                                            const uint16_t* g_hid, uint16_t* u, int T,
                                                            int d, float eps, int32_t* status,
-                                                           const uint16_t* xin, AttnArgs plan, int with_plan) {
+                                                           const uint16_t* xin, AttnArgs plan, int with_plan,
+                                                           const int32_t* t_dev, const int32_t* s_dev) {
     __shared__ float red[4];
     if (with_plan && blockIdx.x == 0) {   // the attention split plan, beside the rows
         attn_plan_block(plan);
         return;
     }
     const int o = blockIdx.x - with_plan;
+    if (t_dev && o >= *t_dev) return;   // past the rows present (whole workgroup)
+    if (s_dev) S = *s_dev;
     int id = ids[o];
     if (id < 0 || id >= V) {
         if (threadIdx.x == 0) flag(status, PD_STATUS_BAD_TOKEN);
@@ -214,8 +220,11 @@ __global__ __launch_bounds__(256) void rope_cache_kernel(const float* ws, int S,
                                                          int dh, double inv_step, uint16_t* q_out,
                                                          void* kplane, void* vplane,
                                                          int num_blocks, int32_t* status, int fp8,
-                                                         float k_scale, float v_scale) {
+                                                         float k_scale, float v_scale, const int32_t* t_dev,
+                                                         const int32_t* s_dev) {
     const int o = blockIdx.y;
+    if (t_dev && o >= *t_dev) return;   // past the rows present (whole workgroup)
+    if (s_dev) S = *s_dev;
     const int half = dh / 2;
     const int npairs = (Hq + Hkv) * half;          // rotated pairs (q heads, then k heads)
     const int item = blockIdx.x * 256 + threadIdx.x;
@@ -325,6 +334,88 @@ __global__ __launch_bounds__(1024) void argmax_reduce_kernel(const float* amax_v
     }
 }
 
+// Row compaction (see launch_compact_rows). Workgroup 0: the kept-row
+// prefix over all T rows (each thread a run of ceil(T / 256) rows, one block
+// scan), then the compacted request starts, sampled-row indices and the kept
+// count. Workgroup 1 + i: row i, if kept: its index (the kept rows before it,
+// counted by the whole block), metadata and hidden-row copy (16-byte loads).
+__global__ __launch_bounds__(256) void compact_rows_kernel(
+    const uint8_t* is_rejected, const int32_t* ids, const int32_t* positions, const int32_t* slots,
+    const int32_t* cu_out, const int32_t* nti, const uint16_t* hidden, int T, int C, int R, int h3,
+    uint16_t* hid_c, int32_t* ids_c, int32_t* pos_c, int32_t* slot_c, int32_t* cu_c, int32_t* nti_c,
+    int32_t* rowmap, int32_t* t_eff, int32_t* status) {
+    __shared__ int s_pre[kCompactMaxRows + 1];
+    __shared__ int s_w[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (blockIdx.x == 0) {
+        const int per = (T + 255) / 256;
+        const int r0 = min(T, tid * per), r1 = min(T, r0 + per);
+        int cnt = 0;
+        for (int i = r0; i < r1; ++i) cnt += is_rejected[i] == 0;
+        // exclusive prefix of the per-thread counts over the block
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) s_w[w] = incl;
+        __syncthreads();
+        int run = incl - cnt;
+        for (int k = 0; k < w; ++k) run += s_w[k];
+        for (int i = r0; i < r1; ++i) {
+            s_pre[i] = run;
+            run += is_rejected[i] == 0;
+        }
+        if (tid == 255) s_pre[T] = run;   // (the last thread's run ends at T: per * 256 >= T)
+        __syncthreads();
+        if (tid == 0) t_eff[0] = s_pre[T];
+        for (int r = tid; r <= C; r += 256) {
+            const int c0 = cu_out[r];
+            // request starts as the attention plan checks them: 0 <= start <= T, non-decreasing
+            if (c0 < 0 || c0 > T || (r < C && cu_out[r + 1] < c0)) flag(status, PD_STATUS_BAD_ROW);
+            cu_c[r] = s_pre[min(max(c0, 0), T)];
+        }
+        for (int j = tid; j < R; j += 256) {
+            const int row = nti[j];
+            const bool ok = row >= 0 && row < T;
+            if (!ok) flag(status, PD_STATUS_BAD_ROW);
+            // a rejected sampled row (a padding request's) has no defined
+            // draft: it takes compacted row 0
+            nti_c[j] = (ok && is_rejected[row] == 0) ? s_pre[row] : 0;
+        }
+        return;
+    }
+    const int i = blockIdx.x - 1;
+    if (is_rejected[i] != 0) return;   // whole workgroup
+    int cnt = 0;
+    for (int j = tid; j < i; j += 256) cnt += is_rejected[j] == 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, kWave);
+    if (lane == 0) s_w[w] = cnt;
+    __syncthreads();
+    const int c = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    if (tid == 0) {
+        rowmap[c] = i;
+        ids_c[c] = ids[i];
+        pos_c[c] = positions[i];
+        slot_c[c] = slots[i];
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(hidden + (size_t)i * h3);
+    uint4* dst = reinterpret_cast<uint4*>(hid_c + (size_t)c * h3);
+    for (int k = tid; k < h3 / 8; k += 256) dst[k] = src[k];
+}
+
+// dst[rowmap[c]] = src[c], c < t_eff (one workgroup per compacted row)
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float* src, float* dst, const int32_t* rowmap,
+                                                           const int32_t* t_eff, int T, int d) {
+    const int c = blockIdx.x;
+    if (c >= t_eff[0]) return;
+    const int i = rowmap[c];
+    if (i < 0 || i >= T) return;
+    for (int k = threadIdx.x; k < d; k += 256) dst[(size_t)i * d + k] = src[(size_t)c * d + k];
+}
+
 }  // namespace
 
 #define PD_ROW_NC(d, launch) \
@@ -338,12 +429,12 @@ __global__ __launch_bounds__(1024) void argmax_reduce_kernel(const float* amax_v
 
 int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, uint16_t* y, int T,
                       int d, float eps, hipStream_t s, const int32_t* rows, int nrows, int32_t* status,
-                      uint16_t* xout) {
+                      uint16_t* xout, const int32_t* t_dev, const int32_t* s_dev) {
     const int nout = rows ? nrows : T;
     if (nout <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
 #define L_(NC) hipLaunchKernelGGL(resid_norm_kernel<NC>, dim3(nout), dim3(256), 0, s, ws, S, x, gamma, y, T, d, \
-                                  eps, rows, status, xout)
+                                  eps, rows, status, xout, t_dev, s_dev)
     PD_ROW_NC(d, L_)
 #undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
@@ -351,7 +442,8 @@ int launch_resid_norm(const float* ws, int S, float* x, const uint16_t* gamma, u
 
 int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32_t* ids, const uint16_t* embed, int V,
                         float* x, const uint16_t* g_emb, const uint16_t* g_hid, uint16_t* u, int T,
-                        int d, float eps, int32_t* status, hipStream_t s, const AttnArgs* plan) {
+                        int d, float eps, int32_t* status, hipStream_t s, const AttnArgs* plan,
+                        const int32_t* t_dev, const int32_t* s_dev) {
     if (T <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
     AttnArgs pa;
@@ -359,7 +451,7 @@ int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32
     else std::memset(&pa, 0, sizeof(pa));
     const int wp = (plan && plan->C > 0) ? 1 : 0;
 #define L_(NC) hipLaunchKernelGGL(layer0_input_kernel<NC>, dim3(T + wp), dim3(256), 0, s, ws, S, ids, embed, V, \
-                                  x, g_emb, g_hid, u, T, d, eps, status, xin, pa, wp)
+                                  x, g_emb, g_hid, u, T, d, eps, status, xin, pa, wp, t_dev, s_dev)
     PD_ROW_NC(d, L_)
 #undef L_
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
@@ -368,14 +460,34 @@ int launch_layer0_input(const uint16_t* xin, const float* ws, int S, const int32
 int launch_rope_cache(const float* ws, int S, const int32_t* positions, const int32_t* slots, int T,
                       int Hq, int Hkv, int dh, float theta, uint16_t* q_out, void* kplane,
                       void* vplane, int num_blocks, int32_t* status, hipStream_t s, int fp8,
-                      float k_scale, float v_scale) {
+                      float k_scale, float v_scale, const int32_t* t_dev, const int32_t* s_dev) {
     if (T <= 0) return PD_OK;
     if (S > kMaxSplits) return PD_EINVAL;
     const int items = (Hq + Hkv) * (dh / 2) + Hkv * dh;
     const double inv_step = std::pow((double)theta, -2.0 / dh);
     hipLaunchKernelGGL(rope_cache_kernel, dim3((items + 255) / 256, T), dim3(256), 0, s, ws, S,
                        positions, slots, T, Hq, Hkv, dh, inv_step, q_out, kplane, vplane, num_blocks,
-                       status, fp8, k_scale, v_scale);
+                       status, fp8, k_scale, v_scale, t_dev, s_dev);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+int launch_compact_rows(const uint8_t* is_rejected, const int32_t* ids, const int32_t* positions,
+                        const int32_t* slots, const int32_t* cu_out, const int32_t* nti,
+                        const uint16_t* hidden, int T, int C, int R, int h3, uint16_t* hid_c,
+                        int32_t* ids_c, int32_t* pos_c, int32_t* slot_c, int32_t* cu_c, int32_t* nti_c,
+                        int32_t* rowmap, int32_t* t_eff, int32_t* status, hipStream_t s) {
+    if (T <= 0 || T > kCompactMaxRows || h3 % 8 || C < 0 || R < 0) return PD_EINVAL;
+    if (((uintptr_t)hidden | (uintptr_t)hid_c) & 15) return PD_EINVAL;   // 16-byte row copies
+    hipLaunchKernelGGL(compact_rows_kernel, dim3(T + 1), dim3(256), 0, s, is_rejected, ids, positions, slots,
+                       cu_out, nti, hidden, T, C, R, h3, hid_c, ids_c, pos_c, slot_c, cu_c, nti_c, rowmap,
+                       t_eff, status);
+    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
+}
+
+int launch_scatter_rows(const float* src, float* dst, const int32_t* rowmap, const int32_t* t_eff, int T, int d,
+                        hipStream_t s) {
+    if (T <= 0) return PD_OK;
+    hipLaunchKernelGGL(scatter_rows_kernel, dim3(T), dim3(256), 0, s, src, dst, rowmap, t_eff, T, d);
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 

@@ -80,6 +80,29 @@ def test_ragged_widths_all_rows(C, K, L):
     c.close()
 
 
+@pytest.mark.parametrize("C,K,L", [(48, 8, 90), (8, 8, 300)], ids=["rows768", "rows128"])
+def test_every_row_computed(C, K, L, monkeypatch):
+    """Passes of more than 64 rows normally compute only the rows that are
+    not rejected (gathered to the front on the device); with PD_COMPACT=0
+    every row is computed in place. Both are checked against the oracle, and
+    the sampled rows' logits of the two agree."""
+    w = synth.Workload(f"ragged-c{C}k{K}", RAGGED, C=C, K=K, context="fixed", L=L, seed=5 + C)
+    _say(f"[forward] {w.name} every row computed")
+    monkeypatch.setenv("PD_COMPACT", "0")
+    full = Case(w, debug_resid=True).run()
+    assert full.status() == 0
+    check_case(full, check_layers=True)
+    monkeypatch.setenv("PD_COMPACT", "1")
+    comp = Case(w, debug_resid=True).run()
+    assert comp.status() == 0
+    check_case(comp, check_layers=True)
+    a, b = full.logits.cpu().numpy(), comp.logits.cpu().numpy()
+    rms = np.sqrt(np.mean(a.astype(np.float64) ** 2, axis=1, keepdims=True))
+    assert np.max(np.abs(a - b) / rms) < 0.03
+    full.close()
+    comp.close()
+
+
 def _sample(b, K, k=3):
     """Requests to check at large C: the longest context, the most rejections, the first."""
     L = b["context_lens"]
