@@ -809,9 +809,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
 // (global_load_lds, 2 BT x 64 B per stage); each resident workgroup walks its
 // work items (tile, K split) without restarting the ring. The copy sources
 // are set once per item, so a stage only adds its K offset. Rows are 64 B in LDS
-// with their 16-byte chunks XOR-permuted by ((row >> 2) & 3): the 16 lanes
-// that one LDS cycle serves (rows r..r+15, one chunk) then read 16 different
-// 16-byte slots of the 256-byte bank line. Items are dealt so that in
+// with their 16-byte chunks XOR-permuted (big_sw): a fragment read (rows
+// r..r+15, one chunk) meets no bank conflict, counting the banks as 64 or
+// as 32 four-byte banks. Items are dealt so that in
 // every round each XCD takes a contiguous run of tiles (M blocks innermost):
 // tiles sharing a W tile and K range meet in one L2. For SwiGLU a tile's W
 // rows are 128 gate rows then the same 128 up rows; a wave takes 64 of each.
@@ -820,8 +820,17 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
 // double-buffered, each W fragment register refilled right after its last
 // MFMA), so a wave never stalls on LDS between MFMAs.
 constexpr int kBT = 256;                 // tile rows of W and of X
+// Chunk permutation of a 64-byte staged row. Rows r..r+15 at one chunk land
+// in 16 distinct 16-byte slots of a 256-byte line set (r & 3 picks the
+// quarter, the permuted chunk differs among rows with equal r & 3), and rows
+// 8t..8t+7 in 8 distinct slots of a 128-byte one (r & 1 picks the half, the
+// permuted chunk differs among rows with equal parity). With the
+// permutation (r >> 2) & 3 alone the 128-byte view saw 2-way conflicts on
+// half of the LDS cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = 0.5).
+__device__ __forceinline__ int big_sw(int r) { return ((r >> 2) ^ (r >> 1)) & 3; }
 constexpr int kBS = 32;                  // reduction elements per stage (64 B of each row)
-constexpr int kBNST = 4;                 // ring stages
+constexpr int kBNST = 4;                 // ring stages (max/argmax epilogue: its LDS tables fit beside 4)
+constexpr int kBNSTP = 4;                // ring stages of the other epilogues
 
 template <int EPI, int BT>
 __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
@@ -831,7 +840,8 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     constexpr int NA = BT / 32;               // W fragments (16 output columns each) per wave
     constexpr int SE = 2 * BT * kBS;          // elements per stage: W tile rows, then X tile rows
     constexpr int COLS = DUAL ? BT / 2 : BT;  // output columns per tile
-    __shared__ __align__(16) uint16_t ring[kBNST * SE];
+    constexpr int NST = EPI == EPI_ARGMAX ? kBNST : kBNSTP;
+    __shared__ __align__(16) uint16_t ring[NST * SE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r16 = lane & 15, g4 = lane >> 4;
@@ -866,7 +876,7 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
         const int u = tid + NT * j;
         const int r = (j < 2 ? u : u - 2 * NT) >> 2;
         rowrel[j] = r;
-        ch[j] = ((u & 3) ^ ((r >> 2) & 3)) * 8;
+        ch[j] = ((u & 3) ^ big_sw(r)) * 8;
     }
     const uint16_t* zp = g_gemm_zero;
     const unsigned lds0 = ring_lds(ring);
@@ -935,7 +945,7 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     // fragment i lies arow(i) rows further (gate rows, then the matching up
     // rows COLS further for SwiGLU), X fragment j 16 j rows further: both
     // compile-time, so every fragment read is one base plus an immediate
-    const int rsw = (r16 >> 2) & 3;
+    const int rsw = big_sw(r16);
     const int pos = (g4 ^ rsw) * 8;
     const int la = ((DUAL ? BT / 4 : BT / 2) * wn + r16) * kBS + pos;
     const int lb = (BT + 64 * wm + r16) * kBS + pos;
@@ -945,11 +955,11 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     // next stage's one by one, each right after its last MFMA has been issued;
     // X fragments are double-buffered (read at the start of the previous stage)
     auto read_a = [&](int q, int i) {
-        const uint16_t* Ws = ring + ((unsigned)q % kBNST) * SE + la;
+        const uint16_t* Ws = ring + ((unsigned)q % NST) * SE + la;
         return *reinterpret_cast<const bf16x8*>(Ws + arow(i) * kBS);
     };
     auto read_b = [&](bf16x8 (&b)[4], int q) {
-        const uint16_t* Xs = ring + ((unsigned)q % kBNST) * SE + lb;
+        const uint16_t* Xs = ring + ((unsigned)q % NST) * SE + lb;
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const bf16x8*>(Xs + 16 * j * kBS);
     };
@@ -1040,11 +1050,11 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
         }
     };
 
-    // all ring slots filled up front; stage q lives in slot q % kBNST
-    for (int st = 0; st < kBNST && st < total; ++st) issue(st);
+    // all ring slots filled up front; stage q lives in slot q % NST
+    for (int st = 0; st < NST && st < total; ++st) issue(st);
     bf16x8 af[NA], bc[4], bn[4];
     if (total > 0) {
-        ring_wait_later<L, kBNST - 1>(min(kBNST - 1, total - 1));
+        ring_wait_later<L, NST - 1>(min(NST - 1, total - 1));
         ring_barrier();
 #pragma unroll
         for (int i = 0; i < NA; ++i) af[i] = read_a(0, i);
@@ -1057,12 +1067,12 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
     // (in-bounds) slot whose values are never used; the waits and barriers
     // are uniform over the workgroup.
     auto stage = [&](bf16x8 (&bc)[4], bf16x8 (&bn)[4]) {
-        // the next stage's copies done: the two later stages stay in flight
-        // while both were issued (qc + 3 < total); near the end wait for all
-        if (qc + 3 < total) ring_wait<L * (kBNST - 2)>();
+        // the next stage's copies done, the ones issued after it still in
+        // flight (near the end: all done)
+        if (qc + NST - 1 < total) ring_wait<L * (NST - 2)>();
         else ring_wait<0>();
         ring_barrier();
-        if (qc + kBNST < total) issue((unsigned)(qc + kBNST) % kBNST);
+        if (qc + NST < total) issue((unsigned)(qc + NST) % NST);
         read_b(bn, qc + 1);
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
