@@ -75,8 +75,16 @@ __device__ __align__(16) uint16_t g_zero_page[PD_PAGE * 128];
 
 // Per head size and cache type: waves per workgroup, query tiles per wave
 // (one pass covers 128 queries), pages per LDS stage, stages in the ring,
-// 1 KB loads per page (K then V^T) and per wave per stage. An fp8 stage holds
-// twice the pages of a bf16 one (the same bytes). At dh 64 over a bf16 cache
+// 1 KB loads per page (K then V^T) and per wave per stage. fp8 pages at dh 64
+// (CONV): a stage holds as many pages as a bf16 one, in half the bytes; after
+// it lands, one pass of the whole workgroup turns it into bf16 pages (each
+// code once, not once per wave) in the layout the bf16 fragment reads use
+// (C = 64 over ~4k-key contexts: 125-128 vs 134 us per launch on a bf16 cache).
+// fp8 pages at dh 128: a stage holds twice the pages of a bf16 one (the same
+// bytes) and every wave converts the fragments it reads (the conversion pass
+// measured slower there: 149 vs 135 us on 16 x 20000 keys, its LDS round
+// trip and second barrier per 2-page stage cost more than the conversions
+// it saves). At dh 64 over a bf16 cache
 // a 3-stage ring (~51 KB of LDS) lets three workgroups share a CU instead of
 // two, with the same bytes in flight per CU: the kernel is bound by issue
 // (MFMA, softmax, LDS reads) as much as by the KV stream, and the third
@@ -86,7 +94,8 @@ struct AttnCfg {
     static constexpr int NW = 4;
     static constexpr int TPW = 2;
     static constexpr int EB = F8 ? 1 : 2;          // bytes per cached element
-    static constexpr int CH = (DH == 64 ? 4 : 2) * (F8 ? 2 : 1);
+    static constexpr bool CONV = F8 && DH == 64;   // fp8 stage converted by a workgroup pass
+    static constexpr int CH = (DH == 64 ? 4 : 2) * (F8 && !CONV ? 2 : 1);   // pages per stage
     static constexpr int NST = NS ? NS : ((DH == 64 && !F8) ? 3 : 4);
     static constexpr int PE = 16 * DH;             // elements of one page of K (or V)
     static constexpr int LPP = 2 * PE * EB / 1024; // 1 KB blocks per page: K half, V half
@@ -112,15 +121,16 @@ __device__ __forceinline__ int key_swp(int key, int page) {
 }
 __device__ __forceinline__ int v_half(int row, int half) { return half ^ ((row >> 2) & 1); }
 
-// fp8 pages: a K row (one key, DH bytes) keeps its 16-byte chunks
-// XOR-permuted by key_sw8; the 16 lanes of one fragment read are keys
-// {0-3, 8-11} of both pages of a pair at one chunk, and the permutation puts
-// them on 16 distinct 16-byte slots of a 256-byte bank line. V^T rows are
-// 16 bytes (16 keys) and are read 8 bytes at a time: no permutation needed.
-template <int DH>
+// fp8 pages with the conversion pass are staged as they are cached (K
+// [16][dh], V^T [dh][16] codes, no permutation): only that pass reads them,
+// 16 bytes per lane in order. fp8 pages read directly (dh 128): a K row (one
+// key, 128 bytes) keeps its 16-byte chunks XOR-permuted by key_sw8; the 16
+// lanes of one fragment read are keys {0-3, 8-11} of both pages of a pair at
+// one chunk, and the permutation puts them on 16 distinct 16-byte slots of a
+// 256-byte bank line. V^T rows are 16 bytes (16 keys) and are read 8 bytes at
+// a time: no permutation needed.
 __device__ __forceinline__ int key_sw8(int key, int page) {
-    if constexpr (DH == 64) return ((key >> 3) & 1) | ((page & 1) << 1);
-    else return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | ((page & 1) << 2);
+    return ((key >> 1) & 1) | (((key >> 3) & 1) << 1) | ((page & 1) << 2);
 }
 
 // 8 E4M3 codes -> 8 bf16 (exact: every E4M3 value is a bf16 value)
@@ -176,6 +186,8 @@ struct AttnSmem {
     using Cf = AttnCfg<DH, F8, NS>;
     using ET = typename std::conditional<F8, uint8_t, uint16_t>::type;
     __align__(16) ET kv[Cf::NST][Cf::CH][2][Cf::PE];   // [stage][page][K, V^T]
+    // CONV: the stage being consumed, converted to bf16 pages (bf16 layout)
+    __align__(16) uint16_t cv[Cf::CONV ? Cf::CH : 1][2][Cf::CONV ? Cf::PE : 8];
     int btc[kBtMax + Cf::CH];
     int pv[Cf::NST][Cf::CH];
 };
@@ -191,6 +203,7 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
     constexpr int KB = DH / 32;  // 16x16x32 steps over dh for the scores
     constexpr int OT = DH / 16;  // 16-dim output tiles
     constexpr int TPW = Cf::TPW, NW = Cf::NW, NT = 64 * NW, CH = Cf::CH, NST = Cf::NST;
+    constexpr bool CONV = Cf::CONV;
     auto& kv = sm.kv;
     auto& btc = sm.btc;
     auto& pv = sm.pv;
@@ -237,9 +250,9 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
             const uint16_t* qp = a.q + ((size_t)qrow[tt] * a.Hq + qh[tt]) * DH;
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) {
-                // fp8: the dims of a score step are regrouped so that one 16-byte
-                // read of a key row feeds two steps (the q side follows suit)
-                const int dim = F8 ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
+                // fp8 read directly: the dims of a score step are regrouped so that
+                // one 16-byte read of a key row feeds two steps (the q side follows)
+                const int dim = (F8 && !CONV) ? 64 * (kk >> 1) + 16 * g4 + 8 * (kk & 1) : 32 * kk + 8 * g4;
                 qv[tt][kk] = qok[tt] ? ldc<CG>(reinterpret_cast<const bf16x8*>(qp + dim)) : zero_bf16x8();
             }
         }
@@ -276,10 +289,12 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
                 const int row = 32 * (part - Cf::LPP / 2) + lane / 2;
                 loff[qd] = row * PD_PAGE + (v_half(row, lane & 1) << 3);
             }
+        } else if constexpr (CONV) {   // the block's 1 KB in order (K part, then V^T part)
+            loff[qd] = (part % (Cf::LPP / 2)) * 1024 + lane * 16;
         } else {
             if (part < Cf::LPP / 2) {               // K: 1024 / DH keys per 1 KB block
                 const int key = (1024 / DH) * part + lane / (DH / 16);
-                loff[qd] = key * DH + (((lane % (DH / 16)) ^ key_sw8<DH>(key, blk_page(qd))) << 4);
+                loff[qd] = key * DH + (((lane % (DH / 16)) ^ key_sw8(key, blk_page(qd))) << 4);
             } else {                                // V^T: 64 dim rows of 16 keys per 1 KB block
                 loff[qd] = (64 * (part - Cf::LPP / 2) + lane) * PD_PAGE;
             }
@@ -325,6 +340,27 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
+    // CONV: ring slot b's pages -> bf16 pages in sm.cv, in the bf16 layout
+    // (K rows permuted by key_swp, V^T halves by v_half). Thread t converts
+    // one 16-code K chunk (key, chunk) and one V^T row (16 keys) of page
+    // t / DH: 16 keys x DH / 16 chunks = DH rows = DH threads per page.
+    auto convert = [&](int b) {
+        if constexpr (CONV) {
+            static_assert(NT == CH * DH, "one K chunk and one V^T row per thread");
+            const int p = tid / DH, idx = tid % DH;
+            const int key = idx / (DH / 16), c16 = idx % (DH / 16);
+            const uint4 kw = *reinterpret_cast<const uint4*>(&kv[b][p][0][key * DH + 16 * c16]);
+            const uint4 vw = *reinterpret_cast<const uint4*>(&kv[b][p][1][idx * PD_PAGE]);
+            const int ks = key_swp<DH>(key, p);
+            uint16_t* kd = &sm.cv[p][0][key * DH];
+            uint16_t* vd = &sm.cv[p][1][idx * PD_PAGE];
+            *reinterpret_cast<bf16x8*>(kd + (((2 * c16) ^ ks) << 3)) = fp8x8_to_bf16(kw.x, kw.y);
+            *reinterpret_cast<bf16x8*>(kd + (((2 * c16 + 1) ^ ks) << 3)) = fp8x8_to_bf16(kw.z, kw.w);
+            *reinterpret_cast<bf16x8*>(vd + (v_half(idx, 0) << 3)) = fp8x8_to_bf16(vw.x, vw.y);
+            *reinterpret_cast<bf16x8*>(vd + (v_half(idx, 1) << 3)) = fp8x8_to_bf16(vw.z, vw.w);
+        }
+    };
+
     for (int qbase = 0; qbase < nq; qbase += NW * TPW * 16) {
         if (qbase > 0) load_q(qbase);
         const bool wave_has = qbase + wave * 16 < nq;   // wave-uniform
@@ -351,16 +387,30 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
             barrier_lds();
             if (c + NST - 1 < nchunks) issue(c + NST - 1, (c + NST - 1) % NST);
             const int b = c % NST;
+            if constexpr (CONV) {
+                // every wave converts its share (the chunk's slot landed; the
+                // previous chunk's converted pages are no longer read), then all
+                convert(b);
+                barrier_lds();
+            }
             if (!wave_has) continue;
 #pragma unroll
             for (int pi = 0; pi < CH; pi += 2) {
                 const int p0 = kb + (c * CH + pi) * PD_PAGE;
                 if (p0 >= ke) break;
                 const bool pgok = pv[b][pi + vpage] != 0;   // this lane group's page
-                const ET* Kp = kv[b][pi + kpage][0];
-                const ET* Vp = kv[b][pi + vpage][1];
                 bf16x8 k0[KB], k1[KB], vf[OT];
-                if constexpr (!F8) {
+                if constexpr (!F8 || CONV) {
+                    // bf16 pages: the ring slot's, or (CONV) their conversion
+                    const uint16_t* Kp;
+                    const uint16_t* Vp;
+                    if constexpr (CONV) {
+                        Kp = sm.cv[pi + kpage][0];
+                        Vp = sm.cv[pi + vpage][1];
+                    } else {
+                        Kp = reinterpret_cast<const uint16_t*>(kv[b][pi + kpage][0]);
+                        Vp = reinterpret_cast<const uint16_t*>(kv[b][pi + vpage][1]);
+                    }
 #pragma unroll
                     for (int kk = 0; kk < KB; ++kk) {
                         const int ch = ((4 * kk + g4) ^ ksw) << 3;
@@ -371,8 +421,10 @@ __device__ __forceinline__ void attn_split_item(const AttnArgs& a, int blk, Attn
                     for (int j = 0; j < OT; ++j)
                         vf[j] = *reinterpret_cast<const bf16x8*>(Vp + 16 * PD_PAGE * j + voff);
                 } else {
+                    const uint8_t* Kp = reinterpret_cast<const uint8_t*>(kv[b][pi + kpage][0]);
+                    const uint8_t* Vp = reinterpret_cast<const uint8_t*>(kv[b][pi + vpage][1]);
                     // K: one 16-byte read per key row feeds score steps 2m and 2m + 1
-                    const int sw = key_sw8<DH>(key0, kpage);   // the same for key0 + 4
+                    const int sw = key_sw8(key0, kpage);   // the same for key0 + 4
 #pragma unroll
                     for (int m2 = 0; m2 < KB / 2; ++m2) {
                         const int ch = ((4 * m2 + g4) ^ sw) << 4;
