@@ -593,13 +593,14 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
         roof = {"bound": "hbm", "kernel": "decode_kernel (persistent: the whole drafter pass in one launch)",
                 "achieved": fb / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": fb}
     elif dom == "lm_head":
-        if R <= 128:   # weight-streaming ring kernel (R flop per weight byte, below the ridge): HBM-bound
-            kname = "gemm_ring_kernel<ARGMAX>" if R <= 64 else "gemm_ring_kernel<ARGMAX, 8 X tiles>"
+        kname = ("gemm_ring_kernel<ARGMAX>" if R <= 64 else "gemm_ring_kernel<ARGMAX, 8 X tiles>" if R <= 128
+                 else "gemm_big_kernel<ARGMAX, 256-row tiles>")
+        # R flop per weight byte: below the ridge (peak flops / peak bytes) the
+        # weight stream bounds it, above it the matrix cores
+        if R < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
             roof = {"bound": "hbm", "kernel": f"{kname} (LM head + fused argmax)",
                     "achieved": lm_head_bytes(dm, R) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-        else:         # many rows: MFMA-bound
-            kname = ("gemm_tiled_kernel<ARGMAX>" if R < 256 else
-                     "gemm_big_kernel<ARGMAX, 128-row tiles>" if R < 384 else "gemm_big_kernel<ARGMAX>")
+        else:
             roof = {"bound": "mfma", "kernel": f"{kname} (LM head + fused argmax)",
                     "achieved": lm_flops / k_avg_s / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
     else:
@@ -626,7 +627,7 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
         "step_algorithmic_bytes": sb,
         "step_hbm_frac": sb / (ms_step / 1000) / 1e9 / HBM_PEAK_GBS,
         "roofline": roof,
-        "gemm_roofline": None if (g_n + l_n) == 0 else {
+        "gemm_roofline": None if (g_n + l_n) == 0 or gemm_us < 1.0 else {
             "bound": "mfma", "kernels": "every projection GEMM + the LM head",
             "flops_per_step": gf, "rows_credited": T_eff,
             "us_per_step": gemm_us, "projections_us": proj_us, "lm_head_us": lm_us,

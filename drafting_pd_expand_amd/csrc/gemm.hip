@@ -6,15 +6,16 @@
 // few rows per step: the draft batch has v_r + K - 1 computed rows per
 // request and the LM head C*K rows. Three kernels:
 //
-//  * M <= 64 rows (low concurrency): every projection is a stream of its
-//    weight matrix. A persistent ring kernel (one workgroup per CU) copies W
-//    and the matching X columns straight from HBM into a ring of LDS stages
-//    and runs v_mfma_f32_16x16x32_bf16 on them (W rows are the A operand, X
-//    rows the B operand, so a lane ends with 4 consecutive output columns of
-//    one row);
+//  * M <= 64 rows (low concurrency; the LM head up to 128 rows): every
+//    projection is a stream of its weight matrix. A persistent ring kernel
+//    (one workgroup per CU) copies W and the matching X columns straight from
+//    HBM into a ring of LDS stages and runs v_mfma_f32_16x16x32_bf16 on them
+//    (W rows are the A operand, X rows the B operand, so a lane ends with 4
+//    consecutive output columns of one row); the projections of 17..64 rows
+//    stage only W (X fragments go straight to registers);
 //  * more rows: persistent tiles fed by a global -> LDS ring, 256 x 256 from
-//    384 rows on, 128 x 128 (two workgroups per CU) below; the LM head below
-//    256 rows uses 128 x 128 tiles staged through registers instead.
+//    384 rows on (the LM head from 129), 128 x 128 (two workgroups per CU)
+//    below.
 //
 // Projections with few output columns are split over workgroups along K.
 // Those splits never meet inside the GEMM: each writes an fp32 partial plane,
@@ -586,218 +587,6 @@ __global__ __launch_bounds__(256) void gemm_wring_kernel(GemmArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// Tiled kernel (the LM head at 64 < M < 256): a 128 x 128 output tile per workgroup,
-// K in steps of 64 staged through LDS (double buffered: the next step's
-// global loads are in registers while the current step's MFMAs run), four
-// waves each owning a 64 x 64 quarter (4 x 4 MFMA tiles); two workgroups fit
-// a CU. Used for the LM head at 64 < M < 256 rows, where the 256-row tiles
-// below would mostly be padding. For SwiGLU the tile's 128 W rows are 64 gate rows then
-// the same 64 up rows, and each wave takes 32 of each: a lane holds matching
-// gate and up columns.
-constexpr int kTM = 128, kTN = 128, kTK = 64;
-constexpr int kTRow = kTK + 8;   // padded LDS row (elements): 144 B stride, conflict-free 16-byte reads
-
-template <int EPI, bool WSTREAM>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs a) {
-    constexpr bool DUAL = (EPI == EPI_SWIGLU);
-    __shared__ __align__(16) uint16_t ws_[2][kTN * kTRow];
-    __shared__ __align__(16) uint16_t xs_[2][kTM * kTRow];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r16 = lane & 15, g4 = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;
-    // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs,
-    // so XCD x takes the contiguous tile range [x*chunk, (x+1)*chunk) with the
-    // M blocks innermost: the workgroups sharing a W tile run back to back on
-    // one XCD and find it in that XCD's L2.
-    const int mblocks = (a.M + kTM - 1) / kTM;
-    const int total = a.ntiles * mblocks;
-    const int chunk = (total + 7) / 8;
-    const int tile = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
-    if (tile >= total) return;
-    const int m0 = (tile % mblocks) * kTM;
-    // column base of the tile: 128 W rows, or 64 gate + 64 up rows for SwiGLU
-    const int ntile = tile / mblocks;
-    const int n0 = ntile * (DUAL ? kTN / 2 : kTN);
-
-    // K range of this split (multiples of kTK)
-    const int ksteps = (a.K + kTK - 1) / kTK;
-    const int per = (ksteps + a.splits - 1) / a.splits;
-    const int kb = min(a.K, blockIdx.z * per * kTK);
-    const int ke = min(a.K, (blockIdx.z + 1) * per * kTK);
-
-    // staging: each thread moves 4 W and 4 X 16-byte units per K step
-    const uint16_t* wsrc[4];
-    const uint16_t* xsrc[4];
-    bool wok[4], xok[4];
-    int soff[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int u = tid + 256 * j;
-        const int row = u >> 3, c8 = u & 7;
-        soff[j] = row * kTRow + c8 * 8;
-        int wrow;
-        if constexpr (DUAL) {
-            wrow = n0 + (row & 63);
-            wok[j] = wrow < a.N;
-            wsrc[j] = (row < 64 ? a.W : a.W2) + (size_t)(wok[j] ? wrow : 0) * a.K + c8 * 8;
-        } else {
-            wrow = n0 + row;
-            wok[j] = wrow < a.N;
-            wsrc[j] = a.W + (size_t)(wok[j] ? wrow : 0) * a.K + c8 * 8;
-        }
-        const int m = m0 + row;
-        xok[j] = m < a.M;
-        int xr = m;
-        if (xok[j] && a.xrows) {
-            xr = a.xrows[m];
-            if (xr < 0 || xr >= a.xrows_limit) {
-                xok[j] = false;
-                flag(a.status, PD_STATUS_BAD_ROW);
-            }
-        }
-        xsrc[j] = a.X + (size_t)(xok[j] ? xr : 0) * a.ldx + c8 * 8;
-    }
-    uint4 wreg[4], xreg[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = k0 + ((tid + 256 * j) & 7) * 8;
-            // WSTREAM (one row block: every weight is read once): non-temporal
-            // loads, so the weight stream does not evict the X rows every tile
-            // re-reads from L2; with more row blocks they share each W tile in L2
-            if (wok[j] && k < ke) {
-                typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-                const u32x4* src = reinterpret_cast<const u32x4*>(wsrc[j] + k0);
-                u32x4 t;
-                if constexpr (WSTREAM) t = __builtin_nontemporal_load(src);
-                else t = *src;
-                wreg[j] = make_uint4(t.x, t.y, t.z, t.w);
-            } else {
-                wreg[j] = make_uint4(0, 0, 0, 0);
-            }
-            xreg[j] = (xok[j] && k < ke) ? *reinterpret_cast<const uint4*>(xsrc[j] + k0) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto sstore = [&](int b) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            *reinterpret_cast<uint4*>(&ws_[b][soff[j]]) = wreg[j];
-            *reinterpret_cast<uint4*>(&xs_[b][soff[j]]) = xreg[j];
-        }
-    };
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // LDS rows of this wave's A (W) and B (X) fragments
-    int wrow_l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        wrow_l[i] = DUAL ? (i < 2 ? 32 * wn + 16 * i : 64 + 32 * wn + 16 * (i - 2)) : 64 * wn + 16 * i;
-
-    if (kb < ke) {
-        gload(kb);
-        sstore(0);
-    }
-    __syncthreads();
-    int b = 0;
-    for (int k0 = kb; k0 < ke; k0 += kTK) {
-        const bool more = k0 + kTK < ke;
-        if (more) gload(k0 + kTK);
-#pragma unroll
-        for (int kk = 0; kk < kTK / 32; ++kk) {
-            bf16x8 af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(&ws_[b][(wrow_l[i] + r16) * kTRow + 32 * kk + 8 * g4]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const bf16x8*>(&xs_[b][(64 * wm + 16 * j + r16) * kTRow + 32 * kk + 8 * g4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(af[i], bf[j], acc[i][j]);
-        }
-        if (more) sstore(b ^ 1);
-        __syncthreads();
-        b ^= 1;
-    }
-
-    // lane holds rows m = m0 + 64*wm + 16*j + r16 and 4 consecutive columns per fragment i
-    if constexpr (EPI == EPI_ARGMAX) {
-        __shared__ float s_v[2][kTM];
-        __shared__ int s_i[2][kTM];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ml = 64 * wm + 16 * j + r16;
-            const int m = m0 + ml;
-            float bv = -FLT_MAX;
-            int bi = INT_MAX;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = n0 + 64 * wn + 16 * i + 4 * g4;
-                if (n >= a.N) continue;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) better(bv, bi, acc[i][j][e], n + e);
-                if (a.logits && m < a.M)
-                    *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[i][j];
-            }
-#pragma unroll
-            for (int off = 16; off <= 32; off <<= 1) {
-                const float ov = __shfl_xor(bv, off, kWave);
-                const int oi = __shfl_xor(bi, off, kWave);
-                better(bv, bi, ov, oi);
-            }
-            if (g4 == 0) {
-                s_v[wn][ml] = bv;
-                s_i[wn][ml] = bi;
-            }
-        }
-        __syncthreads();
-        if (tid < kTM) {
-            const int m = m0 + tid;
-            float bv = s_v[0][tid];
-            int bi = s_i[0][tid];
-            better(bv, bi, s_v[1][tid], s_i[1][tid]);
-            if (m < a.M) {
-                a.amax_v[(size_t)m * a.ntiles + ntile] = bv;
-                a.amax_i[(size_t)m * a.ntiles + ntile] = bi;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int m = m0 + 64 * wm + 16 * j + r16;
-            if (m >= a.M) continue;
-            if constexpr (EPI == EPI_PARTIAL) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int n = n0 + 64 * wn + 16 * i + 4 * g4;
-                    if (n < a.N)
-                        *reinterpret_cast<f32x4*>(a.ws + ((size_t)blockIdx.z * a.M + m) * a.N + n) = acc[i][j];
-                }
-            } else {  // SwiGLU: fragments 0,1 = gate, 2,3 = the matching up columns
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int n = n0 + 32 * wn + 16 * i + 4 * g4;
-                    if (n >= a.N) continue;
-                    float h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) h[e] = silu(acc[i][j][e]) * acc[i + 2][j][e];
-                    uint2 pk;
-                    pk.x = uint32_t(f2bf(h[0])) | (uint32_t(f2bf(h[1])) << 16);
-                    pk.y = uint32_t(f2bf(h[2])) | (uint32_t(f2bf(h[3])) << 16);
-                    *reinterpret_cast<uint2*>(a.yb + (size_t)m * a.ldyb + n) = pk;
-                }
-            }
-        }
-    }
-}
-
 // Persistent ring-fed tile kernel for many rows (M > 64). With BT = 256 a
 // workgroup of 8 waves (two per SIMD: one wave per SIMD cannot keep the
 // matrix core busy) owns a 256 (W rows = output columns) x 256 (X rows =
@@ -1113,16 +902,6 @@ int launch_big(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
 }
 
-template <int EPI>
-int launch_tiled(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
-    const int chunk = (p.ntiles * p.mblocks + 7) / 8;
-    if (p.mblocks == 1)
-        hipLaunchKernelGGL((gemm_tiled_kernel<EPI, true>), dim3(8 * chunk, 1, p.splits), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((gemm_tiled_kernel<EPI, false>), dim3(8 * chunk, 1, p.splits), dim3(256), 0, s, a);
-    return hipGetLastError() == hipSuccess ? PD_OK : PD_EHIP;
-}
-
 template <int EPI, int NM>
 int launch_ring_nm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     constexpr int WN = EPI == EPI_SWIGLU ? 2 : 4;
@@ -1172,7 +951,6 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     switch (p.kind) {
         case GEMM_RING: return launch_ring<EPI>(p, a, s);
         case GEMM_WRING: return launch_wring<EPI>(p, a, s);
-        case GEMM_TILED: return launch_tiled<EPI>(p, a, s);
         case GEMM_BIG: return launch_big<EPI>(p, a, s);
         default: return PD_EINVAL;
     }
@@ -1183,14 +961,13 @@ int launch_epi(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
 GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
     GemmPlan p;
     p.nm = 1;
-    // M <= 64: weight-streaming ring. 64 < M < 256: the LM head (max/argmax
-    // epilogue) on 128 x 128 register-staged tiles, everything else with more
-    // than 64 rows on the ring-fed tile kernel: 128-row tiles below 384 rows,
-    // 256-row tiles from there. (Measured on the drafting step: the 128-row
-    // ring-fed kernel runs the 224-row projections of the Qwen3-Coder-scale
-    // drafter and a 320-row LM head faster than the register-staged tiles,
-    // a 112-row LM head slower and a 192-row one alike.)
-    p.kind = M <= 64 ? GEMM_RING : ((M < 256 && epi == EPI_ARGMAX) ? GEMM_TILED : GEMM_BIG);
+    // M <= 64: weight-streaming ring (the LM head up to 128 rows, below).
+    // More rows: the ring-fed tile kernel, 128-row tiles below 384 rows,
+    // 256-row tiles from there, and for the LM head from 129 rows (measured
+    // on the C = 64 step: 192 rows 372 us on 256-row tiles against 432 on
+    // 128 x 128 register-staged tiles and 427 on 128-row ones; 320 rows 551
+    // against 564 on 128-row tiles).
+    p.kind = M <= 64 ? GEMM_RING : GEMM_BIG;
     p.splits = 1;
     p.grid = 0;
     p.krs = kRS;
@@ -1216,7 +993,7 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
         // 384 rows on, 128 (4 waves, two workgroups per CU) below; K splits
         // (partial planes, summed by the consumer) chosen to minimise the
         // stages of the busiest of the resident workgroups
-        const int bt = M >= 384 ? kBT : kBT / 2;
+        const int bt = (M >= 384 || (epi == EPI_ARGMAX && M > 128)) ? kBT : kBT / 2;
         const long cap = bt == kBT ? 256 : 512;
         p.mt = 0;
         p.wn = bt / 32;
@@ -1229,30 +1006,6 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
         p.ntiles = ntn;
         const long items = tiles * p.splits;
         p.grid = (int)(items < cap ? items : cap);
-        return p;
-    }
-    if (p.kind == GEMM_TILED) {
-        // 128 x 128 tiles, two workgroups per CU; K splits only when the tile
-        // count leaves most of the 256 CUs idle
-        p.mt = 0;
-        p.wn = 4;
-        p.mblocks = (M + kTM - 1) / kTM;
-        const int cols = (epi == EPI_SWIGLU) ? kTN / 2 : kTN;
-        p.ntiles = (N + cols - 1) / cols;
-        if (epi == EPI_PARTIAL) {
-            // the split count that minimises the K steps of the busiest of
-            // the 512 resident workgroups (two per CU): a grid just over 512
-            // would run a second round for a few workgroups
-            const long tiles = (long)p.ntiles * p.mblocks;
-            const int ksteps = (K + kTK - 1) / kTK;
-            long best = -1;
-            for (int sp = 1; sp <= 8 && sp <= ksteps; ++sp) {
-                const int per = (ksteps + sp - 1) / sp;
-                if ((sp - 1) * per >= ksteps) continue;   // no empty split
-                const long span = ((tiles * sp + 511) / 512) * per;
-                if (best < 0 || span < best) { best = span; p.splits = sp; }
-            }
-        }
         return p;
     }
     // persistent LDS ring: nm groups of 16 output columns per wave, 4 waves

@@ -54,15 +54,15 @@ struct GemmArgs {
 
 enum GemmKind : int {
     GEMM_RING = 0,    // M <= 64 (LM head: <= 128): persistent LDS-ring weight streaming
-    GEMM_TILED = 1,   // LM head at 64 < M < 256: 128 x 128 register-staged tiles, two workgroups per CU
-    GEMM_BIG = 2,     // other M > 64: persistent ring-fed tiles, 256 x 256 (8 waves) from 384 rows, else 128 x 128
+    GEMM_BIG = 2,     // M > 64 (LM head: > 128): persistent ring-fed tiles, 256 x 256 (8 waves) from 384
+                      // rows (LM head: 129), else 128 x 128
     GEMM_WRING = 3,   // M <= 64: weight-only LDS ring, X fragments loaded into registers
 };
 
 struct GemmPlan {
     int kind;      // GemmKind
     int mt;        // ring: 16-row X tiles (1, 2, 4, or 8 for the LM head at 65..128 rows)
-    int mblocks;   // tiled / big: workgroups along M
+    int mblocks;   // big: row blocks (workgroup tiles along M)
     int wn;        // waves per workgroup (ring-fed tiles: 8 = 256-row, 4 = 128-row)
     int nm;        // ring / weight-only ring: groups of 16 output columns (W rows) per wave
     int ntiles;    // column tiles (ARGMAX: groups of the max/argmax partial results per row)

@@ -41,7 +41,7 @@ def test_tiny_prefill_all_rows_and_layers():
     (GQA64, 3, 16, "fixed", 40),
     (GQA128, 3, 7, "fixed", 1000),
     (GQA128, 2, 3, "lognormal", 0),
-    # 65..128 sampled rows: the LM head on the 128 x 128 tile kernel, every row checked
+    # 65..128 sampled rows: the LM head on the 8-tile weight-streaming ring, every row checked
     (GQA64, 13, 7, "lognormal", 0),
     (GQA128, 16, 8, "fixed", 300),
 ], ids=["gqa64-c5k5", "gqa64-k1", "gqa64-k16", "gqa128-c3k7", "gqa128-c2k3", "gqa64-c13k7-lm",
