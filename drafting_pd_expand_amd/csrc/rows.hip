@@ -348,10 +348,15 @@ __global__ __launch_bounds__(256) void compact_rows_kernel(
     __shared__ int s_w[4];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (blockIdx.x == 0) {
-        const int per = (T + 255) / 256;
+        const int per = (T + 255) / 256;   // <= 16 rows per thread
         const int r0 = min(T, tid * per), r1 = min(T, r0 + per);
         int cnt = 0;
-        for (int i = r0; i < r1; ++i) cnt += is_rejected[i] == 0;
+        unsigned keep = 0;   // bit i - r0: row i kept
+        for (int i = r0; i < r1; ++i) {
+            const unsigned k = is_rejected[i] == 0;
+            keep |= k << (i - r0);
+            cnt += (int)k;
+        }
         // exclusive prefix of the per-thread counts over the block
         int incl = cnt;
 #pragma unroll
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(256) void compact_rows_kernel(
         for (int k = 0; k < w; ++k) run += s_w[k];
         for (int i = r0; i < r1; ++i) {
             s_pre[i] = run;
-            run += is_rejected[i] == 0;
+            run += (int)((keep >> (i - r0)) & 1u);
         }
         if (tid == 255) s_pre[T] = run;   // (the last thread's run ends at T: per * 256 >= T)
         __syncthreads();
@@ -381,13 +386,29 @@ __global__ __launch_bounds__(256) void compact_rows_kernel(
             const bool ok = row >= 0 && row < T;
             if (!ok) flag(status, PD_STATUS_BAD_ROW);
             // a rejected sampled row (a padding request's) has no defined
-            // draft: it takes compacted row 0
-            nti_c[j] = (ok && is_rejected[row] == 0) ? s_pre[row] : 0;
+            // draft: it takes compacted row 0 (kept rows: s_pre steps there)
+            nti_c[j] = (ok && s_pre[row + 1] != s_pre[row]) ? s_pre[row] : 0;
         }
         return;
     }
     const int i = blockIdx.x - 1;
     if (is_rejected[i] != 0) return;   // whole workgroup
+    // the row's loads go out first (they do not depend on its index c), then
+    // the count of kept rows before it, then the stores (a load-store loop
+    // would wait out one memory round trip per iteration: the compiler cannot
+    // tell the two rows apart); h3 <= 16384: at most 8 chunks per thread
+    const uint4* src = reinterpret_cast<const uint4*>(hidden + (size_t)i * h3);
+    constexpr int kMaxChunks = 8;
+    uint4 buf[kMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j)
+        if (j * 256 + tid < h3 / 8) buf[j] = src[j * 256 + tid];
+    int meta[3] = {0, 0, 0};
+    if (tid == 0) {
+        meta[0] = ids[i];
+        meta[1] = positions[i];
+        meta[2] = slots[i];
+    }
     int cnt = 0;
     for (int j = tid; j < i; j += 256) cnt += is_rejected[j] == 0;
 #pragma unroll
@@ -397,13 +418,14 @@ __global__ __launch_bounds__(256) void compact_rows_kernel(
     const int c = s_w[0] + s_w[1] + s_w[2] + s_w[3];
     if (tid == 0) {
         rowmap[c] = i;
-        ids_c[c] = ids[i];
-        pos_c[c] = positions[i];
-        slot_c[c] = slots[i];
+        ids_c[c] = meta[0];
+        pos_c[c] = meta[1];
+        slot_c[c] = meta[2];
     }
-    const uint4* src = reinterpret_cast<const uint4*>(hidden + (size_t)i * h3);
     uint4* dst = reinterpret_cast<uint4*>(hid_c + (size_t)c * h3);
-    for (int k = tid; k < h3 / 8; k += 256) dst[k] = src[k];
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j)
+        if (j * 256 + tid < h3 / 8) dst[j * 256 + tid] = buf[j];
 }
 
 // dst[rowmap[c]] = src[c], c < t_eff (one workgroup per compacted row)
@@ -476,7 +498,7 @@ int launch_compact_rows(const uint8_t* is_rejected, const int32_t* ids, const in
                         const uint16_t* hidden, int T, int C, int R, int h3, uint16_t* hid_c,
                         int32_t* ids_c, int32_t* pos_c, int32_t* slot_c, int32_t* cu_c, int32_t* nti_c,
                         int32_t* rowmap, int32_t* t_eff, int32_t* status, hipStream_t s) {
-    if (T <= 0 || T > kCompactMaxRows || h3 % 8 || C < 0 || R < 0) return PD_EINVAL;
+    if (T <= 0 || T > kCompactMaxRows || h3 % 8 || h3 > 8 * 256 * 8 || C < 0 || R < 0) return PD_EINVAL;
     if (((uintptr_t)hidden | (uintptr_t)hid_c) & 15) return PD_EINVAL;   // 16-byte row copies
     hipLaunchKernelGGL(compact_rows_kernel, dim3(T + 1), dim3(256), 0, s, is_rejected, ids, positions, slots,
                        cu_out, nti, hidden, T, C, R, h3, hid_c, ids_c, pos_c, slot_c, cu_c, nti_c, rowmap,
