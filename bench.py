@@ -434,11 +434,16 @@ def yardsticks() -> dict:
     streaming read (sum of a 2 GiB bf16 tensor, fp32 accumulation in torch),
     a device-to-device copy of 1 GiB, and torch.matmul in bf16 (the installed
     vendor GEMM) at the C = 64, K = 7 LM-head shape (448 x 2880 by
-    2880 x 201088), at the two largest projection shapes of that step (896
-    rows: gate and up together, and down) and at a large square shape."""
+    2880 x 201088), at the two largest projection shapes of that step (the
+    rows its projections compute, the non-rejected ones: gate and up
+    together, and down) and at a large square shape."""
     import torch
+    import synth
     dev = torch.device("cuda:0")
     out = {}
+    w = synth.get_workload("g_c64")
+    bb = synth.make_batch(w)
+    rows = int((bb["num_tokens"] - bb["num_rejected"] + w.K - 1).sum())
 
     def timed(fn, reps):
         fn()
@@ -463,8 +468,8 @@ def yardsticks() -> dict:
     # the drafter's layout: weights row-major [N][K] (out x in), Y = X W^T
     # (a 2-D product with a transposed-view right operand: one library call,
     # no copy)
-    for name, (M, K, N) in (("lm_head_c64_k7", (448, 2880, 201088)), ("gate_up_c64_k7", (896, 2880, 15360)),
-                            ("down_c64_k7", (896, 7680, 2880)), ("square_8192", (8192, 8192, 8192))):
+    for name, (M, K, N) in (("lm_head_c64_k7", (448, 2880, 201088)), ("gate_up_c64_k7", (rows, 2880, 15360)),
+                            ("down_c64_k7", (rows, 7680, 2880)), ("square_8192", (8192, 8192, 8192))):
         A = torch.randn(M, K, dtype=torch.bfloat16, device=dev)
         W = torch.randn(N, K, dtype=torch.bfloat16, device=dev)
         t = timed(lambda: torch.matmul(A, W.t()), 10)
@@ -539,8 +544,10 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
     eager_ids = draft.clone()
 
     # which kernel dominates: the persistent decode kernel (the whole pass in
-    # one launch, at few rows), else the LM head (one launch) or the attention
-    # kernel (one per layer), from one step with events around those classes
+    # one launch, at few rows), else the LM head (once per step: one launch,
+    # or two when its last round of tiles goes to a second launch) or the
+    # attention kernel (one launch per layer), from one step with events
+    # around those classes
     h.profile((1 << pdx.KERNEL_LMHEAD) | (1 << pdx.KERNEL_ATTN) | (1 << pdx.KERNEL_DECODE))
     step(stream)
     torch.cuda.synchronize()
@@ -551,7 +558,7 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
     if de_n > 0:
         dom = "decode"
     else:
-        dom = "lm_head" if lm_ms / max(lm_n, 1) >= at_ms / max(at_n, 1) else "attention"
+        dom = "lm_head" if lm_ms >= at_ms / max(at_n, 1) else "attention"
     dom_cls = {"decode": pdx.KERNEL_DECODE, "lm_head": pdx.KERNEL_LMHEAD, "attention": pdx.KERNEL_ATTN}[dom]
 
     def timed_region(class_mask):
@@ -573,6 +580,9 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
     wall = time.perf_counter() - w0
     k_ms, k_n = h.profile_read(dom_cls)
     h.profile(0)
+    lm_launches = k_n // steps if dom == "lm_head" else 1
+    if dom == "lm_head":   # the LM head's time per step (both launches when split)
+        k_n = steps
     steps_s = 1000.0 / ms_step
     k_avg_s = k_ms / max(k_n, 1) / 1000.0
 
@@ -594,7 +604,8 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
                 "achieved": fb / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": fb}
     elif dom == "lm_head":
         kname = ("gemm_ring_kernel<ARGMAX>" if R <= 64 else "gemm_ring_kernel<ARGMAX, 8 X tiles>" if R <= 128
-                 else "gemm_big_kernel<ARGMAX, 256-row tiles>")
+                 else "gemm_big_kernel<ARGMAX, 256-row tiles>" if lm_launches == 1
+                 else "gemm_big_kernel<ARGMAX>, 256-row tiles + a last-round launch on 128-row tiles")
         # R flop per weight byte: below the ridge (peak flops / peak bytes) the
         # weight stream bounds it, above it the matrix cores
         if R < BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
@@ -608,7 +619,9 @@ def run_leg(workload: str, steps: int, warmup: int, extras: bool, cpu: bool, cpu
                 "achieved": attn_bytes(dm, b, w.K) / k_avg_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(workload) if dom == "lm_head" else None
-    roof["us_per_launch"] = k_avg_s * 1e6
+    roof["us_per_launch"] = k_avg_s * 1e6   # (the LM head: per step, over its launches)
+    if dom == "lm_head":
+        roof["launches_per_step"] = lm_launches
     sb = step_bytes(dm, b, w.K)
     v = b["num_tokens"] - b["num_rejected"]
     T_eff = int((v + w.K - 1).sum())

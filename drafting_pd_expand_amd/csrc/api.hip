@@ -165,7 +165,7 @@ Layout plan_layout(const pd_model* m, const pd_batch_dims* d, bool fp8, bool hid
         need(T, m->d, m->F);
     };
     need_all();
-    L.ntilesV = plan_gemm(R, m->V, m->d, EPI_ARGMAX).ntiles;
+    L.ntilesV = plan_lm_head(R, m->V, m->d).ntiles;
     L.amax_cap = L.ntilesV;
     L.dp = plan_decode(*m, T, R, fp8);
     if (!decode_enabled()) L.dp.ok = false;
@@ -365,6 +365,34 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
         Timed t(h, cls, s);
         return launch_gemm(epi, p, a, s);
     };
+    // LM head on the packed sampled rows xg (one or two launches, see
+    // plan_lm_head), argmax partials for all of V in every row
+    auto lm_head = [&]() -> int {
+        const LmHeadPlan lp = plan_lm_head(R, m->V, d);
+        if (lp.ntiles != L.ntilesV) return PD_EINVAL;
+        int r;
+        for (int part = 0; part < 2; ++part) {
+            const GemmPlan& p = part ? lp.tail : lp.main;
+            if (p.kind < 0) break;
+            const int n0 = part ? lp.n_main : 0;
+            GemmArgs a;
+            std::memset(&a, 0, sizeof(a));
+            a.X = xg; a.ldx = d;
+            a.W = m->lm_head + (size_t)n0 * d;
+            a.M = R; a.N = part ? m->V - lp.n_main : lp.n_main; a.K = d;
+            a.logits = logits ? logits + n0 : nullptr; a.ldlog = m->V;
+            a.amax_v = (float*)(S + L.amv) + (part ? lp.main.ntiles : 0);
+            a.amax_i = (int*)(S + L.ami) + (part ? lp.main.ntiles : 0);
+            a.status = st;
+            if (lp.tail.kind >= 0) {
+                a.n_base = n0;
+                a.amax_ld = lp.ntiles;
+            }
+            Timed t(h, PD_KERNEL_LMHEAD, s);
+            if ((r = launch_gemm(EPI_ARGMAX, p, a, s)) != PD_OK) return r;
+        }
+        return PD_OK;
+    };
     auto dbg = [&](int slot) -> int {
         if (!h || !h->dbg) return PD_OK;
         if (L.compact) {   // compacted rows back to their places (rejected rows are left as they are)
@@ -430,8 +458,7 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
         }
         if (L.dp.lm_in_kernel) return PD_OK;
         // LM head on the packed sampled rows the pass left in xg, greedy argmax
-        PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, xg, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
-                    nullptr, 0, nullptr));
+        PD_TRY(lm_head());
         Timed t(h, PD_KERNEL_OTHER, s);
         return launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV, draft_ids, st, s);
     }
@@ -533,8 +560,7 @@ int forward_impl(pd_handle* h, char* S, const Layout& L, int32_t* st, const pd_m
                                  hidden_out));
     }
     // LM head on the packed sampled rows, greedy argmax
-    PD_TRY(gemm(PD_KERNEL_LMHEAD, EPI_ARGMAX, xg, d, nullptr, 0, m->lm_head, nullptr, R, m->V, d,
-                nullptr, 0, nullptr));
+    PD_TRY(lm_head());
     {
         Timed t(h, PD_KERNEL_OTHER, s);
         PD_TRY(launch_argmax_reduce((float*)(S + L.amv), (int*)(S + L.ami), R, L.ntilesV,

@@ -783,7 +783,7 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
                     const int n = n0 + (BT / 2) * wn + 16 * i + 4 * g4;
                     if (n >= a.N) continue;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) better(bv, bi, acc[i][j][e], n + e);
+                    for (int e = 0; e < 4; ++e) better(bv, bi, acc[i][j][e], a.n_base + n + e);
                     if (a.logits && m < a.M)
                         *reinterpret_cast<f32x4*>(a.logits + (size_t)m * a.ldlog + n) = acc[i][j];
                 }
@@ -804,9 +804,10 @@ __global__ __launch_bounds__(2 * BT, 2) void gemm_big_kernel(GemmArgs a) {
                 float bv = s_v[0][tid];
                 int bi = s_i[0][tid];
                 better(bv, bi, s_v[1][tid], s_i[1][tid]);
+                const int ld = a.amax_ld ? a.amax_ld : a.ntiles;
                 if (m < a.M) {
-                    a.amax_v[(size_t)m * a.ntiles + ntile] = bv;
-                    a.amax_i[(size_t)m * a.ntiles + ntile] = bi;
+                    a.amax_v[(size_t)m * ld + ntile] = bv;
+                    a.amax_i[(size_t)m * ld + ntile] = bi;
                 }
             }
         } else {
@@ -1105,6 +1106,41 @@ GemmPlan plan_gemm(int M, int N, int K, int epi, bool rows_on_device) {
     return p;
 }
 
+LmHeadPlan plan_lm_head(int M, int N, int K) {
+    LmHeadPlan lp;
+    lp.main = plan_gemm(M, N, K, EPI_ARGMAX);
+    lp.tail = lp.main;
+    lp.tail.kind = -1;
+    lp.n_main = N;
+    lp.ntiles = lp.main.ntiles;
+    if (lp.main.kind != GEMM_BIG || lp.main.wn != 8) return lp;
+    // one workgroup per CU on 256-row tiles: rounds of 256 tiles (row blocks
+    // innermost). With less than half a round left over, the main launch
+    // keeps the largest column count whose tiles fill whole rounds (C = 64,
+    // K = 7: 1,572 tiles are 6 rounds + 36; the 36 tiles' columns, 4,480 of
+    // 201,088, run as 128 x 128 tiles, about a quarter of a round)
+    const int mb = lp.main.mblocks, ntn = lp.main.ntiles;
+    const long tiles = (long)ntn * mb;
+    int g = 256, b = mb;
+    while (b) { const int t = g % b; g = b; b = t; }   // gcd(256, mb)
+    const int step = 256 / g;                           // column tiles per whole round set
+    const int ntn_main = ntn / step * step;
+    if (tiles % 256 == 0 || (tiles % 256) * 2 > 256 || ntn_main == 0 || ntn_main >= ntn) return lp;
+    lp.n_main = ntn_main * kBT;
+    lp.main = plan_gemm(M, lp.n_main, K, EPI_ARGMAX);
+    GemmPlan t = lp.main;
+    t.kind = GEMM_BIG;
+    t.wn = 4;                                           // 128-row tiles, two workgroups per CU
+    t.mblocks = (M + kBT / 2 - 1) / (kBT / 2);
+    t.ntiles = (N - lp.n_main + kBT / 2 - 1) / (kBT / 2);
+    t.splits = 1;
+    const long tt = (long)t.ntiles * t.mblocks;
+    t.grid = (int)(tt < 512 ? tt : 512);
+    lp.tail = t;
+    lp.ntiles = lp.main.ntiles + t.ntiles;
+    return lp;
+}
+
 size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi) {
     return epi == EPI_PARTIAL ? (size_t)p.splits * M * N : 0;
 }
@@ -1112,6 +1148,9 @@ size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi) {
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s) {
     // device row counts: many-row kernel only, not with the max/argmax epilogue
     if ((a.m_dev || a.splits_out) && (p.kind != GEMM_BIG || epi == EPI_ARGMAX)) return PD_EINVAL;
+    // column offset / partial stride of a split LM head: many-row kernel only
+    if ((a.n_base || a.amax_ld) && (p.kind != GEMM_BIG || epi != EPI_ARGMAX)) return PD_EINVAL;
+    if (a.amax_ld && a.amax_ld < p.ntiles) return PD_EINVAL;
     a.splits = p.splits;
     a.ntiles = p.ntiles;
     switch (epi) {

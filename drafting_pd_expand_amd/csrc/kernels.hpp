@@ -50,6 +50,11 @@ struct GemmArgs {
     // consumer of the planes.
     const int32_t* m_dev;
     int32_t* splits_out;
+    // max/argmax epilogue, many-row kernel only: index of this launch's first
+    // output column in the whole row (the argmax reports n_base + column) and
+    // the partials per row of amax_v / amax_i (0: this launch's own count)
+    int n_base;
+    int amax_ld;
 };
 
 enum GemmKind : int {
@@ -89,6 +94,17 @@ __host__ __device__ inline int big_splits(long tiles, int ksteps, long slots, in
     return best_sp;
 }
 GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm);
+// The LM head (max/argmax epilogue) as one or two launches: on 256-row tiles
+// a last round of the persistent grid that is less than half full goes to a
+// second launch on 128-row tiles over the last columns (n_main onwards), so
+// that the first runs whole rounds only. ntiles: argmax partials per row of
+// the two together (the first launch's first).
+struct LmHeadPlan {
+    GemmPlan main, tail;   // tail.kind < 0: one launch
+    int n_main;            // columns of the first launch
+    int ntiles;
+};
+LmHeadPlan plan_lm_head(int M, int N, int K);
 size_t gemm_ws_floats(const GemmPlan& p, int M, int N, int epi);
 int launch_gemm(int epi, const GemmPlan& p, GemmArgs a, hipStream_t s);
 

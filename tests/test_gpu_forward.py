@@ -80,6 +80,33 @@ def test_ragged_widths_all_rows(C, K, L):
     c.close()
 
 
+# An LM head of 288 sampled rows over V = 33040 columns: on 256-row tiles
+# 130 column tiles x 2 row blocks = 260 tiles, 4 past one round of 256, so it
+# runs as two launches, columns 0..32767 on 256-row tiles and the last 272
+# (a partial last tile) on 128-row tiles; every row's logits and argmax are
+# checked across the seam.
+LMSPLIT = synth.ModelDims("lmsplit", d=208, Hq=4, Hkv=2, dh=64, F=688, N=1, V=33040)
+
+
+def test_lm_head_in_two_launches():
+    w = synth.Workload("lmsplit-c36k8", LMSPLIT, C=36, K=8, context="fixed", L=60, seed=41)
+    _say(f"[forward] {w.name}")
+    c = Case(w).run()
+    assert c.status() == 0
+    res = check_case(c, check_cache=False)
+    assert res["rows"] == 36 * 8
+    # the fused argmax of every row equals the argmax of the logits the same
+    # launches wrote (lowest index on ties), whichever launch holds it: the
+    # second launch reports its columns with their offset (with this seed the
+    # oracle's maximum of one row lies past column 32768)
+    lg = c.logits.cpu().numpy()
+    got = c.draft.cpu().numpy()
+    assert np.array_equal(got, np.argmax(lg, axis=1))
+    _say(f"  worst logit err/RMS {res['worst_logit_ratio']:.4g}, argmax checked {res['argmax_checked']}, "
+         f"argmax past the seam in {int((got >= 32768).sum())} rows")
+    c.close()
+
+
 @pytest.mark.parametrize("C,K,L", [(48, 8, 90), (8, 8, 300)], ids=["rows768", "rows128"])
 def test_every_row_computed(C, K, L, monkeypatch):
     """Passes of more than 64 rows normally compute only the rows that are
