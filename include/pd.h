@@ -188,7 +188,11 @@ typedef struct pd_handle pd_handle;
  * SwiGLU MLP + residual; then the final RMSNorm and LM head on the K rows
  * named by new_token_indices, and the greedy argmax (lowest index on ties).
  * Within a layer every K/V write lands before any row attends. Rejected
- * rows are computed as don't-care values and influence nothing.
+ * rows influence nothing: passes of more than 64 rows (at most 4096) gather
+ * the other rows to the front on the device and compute only those; smaller
+ * passes compute rejected rows as don't-care values. A sampled row
+ * (new_token_indices) that is rejected, as a padding request's is, yields an
+ * unspecified draft; one outside [0, T_out) sets PD_STATUS_BAD_ROW.
  *
  * Arguments:
  *   h          [host] handle slot: *h == NULL creates the handle (scratch is
@@ -312,7 +316,8 @@ int pd_status(pd_handle* h, int32_t* out, void* stream);
 
 /* Optional copy of the residual stream: when dst [dev] is non-NULL, later
  * pd_draft_forward calls write float [N+1][T_out][d] (after fc, then after
- * each layer). Pass NULL to stop. */
+ * each layer). Rows of rejected tokens are not computed in passes of more
+ * than 64 rows, and there they are left as they are. Pass NULL to stop. */
 int pd_set_debug_resid(pd_handle* h, float* dst);
 
 /* Optional phase timestamps of the persistent decode kernel (the pass of up
