@@ -130,6 +130,25 @@ def test_every_row_computed(C, K, L, monkeypatch):
     comp.close()
 
 
+@pytest.mark.parametrize("C,K,n,accept,L", [(1, 2, 64, "uniform", 40), (9, 8, 0, "all", 50), (8, 4, 0, "uniform", 70)],
+                         ids=["rows65-two-kept", "rows144-none-rejected", "rows64"])
+def test_compaction_edges(C, K, n, accept, L):
+    """Row compaction at its edges: 65 expanded rows (the first size that is
+    compacted; 63 of them rejected), a batch with no rejected row (every row
+    kept) and 64 rows (the last size computed in place); all rows and the
+    residual stream layer by layer against the oracle."""
+    w = synth.Workload(f"ragged-c{C}k{K}-{accept}", RAGGED, C=C, K=K, context="fixed", L=L, n_verify=n,
+                       accept=accept, seed=11 + C)
+    b = synth.make_batch(w)
+    T_out = int(b["num_tokens"].sum()) + C * (K - 1)
+    _say(f"[forward] {w.name}: {T_out} expanded rows")
+    c = Case(w, debug_resid=True, batch=b).run()
+    assert c.status() == 0
+    res = check_case(c, check_layers=True)
+    _say(f"  worst logit err/RMS {res['worst_logit_ratio']:.4g}")
+    c.close()
+
+
 def _sample(b, K, k=3):
     """Requests to check at large C: the longest context, the most rejections, the first."""
     L = b["context_lens"]
