@@ -67,15 +67,24 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
 // the ring runs on across item boundaries, so a CU never waits for a new
 // workgroup's first loads.
 constexpr int kRS = 128;   // reduction elements per ring stage (256 B of each row)
+// Waves per column group of the LM head on 8 X tiles (65..128 rows) and on 2
+// (17..32 rows): two, each taking half of the X tiles, so that two waves
+// share a SIMD and hide each other's waits (C = 16, 112 rows: 136 vs 157 us,
+// 4.6 vs 4.0 TB/s; four waves per group 138 us; C = 4, 28 rows: 174.5 vs
+// 176.4 us)
+constexpr int kRingLmRowSplit = 2;
+constexpr int kRingLm2RowSplit = 2;
 
 // 16 zero bytes: the source of out-of-range chunks (zero-initialised at load)
 __device__ __align__(16) uint16_t g_gemm_zero[8];
 
 // KRS: reduction elements per stage (128: rows of 16 16-byte chunks; 64: rows
 // of 8 chunks, for 8 X tiles, whose X rows would otherwise crowd the ring).
-template <int WN, int NM, int MT, int KRS = kRS>
+// RS: waves per column group, each taking MT / RS of the X tiles (2 for the
+// LM head on 8 or 2 X tiles: two waves per SIMD)
+template <int WN, int NM, int MT, int KRS = kRS, int RS = 1>
 struct RingCfg {
-    static constexpr int NT = 64 * WN;
+    static constexpr int NT = 64 * WN * RS;
     static constexpr int CH = KRS / 8;        // 16-byte chunks per staged row
     static constexpr int WR = 16 * WN * NM;   // W rows per stage (64 or 128)
     static constexpr int XR = 16 * MT;        // X rows per stage
@@ -124,15 +133,18 @@ __device__ __forceinline__ unsigned ring_lds(void* p) {
     return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)p);
 }
 
-template <int WN, int NM, int MT, int EPI, int KRS = kRS>
-__global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
-    using Cf = RingCfg<WN, NM, MT, KRS>;
+template <int WN, int NM, int MT, int EPI, int KRS = kRS, int RS = 1>
+__global__ __launch_bounds__(64 * WN * RS) void gemm_ring_kernel(GemmArgs a) {
+    using Cf = RingCfg<WN, NM, MT, KRS, RS>;
+    constexpr int MTW = MT / RS;   // X tiles of each wave
+    static_assert(MT % RS == 0 && (RS == 1 || EPI == EPI_ARGMAX), "row split: the LM head only");
     constexpr int NT = Cf::NT, NST = Cf::NST, L = Cf::L, WL = Cf::WL, XL = Cf::XL, CH = Cf::CH;
     constexpr bool PAIR = (EPI == EPI_SWIGLU);          // row groups = gate, up of the same columns
     constexpr int TW = 16 * WN * (PAIR ? 1 : NM);       // output columns per tile
     __shared__ __align__(16) uint16_t ring[NST * Cf::SE];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave % WN, tb = (wave / WN) * MTW;   // column group of the wave, its first X tile
     const int r16 = lane & 15, g4 = lane >> 4;
 
     const int ksteps = (a.K + KRS - 1) / KRS;
@@ -143,11 +155,12 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 
     // this thread's fixed share of every stage: W (row within the tile,
     // chunk) and X (row pointer, chunk)
-    int wrr[WL], wch[WL], wofs[WL];
+    int wrr[WL], wgq[WL], wch[WL], wofs[WL];
 #pragma unroll
     for (int j = 0; j < WL; ++j) {
         const int u = tid + NT * j, wr = u / CH;
         wrr[j] = wr % (16 * WN);
+        wgq[j] = wr / (16 * WN);   // row group of this load
         wch[j] = ((u % CH) ^ ring_sw<CH>(wr)) * 8;
         wofs[j] = wrr[j] * a.K + wch[j];   // element offset from the tile's first row, k = 0
     }
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
         wfull = n0 + TW <= a.N;
 #pragma unroll
         for (int j = 0; j < WL; ++j) {
-            const int q = j * NT / (CH * 16 * WN);   // row group of this load (compile-time)
+            const int q = wgq[j];
             const int nq = n0 + (PAIR ? 0 : q * 16 * WN);
             const uint16_t* base = (PAIR && q == 1) ? a.W2 : a.W;
             wp[j] = (nq + wrr[j] < a.N) ? base + (size_t)nq * a.K + wofs[j] : nullptr;
@@ -240,10 +253,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
 
     // LM head: a lane's best (value, lowest index) of row 16t + r16 over every
     // column it sees, across all of the workgroup's items
-    float runv[MT];
-    int runi[MT];
+    float runv[MTW];
+    int runi[MTW];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
+    for (int t = 0; t < MTW; ++t) {
         runv[t] = -FLT_MAX;
         runi[t] = INT_MAX;
     }
@@ -252,9 +265,9 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
         const int sp = it / ntn;
         const int kb = sp * per, ke = min(ksteps, (sp + 1) * per);
         if (kb >= ke) continue;
-        f32x4 acc[MT][NM];
+        f32x4 acc[MTW][NM];
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MTW; ++t)
 #pragma unroll
             for (int q = 0; q < NM; ++q) acc[t][q] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int ks = kb; ks < ke; ++ks, ++qc) {
@@ -272,26 +285,26 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
                 bf16x8 wf[NM];
 #pragma unroll
                 for (int q = 0; q < NM; ++q)
-                    wf[q] = *reinterpret_cast<const bf16x8*>(Ws + (q * 16 * WN + 16 * wave + r16) * KRS + pos);
+                    wf[q] = *reinterpret_cast<const bf16x8*>(Ws + (q * 16 * WN + 16 * wn + r16) * KRS + pos);
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(Xs + (16 * t + r16) * KRS + pos);
+                for (int t = 0; t < MTW; ++t) {
+                    const bf16x8 xf = *reinterpret_cast<const bf16x8*>(Xs + (16 * (tb + t) + r16) * KRS + pos);
 #pragma unroll
                     for (int q = 0; q < NM; ++q) acc[t][q] = mfma_16x16x32(wf[q], xf, acc[t][q]);
                 }
             }
         }
 
-        // lane holds rows m = 16t + r16 and columns n .. n+3 of each column group q
-        const int n0 = (it % ntn) * TW + 16 * wave + 4 * g4;
+        // lane holds rows m = 16 (tb + t) + r16 and columns n .. n+3 of each column group q
+        const int n0 = (it % ntn) * TW + 16 * wn + 4 * g4;
         if constexpr (EPI == EPI_ARGMAX) {
 #pragma unroll
             for (int q = 0; q < NM; ++q) {
                 const int n = n0 + q * 16 * WN;
                 if (n >= a.N) continue;
 #pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    const int m = 16 * t + r16;
+                for (int t = 0; t < MTW; ++t) {
+                    const int m = 16 * (tb + t) + r16;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) better(runv[t], runi[t], acc[t][q][e], n + e);
                     if (a.logits && m < a.M)
@@ -300,8 +313,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
             }
         } else {
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int m = 16 * t + r16;
+            for (int t = 0; t < MTW; ++t) {
+                const int m = 16 * (tb + t) + r16;
                 if (m >= a.M) continue;
                 if constexpr (EPI == EPI_PARTIAL) {
 #pragma unroll
@@ -323,9 +336,9 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
         }
     }
     if constexpr (EPI == EPI_ARGMAX) {
-        // one (value, index) per row per wave: entry blockIdx.x * WN + wave
+        // one (value, index) per row per column group: entry blockIdx.x * WN + wn
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
+        for (int t = 0; t < MTW; ++t) {
             float bv = runv[t];
             int bi = runi[t];
 #pragma unroll
@@ -334,10 +347,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_ring_kernel(GemmArgs a) {
                 const int oi = __shfl_xor(bi, off, kWave);
                 better(bv, bi, ov, oi);
             }
-            const int m = 16 * t + r16;
+            const int m = 16 * (tb + t) + r16;
             if (g4 == 0 && m < a.M) {
-                a.amax_v[(size_t)m * a.ntiles + blockIdx.x * WN + wave] = bv;
-                a.amax_i[(size_t)m * a.ntiles + blockIdx.x * WN + wave] = bi;
+                a.amax_v[(size_t)m * a.ntiles + blockIdx.x * WN + wn] = bv;
+                a.amax_i[(size_t)m * a.ntiles + blockIdx.x * WN + wn] = bi;
             }
         }
     }
@@ -907,14 +920,29 @@ template <int EPI, int NM>
 int launch_ring_nm(const GemmPlan& p, const GemmArgs& a, hipStream_t s) {
     constexpr int WN = EPI == EPI_SWIGLU ? 2 : 4;
     if (p.wn != WN) return PD_EINVAL;
+    // row splits: the LM head on 8 or 2 X tiles, two waves per column group
+    if (p.rs != 1 && !(EPI == EPI_ARGMAX && (p.mt == 8 || p.mt == 2) && p.rs == 2)) return PD_EINVAL;
     switch (p.mt) {
         case 1: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 1, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 2, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
+        case 2:
+            if (p.rs == 2) {
+                if constexpr (EPI == EPI_ARGMAX)
+                    hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 2, EPI, kRS, 2>), dim3(p.grid), dim3(128 * WN), 0, s, a);
+                else
+                    return PD_EINVAL;
+            } else {
+                hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 2, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a);
+            }
+            break;
         case 4: hipLaunchKernelGGL((gemm_ring_kernel<WN, NM, 4, EPI>), dim3(p.grid), dim3(64 * WN), 0, s, a); break;
         case 8:
             if constexpr (EPI == EPI_ARGMAX && NM == 2) {
                 if (p.krs != 64) return PD_EINVAL;
-                hipLaunchKernelGGL((gemm_ring_kernel<WN, 2, 8, EPI_ARGMAX, 64>), dim3(p.grid), dim3(64 * WN), 0, s, a);
+                if (p.rs == 2)
+                    hipLaunchKernelGGL((gemm_ring_kernel<WN, 2, 8, EPI_ARGMAX, 64, 2>), dim3(p.grid), dim3(128 * WN), 0,
+                                       s, a);
+                else
+                    hipLaunchKernelGGL((gemm_ring_kernel<WN, 2, 8, EPI_ARGMAX, 64>), dim3(p.grid), dim3(64 * WN), 0, s, a);
                 break;
             } else {
                 return PD_EINVAL;
@@ -983,6 +1011,7 @@ GemmPlan plan_gemm_nm(int M, int N, int K, int epi, int ring_nm) {
         p.wn = 4;
         p.nm = 2;
         p.krs = 64;
+        p.rs = kRingLmRowSplit;
         const long items = (N + 127) / 128;
         const long rounds = (items + 255) / 256;
         p.grid = (int)((items + rounds - 1) / rounds);
@@ -1100,7 +1129,8 @@ GemmPlan plan_gemm(int M, int N, int K, int epi, bool rows_on_device) {
     if (M > 16 && M <= 64 && epi != EPI_ARGMAX && (long long)N * K * 2 < (1LL << 31)) return plan_wring(N, K, epi);
     const GemmPlan p = plan_gemm_nm(M, N, K, epi, 1);
     if (p.kind == GEMM_RING && p.mt >= 2 && p.mt <= 4 && epi != EPI_SWIGLU) {
-        const GemmPlan w = plan_gemm_nm(M, N, K, epi, 2);
+        GemmPlan w = plan_gemm_nm(M, N, K, epi, 2);
+        if (w.mt == 2 && epi == EPI_ARGMAX) w.rs = kRingLm2RowSplit;
         if (w.grid >= 220) return w;
     }
     return p;

@@ -74,6 +74,7 @@ struct GemmPlan {
     int splits;    // K splits (EPI_PARTIAL: one fp32 plane each)
     int grid;      // ring / big: persistent workgroups
     int krs;       // ring: reduction elements per stage (128, or 64 with 8 X tiles)
+    int rs = 1;    // ring, LM head on 8 or 2 X tiles: waves per column group (each takes mt / rs tiles)
 };
 
 // rows_on_device: the rows present are counted on the device (GemmArgs::m_dev,
