@@ -23,9 +23,11 @@
 //   C  the output base of every (segment, depth) run, then per (depth, group)
 //      the group's output base when all its positions fall in one segment;
 //      each wave then takes 4 such groups at a time, lane = 4 consecutive
-//      positions: one 16-byte store of segment ids per lane, and row-list
-//      slot = group base + rank in the mask. The few groups that straddle a
-//      boundary are done last, one wave per group, lane = position.
+//      positions: one 16-byte store of segment ids per lane; row-list slot =
+//      group base + rank in the mask, staged in LDS by rank so that the
+//      group's entries go out as runs of 16 consecutive slots. The few groups
+//      that straddle a boundary are done last, one wave per group, lane =
+//      position.
 // Within a row the segment id is non-decreasing in p, so a (segment, depth)
 // run is a contiguous range of p: no sorting or atomics are needed and the
 // row list comes out segment by segment, depth by depth, p ascending.
@@ -153,6 +155,7 @@ __global__ __launch_bounds__(kPT) void seq_partition_kernel(PartArgs a) {
     __shared__ int s_pre[(PD_PART_MAX_S + 1) * PD_PART_MAX_K];   // row prefix at range starts, [s][d]
     __shared__ int s_adj[PD_PART_MAX_S * PD_PART_MAX_K];         // run base - row prefix, [s][d]
     __shared__ __align__(16) int s_ws[2][KM * kNW];
+    __shared__ int s_stage[kNW][256];   // a wave's row-list entries of its 4 groups, by rank
 
     const int b = blockIdx.x, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -359,21 +362,33 @@ __global__ __launch_bounds__(kPT) void seq_partition_kernel(PartArgs a) {
             const uint32_t nib = (uint32_t)(m >> sub) & 0xfu;
             const int rank0 = __popcll(m & below);
             const int p = g * 64 + sub;
-            const bool mixed = (w & kMixed) != 0;
+            // groups that straddle a boundary are left to phase C2c
+            const bool live = g < ng && (w & kMixed) == 0;
             const int su = (w >> kSegShift) & 0xff;
-            const int bu = (w & kBaseMask) + rank0;
-            if (mixed) continue;   // groups that straddle a boundary: phase C2c
+            int* stage = s_stage[wv] + (lane >> 4) * 64;   // this lane's group, by rank
             int out[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 out[i] = -1;
-                if ((nib >> i) & 1u) {
+                if (live && ((nib >> i) & 1u)) {
                     out[i] = su;
-                    const int r = bu + __popc(nib & ((1u << i) - 1u));
-                    if (r >= 0 && (size_t)r < KN) rows[r] = d * n + p + i;
+                    stage[rank0 + __popc(nib & ((1u << i) - 1u))] = d * n + p + i;
                 }
             }
-            if (p < n) *reinterpret_cast<int4*>(segd + p) = make_int4(out[0], out[1], out[2], out[3]);
+            if (live && p < n) *reinterpret_cast<int4*>(segd + p) = make_int4(out[0], out[1], out[2], out[3]);
+            // the group's row-list entries (consecutive slots from its base)
+            // go out from the stage, 16 consecutive slots per store and group:
+            // whole cache lines instead of a slot every ~2 positions per lane.
+            // A wave's LDS accesses complete in order, so the reads see every
+            // lane's writes above and precede the next group's writes.
+            const int cnt = live ? __popcll(m) : 0;
+            const int gb = w & kBaseMask;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int k = (lane & 15) + 16 * t;
+                const int r = gb + k;
+                if (k < cnt && r >= 0 && (size_t)r < KN) rows[r] = stage[k];
+            }
         }
     }
 
