@@ -390,7 +390,7 @@ def fp8_leg(pdx, mdev, w, b, dims, inp, cache, stream, steps: int, bf16_ids, bf1
             "draft_ids_equal_bf16_cache_frac": agree}
 
 
-def partition_leg(pdx, stream, reps: int = 20) -> dict:
+def partition_leg(pdx, stream, reps: int = 200, warmup: int = 50) -> dict:
     """Sequence partitioning ([Paper] sec. 3.2) on a training batch: 256
     sequences of 8192 tokens, K = 8 depths kept with COD decay r = 0.8 (the
     pages' 8192 / K = 8 / r = 0.8 example, ~34K positions each), 4 segments.
@@ -408,7 +408,8 @@ def partition_leg(pdx, stream, reps: int = 20) -> dict:
     off = torch.empty((B, S + 1), dtype=torch.int32, device=dev)
     rows = torch.empty((B, K * n), dtype=torch.int32, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(3):
+    # (the first few dozen calls run slower while the clocks settle)
+    for _ in range(warmup):
         pdx.pd_seq_partition(keep, bnd, seg, off, rows, st, stream)
     torch.cuda.synchronize()
     if int(st.item()) != 0 or int(off[:, S].sum().item()) != placed:
