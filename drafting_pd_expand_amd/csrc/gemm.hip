@@ -92,8 +92,12 @@ struct RingCfg {
     static constexpr int XL = XR * CH / NT;   // 16-byte X loads per thread per stage
     static constexpr int L = WL + XL;
     static constexpr int SE = (WR + XR) * KRS;   // elements per stage
+    // ring stages. One X tile: 4 (the 1-request step with 6, 4, 3, 2 stages
+    // in one same-box run: 495.7, 484.5, 495.0, 666.1 us; 5 in another: 489.6
+    // against 494.8; the LM head the same at 6 and 4): more stages in flight
+    // per CU do not stream faster
     static constexpr int NST = KRS == 64 ? 4
-                               : (WR == 64 ? (MT == 1 ? 6 : (MT == 2 ? 5 : 4)) : (MT == 1 ? 4 : 3));
+                               : (WR == 64 ? (MT == 1 ? 4 : (MT == 2 ? 5 : 4)) : (MT == 1 ? 4 : 3));
     static_assert(WL * NT == WR * CH && XL * NT == XR * CH, "whole loads per thread");
 };
 
@@ -359,12 +363,10 @@ __global__ __launch_bounds__(64 * WN * RS) void gemm_ring_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Weight-only ring (17..64 rows: the projections of the few-request steps).
 // The ring kernel above stages the X columns in its LDS stages next to the
-// weights; at 33..64 rows they fill half of every stage, and a CU keeps only
-// ~48 KB of weights in flight, which is what bounds a latency-limited stream
-// (the gate/up stream runs ~1.5x slower at 56 rows than at 7, the ratio of
-// the weight bytes in flight). Here the LDS ring holds weights only: NST = 8
-// stages of 64 W rows x 128 reduction elements (16 KB each; 7 stages = 112 KB
-// in flight while one is read). Each of the four waves owns one 16-row X tile
+// weights; at 33..64 rows they fill half of every stage (the gate/up stream
+// ran ~1.5x slower at 56 rows than at 7). Here the LDS ring holds weights
+// only: NST stages of 64 W rows x 128 reduction elements (16 KB each). Each
+// of the four waves owns one 16-row X tile
 // and all 64 columns of the stage, and loads its X fragments straight into
 // registers, from L2 (X is a few hundred KB that every workgroup re-reads).
 // The X loads of a stage are issued with the stage's weight loads, NST - 1
@@ -378,10 +380,14 @@ __global__ __launch_bounds__(64 * WN * RS) void gemm_ring_kernel(GemmArgs a) {
 // partial (NST - 2 stages of loads may remain in flight) because the weight
 // copies use the buffer form (see below). A workgroup owns exactly one
 // (column tile, K split) item and writes it after the loop. Projections
-// only (fp32 partial planes, SwiGLU): measured on the 4-request step, the
-// projections run 24 us faster per step than on the ring kernel (7 vs 3
-// stages of weights in flight), the 28-row LM head 20 us slower.
-constexpr int kWRingStages = 8;
+// only (fp32 partial planes, SwiGLU): measured on the 4-request step (28
+// rows) with 8 stages, the projections ran 24 us faster per step than on the
+// ring kernel, the 28-row LM head 20 us slower. Stages: 4 (three same-box
+// runs of that step against 8 stages at 598-602 us: 6 594.0, 5 577.9, 4
+// 572.6, 3 568.7-574.6, 2 668.1 us; 3 and 4 are within 1%, and 4 keeps more
+// in flight for 33..64 rows, where the X loads take a larger share of each
+// stage).
+constexpr int kWRingStages = 4;
 // word 3 of a raw buffer descriptor on gfx9 (no format conversion, no swizzle)
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
