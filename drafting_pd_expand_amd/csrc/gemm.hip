@@ -380,13 +380,11 @@ __global__ __launch_bounds__(64 * WN * RS) void gemm_ring_kernel(GemmArgs a) {
 // partial (NST - 2 stages of loads may remain in flight) because the weight
 // copies use the buffer form (see below). A workgroup owns exactly one
 // (column tile, K split) item and writes it after the loop. Projections
-// only (fp32 partial planes, SwiGLU): measured on the 4-request step (28
-// rows) with 8 stages, the projections ran 24 us faster per step than on the
-// ring kernel, the 28-row LM head 20 us slower. Stages: 4 (three same-box
-// runs of that step against 8 stages at 598-602 us: 6 594.0, 5 577.9, 4
-// 572.6, 3 568.7-574.6, 2 668.1 us; 3 and 4 are within 1%, and 4 keeps more
-// in flight for 33..64 rows, where the X loads take a larger share of each
-// stage).
+// only (fp32 partial planes, SwiGLU): measured on the 4-request step (56
+// projection rows) with 8 stages, the projections ran 24 us faster per step
+// than on the ring kernel, the 28-row LM head 20 us slower. Stages: 4 (three
+// same-box runs of that step against 8 stages at 598-602 us: 6 594.0, 5
+// 577.9, 4 572.6, 3 568.7-574.6, 2 668.1 us; 3 and 4 are within 1%).
 constexpr int kWRingStages = 4;
 // word 3 of a raw buffer descriptor on gfx9 (no format conversion, no swizzle)
 constexpr int kBufferRsrcWord3 = 0x00020000;
